@@ -1,0 +1,30 @@
+"""CPU oracle for the equivariant message-passing convolution (TEST INFRASTRUCTURE).
+
+This package is a plain, slow, obviously-correct fp64 implementation of the
+convolution
+
+    m_b = (1/N) * sum_{a -> b} (x_a (x) y_ab) (.) s_ab
+
+as defined on the e3j ``Convolution`` API page (class description, the
+formula and the four-step plain implementation: gather by senders, tensor
+product with edge features, mixing with edge scalars, scatter-add onto
+receivers, optional division by ``avg_num_neighbors``).
+
+It exists only to check the HIP implementation.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it.  It shares no code with the HIP path: the irreps parser, the path
+enumeration, the Racah Clebsch-Gordan builder, the real basis, the Wigner D
+matrices and the convolution itself are all written here independently.
+
+Modules
+-------
+irreps  -- irreps string parser (``"8x0e+8x1o"``, ``"64x(0e+1o+2e)"``).
+so3     -- Racah complex CG, complex->real basis change, real CG tensors,
+           real Wigner D matrices from the exponential map of generators.
+conv    -- path enumeration, brute-force and vectorised forward, backward.
+
+Pins (what ties this oracle to something other than itself) live in
+``tests/test_oracle_*.py``; every function here is pinned there.
+"""
+
+from . import irreps, so3, conv  # noqa: F401
