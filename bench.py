@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Throughput of the fused equivariant convolution on one MI355X.
+
+Default workload: the training step of the MACE-scale graph (N=20000 nodes,
+~596k directed edges from a radius graph, 128x0e+128x1o features, spherical
+harmonics to lmax 3, output 128x(0e+1o+2e+3o), fp32): one step is the fused
+forward plus the fused reverse pass (grad x, grad y, grad s) over the whole
+graph.  Inputs are seeded synthetic data, resident in HBM before timing; the
+plan and the receiver CSR are built once per graph, outside the timed region
+(reported separately).
+
+Prints one JSON line: edges/s of whole steps, plus the roofline of the
+dominant kernel (algorithmic bytes / average duration from HIP events on the
+launch stream) and the CPU oracle timed on a bounded sample.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, AMD published
+METRIC = "edges/sec + achieved HBM GB/s (% of peak) for fused TP conv fwd/bwd, 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, help="0..4; 4 = training step (fwd+bwd)")
+    ap.add_argument("--fwd-variant", type=int, default=0)
+    ap.add_argument("--bwd-variant", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-edges", type=int, default=12000)
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every compiled kernel variant (one JSON line each) and exit")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="run a plain device copy of MIB MiB (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def calibrate_copy(mib, reps=5):
+    """A plain device-to-device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4, "reps": reps}), flush=True)
+
+
+def sweep(plan, w, run_fwd, run_bwd, nbytes, reps=10):
+    """Average HIP-event time of every compiled variant."""
+    import numpy as np
+    import torch
+    from equivariant_gnn_message_amd import e3conv as E
+    dt = E.E3CONV_BF16 if w.dtype == "bf16" else E.E3CONV_F32
+    nf, nb = plan.num_variants(dt)
+    for kind, n, run, by in (("fwd", nf, run_fwd, nbytes[0]), ("bwd", nb if w.backward else 0, run_bwd, nbytes[1])):
+        for v in range(n):
+            plan.set_variant(v if kind == "fwd" else 0, v if kind == "bwd" else 0)
+            run()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                run()
+                b.record()
+                ts.append((a, b))
+            torch.cuda.synchronize()
+            ms = float(np.mean([a.elapsed_time(b) for a, b in ts]))
+            print(json.dumps({"workload": w.idx, "kernel": kind, "variant": v, "ms": ms,
+                              "GBps": by / ms / 1e6, "frac": by / ms / 1e6 / PEAK_HBM_GBPS}), flush=True)
+
+
+def alg_bytes(w, N, E, b_in):
+    """Compulsory bytes: every input read once, every output written once."""
+    C, nx, ny, no, P = w.channels, w.num_x, (w.lmax + 1) ** 2, w.num_out, w.num_paths
+    fwd = N * nx * C * b_in + E * (ny * b_in + P * C * b_in + 4) + 4 * (N + 1) + N * no * C * 4
+    bwd = 4 * (2 * N * nx * C + N * no * C + (N + 1) + E * (2 * ny + 2 * P * C + 1))
+    return fwd, bwd
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "layout.h", "kernels.h"):
+        with open(os.path.join(ROOT, "equivariant_gnn_message_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_w{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, sample_edges, with_backward):
+    """The oracle, as it stands, on the first receivers covering ~sample_edges edges."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import conv
+
+    w = inp.workload
+    lay = conv.make_layout(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    ptr = np.searchsorted(inp.receivers, np.arange(inp.num_nodes + 1))
+    nrows = int(np.searchsorted(ptr, sample_edges))
+    nrows = max(1, min(nrows, inp.num_nodes))
+    e1 = int(ptr[nrows])
+    x = inp.as_f32("x")
+    y = inp.as_f32("y")[:e1] if inp.y.dtype != np.float32 else inp.y[:e1]
+    s = inp.s[:e1]
+    if s.dtype == np.uint16:
+        from equivariant_gnn_message_amd import synth
+        s = synth.bf16_to_f32(s).reshape(s.shape)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        out = conv.forward(lay, x, y, s, inp.senders[:e1], inp.receivers[:e1], nrows)
+        if with_backward:
+            conv.backward(lay, x, y, s, inp.g, inp.senders[:e1], inp.receivers[:e1], inp.num_nodes)
+        dt = time.perf_counter() - t0
+    return {"value": e1 / dt, "unit": "edges/s", "cores": 1, "kind": "oracle",
+            "sample": f"receivers 0..{nrows - 1} ({e1} edges) of the same graph, "
+                      f"{'forward + reverse' if with_backward else 'forward'}, fp64 numpy, "
+                      f"{dt:.1f} s"}, out, nrows
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the multi-GPU sharding is described in DESIGN.md, not implemented)", file=sys.stderr)
+        sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+
+    import numpy as np
+    import torch
+
+    from equivariant_gnn_message_amd import e3conv as E
+    from equivariant_gnn_message_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    inp = synth.make_inputs(args.workload)
+    t_gen = time.perf_counter() - t0
+    N, Ecount = inp.num_nodes, inp.num_edges
+    dev = torch.device("cuda:0")
+
+    def t(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    x, y, s, g = t(inp.x), t(inp.y), t(inp.s), t(inp.g)
+    src, dst = t(inp.senders), t(inp.receivers)
+    torch.cuda.synchronize()
+
+    tp = time.perf_counter()
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    plan.set_variant(args.fwd_variant, args.bwd_variant)
+    plan_ms = (time.perf_counter() - tp) * 1e3
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    row_ptr = E.e3conv_csr_from_receivers(dst, N)
+    ev1.record()
+    torch.cuda.synchronize()
+    csr_ms = ev0.elapsed_time(ev1)
+
+    out = torch.empty((N, w.num_out, w.channels), dtype=torch.float32, device=dev)
+    grads = None
+    if w.backward:
+        grads = (torch.empty_like(x), torch.empty_like(y), torch.empty_like(s))
+
+    fwd_ev, bwd_ev = [], []
+
+    def step(record):
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+        plan.forward(x, y, s, src, row_ptr, out=out)
+        if record:
+            b.record()
+            fwd_ev.append((a, b))
+        if w.backward:
+            if record:
+                c, d = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                c.record()
+            plan.backward(x, y, s, src, row_ptr, g, grads=grads)
+            if record:
+                d.record()
+                bwd_ev.append((c, d))
+
+    if args.sweep:
+        b_in = 2 if w.dtype == "bf16" else 4
+        sweep(plan, w, lambda: plan.forward(x, y, s, src, row_ptr, out=out),
+              lambda: plan.backward(x, y, s, src, row_ptr, g, grads=grads),
+              alg_bytes(w, N, Ecount, b_in))
+        return
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+
+    ms_per_step = wall / args.steps * 1e3
+    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in fwd_ev]))
+    b_in = 2 if w.dtype == "bf16" else 4
+    fwd_bytes, bwd_bytes = alg_bytes(w, N, Ecount, b_in)
+    res = {
+        "metric": METRIC,
+        "value": Ecount / (ms_per_step * 1e-3),
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{w.name}: {'forward + reverse' if w.backward else 'forward'} convolution, "
+                         f"radius graph N={N} E={Ecount}, {w.irreps_in} (x) SH lmax {w.lmax} -> "
+                         f"{w.irreps_out}, avg_num_neighbors {w.avg_num_neighbors:g}, "
+                         f"{'bf16 storage / fp32 accumulation' if w.dtype == 'bf16' else 'fp32'}"),
+            "num_nodes": N, "num_edges": Ecount, "channels": w.channels, "num_paths": w.num_paths,
+            "parallelism": "single GPU",
+        },
+        "fwd_ms": fwd_ms,
+        "fwd_hbm_GBps": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
+        "fwd_hbm_frac": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "csr_ms": csr_ms,
+        "plan_ms": plan_ms,
+        "variants": [args.fwd_variant, args.bwd_variant],
+    }
+    kernel, kbytes, kms = "conv_fwd", fwd_bytes, fwd_ms
+    if w.backward:
+        bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in bwd_ev]))
+        res["bwd_ms"] = bwd_ms
+        res["bwd_hbm_GBps"] = bwd_bytes / (bwd_ms * 1e-3) / 1e9
+        res["bwd_hbm_frac"] = res["bwd_hbm_GBps"] / PEAK_HBM_GBPS
+        res["step_hbm_frac"] = (fwd_bytes + bwd_bytes) / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS
+        kernel, kbytes, kms = "conv_bwd", bwd_bytes, bwd_ms
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                       "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic_from_profiles(kernel, args.workload),
+                       "kernel": kernel, "algorithmic_bytes": kbytes}
+    if not args.no_cpu_baseline:
+        base, ref_rows, nrows = cpu_baseline(inp, args.cpu_sample_edges, w.backward)
+        res["cpu_baseline"] = base
+        got = out[:nrows].double().cpu().numpy()
+        rms = math.sqrt(float(np.mean(ref_rows ** 2)))
+        res["parity_sample_max_rel_err"] = float(np.abs(got - ref_rows).max()) / rms
+    else:
+        res["cpu_baseline"] = None
+    res["input_gen_s"] = t_gen
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,375 @@
+// C ABI of the convolution library (declarations and contracts in e3conv.h).
+#include "../../include/e3conv.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "host_core.h"
+#include "kernels.h"
+
+using e3c::HostPath;
+using e3c::Irrep;
+
+struct e3conv_plan_s {
+  int channels = 0;
+  int lmax = 0;
+  int num_x = 0, num_y = 0, num_out = 0;
+  float avg = 1.0f;
+  std::vector<Irrep> xin, out;
+  std::vector<HostPath> paths;
+  std::vector<std::vector<double>> cg;   // per path, [m1][m2][m3]
+  // sparse export
+  std::vector<int> ix, iy, ip, iout;
+  std::vector<double> val;
+  // compiled kernels (nullptr if none) and their coefficient vector
+  const e3c::KernelSet* ks = nullptr;
+  std::vector<float> kcoef;
+  int fwd_variant = 0;
+  int bwd_variant = 0;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+e3conv_status fail(e3conv_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+e3conv_status ok() {
+  g_last_error.clear();
+  return E3CONV_OK;
+}
+
+e3conv_status hip_fail(hipError_t err, const char* what) {
+  return fail(E3CONV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(err));
+}
+
+// block code for kernel lookup: unique l in ascending order, else 0 (no kernel)
+uint32_t block_code(const std::vector<Irrep>& blocks) {
+  uint32_t code = 0;
+  int prev = -1;
+  for (const Irrep& b : blocks) {
+    if (b.l <= prev || b.l > e3c::kMaxL) return 0;
+    prev = b.l;
+    code |= (b.parity > 0 ? 1u : 2u) << (2 * b.l);
+  }
+  return code;
+}
+
+// Pack the kernel coefficients in the kernel's enumeration order and check the
+// host tables against it (paths identical, no nonzero outside the pattern).
+bool bind_kernels(e3conv_plan_s* p, std::string* why) {
+  const uint32_t xc = block_code(p->xin), oc = block_code(p->out);
+  if (xc == 0 || oc == 0) return false;
+  const e3c::KernelSet* ks = e3c::find_kernels(p->channels, xc, p->lmax, oc);
+  if (!ks) return false;
+  const e3c::LayoutTables& T = *ks->tables;
+  if (T.num_paths != (int)p->paths.size() || T.num_x != p->num_x || T.num_out != p->num_out ||
+      T.num_y != p->num_y) {
+    *why = "kernel layout tables disagree with the host path enumeration";
+    return false;
+  }
+  std::vector<float> coef(T.nnz, 0.0f);
+  for (int q = 0; q < T.num_paths; ++q) {
+    const e3c::PathInfo& P = T.path[q];
+    const HostPath& H = p->paths[q];
+    if (P.l1 != H.l1 || P.l2 != H.l2 || P.l3 != H.l3 || P.o1 != H.o1 || P.o2 != H.o2 ||
+        P.o3 != H.o3) {
+      *why = "kernel path order disagrees with the host path enumeration";
+      return false;
+    }
+    const int n2 = 2 * H.l2 + 1, n3 = 2 * H.l3 + 1;
+    const std::vector<double>& C = p->cg[q];
+    std::vector<char> covered(C.size(), 0);
+    for (int e = P.nnz_begin; e < P.nnz_end; ++e) {
+      const e3c::Entry& en = T.entry[e];
+      const size_t idx = ((size_t)en.m1 * n2 + en.m2) * n3 + en.m3;
+      coef[e] = (float)C[idx];
+      covered[idx] = 1;
+    }
+    for (size_t i = 0; i < C.size(); ++i) {
+      if (C[i] != 0.0 && !covered[i]) {
+        *why = "a nonzero CG entry lies outside the kernel's selection-rule pattern";
+        return false;
+      }
+    }
+  }
+  p->ks = ks;
+  p->kcoef.swap(coef);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* e3conv_status_string(e3conv_status st) {
+  switch (st) {
+    case E3CONV_OK: return "ok";
+    case E3CONV_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case E3CONV_ERR_PARSE: return "irreps parse error";
+    case E3CONV_ERR_UNSUPPORTED: return "unsupported layout or dtype";
+    case E3CONV_ERR_NO_PATH: return "output irrep reached by no path";
+    case E3CONV_ERR_GRAPH: return "invalid graph";
+    case E3CONV_ERR_WORKSPACE: return "workspace too small";
+    case E3CONV_ERR_HIP: return "HIP runtime error";
+    case E3CONV_ERR_INTERNAL: return "internal consistency error";
+  }
+  return "unknown status";
+}
+
+const char* e3conv_last_error_detail(void) { return g_last_error.c_str(); }
+
+e3conv_status e3conv_plan(const char* irreps_in, int sh_lmax, const char* irreps_out,
+                          float avg_num_neighbors, e3conv_plan_t* plan_out) {
+  if (!plan_out) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan_out is NULL");
+  *plan_out = nullptr;
+  if (!irreps_in || !irreps_out) return fail(E3CONV_ERR_INVALID_ARGUMENT, "irreps string is NULL");
+  if (sh_lmax < 0 || sh_lmax > 6) return fail(E3CONV_ERR_INVALID_ARGUMENT, "sh_lmax must be in 0..6");
+  if (!(avg_num_neighbors > 0.0f) || !std::isfinite(avg_num_neighbors))
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "avg_num_neighbors must be positive and finite");
+  std::unique_ptr<e3conv_plan_s> p(new (std::nothrow) e3conv_plan_s());
+  if (!p) return fail(E3CONV_ERR_INTERNAL, "out of host memory");
+  std::string err;
+  if (!e3c::parse_irreps(irreps_in, &p->xin, &err))
+    return fail(E3CONV_ERR_PARSE, std::string("irreps_in: ") + err);
+  if (!e3c::parse_irreps(irreps_out, &p->out, &err))
+    return fail(E3CONV_ERR_PARSE, std::string("irreps_out: ") + err);
+  const int C = p->xin[0].mul;
+  if (C <= 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "multiplicity must be positive");
+  for (const auto* list : {&p->xin, &p->out})
+    for (const Irrep& b : *list) {
+      if (b.mul != C)
+        return fail(E3CONV_ERR_INVALID_ARGUMENT, "all blocks need the same multiplicity");
+      if (b.l > 6) return fail(E3CONV_ERR_UNSUPPORTED, "irreps with l > 6 are not supported");
+    }
+  for (const auto* list : {&p->xin, &p->out})
+    for (size_t i = 0; i < list->size(); ++i)
+      for (size_t j = i + 1; j < list->size(); ++j)
+        if ((*list)[i].l == (*list)[j].l && (*list)[i].parity == (*list)[j].parity)
+          return fail(E3CONV_ERR_INVALID_ARGUMENT, "duplicate irreps in a block list");
+  p->channels = C;
+  p->lmax = sh_lmax;
+  p->avg = avg_num_neighbors;
+  for (const Irrep& b : p->xin) p->num_x += 2 * b.l + 1;
+  for (const Irrep& b : p->out) p->num_out += 2 * b.l + 1;
+  p->num_y = (sh_lmax + 1) * (sh_lmax + 1);
+  p->paths = e3c::enumerate_paths(p->xin, sh_lmax, p->out);
+  std::vector<char> reached(p->out.size(), 0);
+  for (const HostPath& h : p->paths) reached[h.i3] = 1;
+  for (size_t i = 0; i < reached.size(); ++i)
+    if (!reached[i])
+      return fail(E3CONV_ERR_NO_PATH, "output block " + std::to_string(p->out[i].l) +
+                                          (p->out[i].parity > 0 ? "e" : "o") + " is reached by no path");
+  if ((int)p->paths.size() > e3c::kMaxPaths)
+    return fail(E3CONV_ERR_UNSUPPORTED, "too many paths");
+  for (size_t q = 0; q < p->paths.size(); ++q) {
+    const HostPath& h = p->paths[q];
+    std::vector<double> cg;
+    if (!e3c::real_cg(h.l1, h.l2, h.l3, &cg))
+      return fail(E3CONV_ERR_INTERNAL, "real CG construction failed");
+    const int n1 = 2 * h.l1 + 1, n2 = 2 * h.l2 + 1, n3 = 2 * h.l3 + 1;
+    for (int a = 0; a < n1; ++a)
+      for (int b = 0; b < n2; ++b)
+        for (int c = 0; c < n3; ++c) {
+          const double v = cg[((size_t)a * n2 + b) * n3 + c];
+          if (v == 0.0) continue;
+          p->ix.push_back(h.o1 + a);
+          p->iy.push_back(h.o2 + b);
+          p->ip.push_back((int)q);
+          p->iout.push_back(h.o3 + c);
+          p->val.push_back(v);
+        }
+    p->cg.push_back(std::move(cg));
+  }
+  std::string why;
+  if (!bind_kernels(p.get(), &why) && !why.empty()) return fail(E3CONV_ERR_INTERNAL, why);
+  *plan_out = p.release();
+  return ok();
+}
+
+void e3conv_plan_destroy(e3conv_plan_t plan) { delete plan; }
+
+e3conv_status e3conv_plan_shape(e3conv_plan_t p, int* channels, int* num_x, int* num_y,
+                                int* num_paths, int* num_out) {
+  if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (channels) *channels = p->channels;
+  if (num_x) *num_x = p->num_x;
+  if (num_y) *num_y = p->num_y;
+  if (num_paths) *num_paths = (int)p->paths.size();
+  if (num_out) *num_out = p->num_out;
+  return ok();
+}
+
+e3conv_status e3conv_plan_paths(e3conv_plan_t p, int* l1, int* p1, int* l2, int* l3, int* p3,
+                                int* o1, int* o2, int* o3) {
+  if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+  for (size_t q = 0; q < p->paths.size(); ++q) {
+    const HostPath& h = p->paths[q];
+    if (l1) l1[q] = h.l1;
+    if (p1) p1[q] = h.p1;
+    if (l2) l2[q] = h.l2;
+    if (l3) l3[q] = h.l3;
+    if (p3) p3[q] = h.p3;
+    if (o1) o1[q] = h.o1;
+    if (o2) o2[q] = h.o2;
+    if (o3) o3[q] = h.o3;
+  }
+  return ok();
+}
+
+e3conv_status e3conv_plan_coefficients(e3conv_plan_t p, int* nnz, int* ix, int* iy, int* ip,
+                                       int* iout, double* value) {
+  if (!p || !nnz) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan or nnz is NULL");
+  *nnz = (int)p->val.size();
+  for (size_t q = 0; q < p->val.size(); ++q) {
+    if (ix) ix[q] = p->ix[q];
+    if (iy) iy[q] = p->iy[q];
+    if (ip) ip[q] = p->ip[q];
+    if (iout) iout[q] = p->iout[q];
+    if (value) value[q] = p->val[q];
+  }
+  return ok();
+}
+
+e3conv_status e3conv_plan_supported(e3conv_plan_t p, int* fwd_f32, int* fwd_bf16, int* bwd_f32) {
+  if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (fwd_f32) *fwd_f32 = p->ks && p->ks->n_fwd_f32 > 0;
+  if (fwd_bf16) *fwd_bf16 = p->ks && p->ks->n_fwd_bf16 > 0;
+  if (bwd_f32) *bwd_f32 = p->ks && p->ks->n_bwd_f32 > 0;
+  return ok();
+}
+
+e3conv_status e3conv_plan_num_variants(e3conv_plan_t p, e3conv_dtype dt, int* nf, int* nb) {
+  if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (dt != E3CONV_F32 && dt != E3CONV_BF16) return fail(E3CONV_ERR_INVALID_ARGUMENT, "bad dtype");
+  if (nf) *nf = p->ks ? (dt == E3CONV_F32 ? p->ks->n_fwd_f32 : p->ks->n_fwd_bf16) : 0;
+  if (nb) *nb = p->ks ? (dt == E3CONV_F32 ? p->ks->n_bwd_f32 : 0) : 0;
+  return ok();
+}
+
+e3conv_status e3conv_plan_set_variant(e3conv_plan_t p, int fv, int bv) {
+  if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!p->ks) return fail(E3CONV_ERR_UNSUPPORTED, "no kernels for this layout");
+  const int maxf = p->ks->n_fwd_f32 > p->ks->n_fwd_bf16 ? p->ks->n_fwd_f32 : p->ks->n_fwd_bf16;
+  if (fv < 0 || fv >= maxf || bv < 0 || bv >= (p->ks->n_bwd_f32 > 0 ? p->ks->n_bwd_f32 : 1))
+    return fail(E3CONV_ERR_UNSUPPORTED, "unknown kernel variant");
+  p->fwd_variant = fv;
+  p->bwd_variant = bv;
+  return ok();
+}
+
+static e3conv_status check_sizes(int64_t N, int64_t E, int channels, int width) {
+  if (N < 0 || E < 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "negative size");
+  if (E >= (int64_t)1 << 31 || N >= ((int64_t)1 << 31) - 1)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "sizes must fit int32 indices");
+  if (N * (int64_t)width * channels >= (int64_t)1 << 31)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "node tensor exceeds 2^31 elements");
+  return E3CONV_OK;
+}
+
+e3conv_status e3conv_forward(e3conv_plan_t p, e3conv_dtype dt, const void* x, const void* y,
+                             const void* s, const int32_t* src, const int32_t* row_ptr,
+                             int64_t N, int64_t E, float* out, void* stream) {
+  if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (dt != E3CONV_F32 && dt != E3CONV_BF16) return fail(E3CONV_ERR_INVALID_ARGUMENT, "bad dtype");
+  e3conv_status st = check_sizes(N, E, p->channels, p->num_out > p->num_x ? p->num_out : p->num_x);
+  if (st != E3CONV_OK) return st;
+  if (N == 0) return ok();
+  if (!out || !row_ptr || (E > 0 && (!x || !y || !s || !src)))
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  if (!p->ks) return fail(E3CONV_ERR_UNSUPPORTED, "no compiled kernel for this layout");
+  const int n = dt == E3CONV_F32 ? p->ks->n_fwd_f32 : p->ks->n_fwd_bf16;
+  if (n == 0) return fail(E3CONV_ERR_UNSUPPORTED, "no compiled kernel for this dtype");
+  const e3c::FwdLauncher* L = dt == E3CONV_F32 ? p->ks->fwd_f32 : p->ks->fwd_bf16;
+  const int v = p->fwd_variant < n ? p->fwd_variant : 0;
+  e3c::FwdParams prm{x, y, s, src, row_ptr, out, (int)N, (int)E, 1.0f / p->avg};
+  const hipError_t err = L[v](prm, p->kcoef.data(), static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "forward launch");
+  return ok();
+}
+
+e3conv_status e3conv_backward_workspace_size(e3conv_plan_t p, int64_t N, int64_t E, size_t* bytes) {
+  if (!p || !bytes) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan or bytes is NULL");
+  if (N < 0 || E < 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "negative size");
+  *bytes = 0;
+  return ok();
+}
+
+e3conv_status e3conv_backward(e3conv_plan_t p, e3conv_dtype dt, const void* x, const void* y,
+                              const void* s, const int32_t* src, const int32_t* row_ptr,
+                              int64_t N, int64_t E, const float* g, float* gx, float* gy,
+                              float* gs, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (dt != E3CONV_F32) return fail(E3CONV_ERR_UNSUPPORTED, "the reverse pass is fp32 only");
+  e3conv_status st = check_sizes(N, E, p->channels, p->num_out > p->num_x ? p->num_out : p->num_x);
+  if (st != E3CONV_OK) return st;
+  if (!gx && !gy && !gs) return ok();
+  if (N == 0) return ok();
+  if (!gx || !g || !row_ptr || (E > 0 && (!x || !y || !s || !src || !gy || !gs)))
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  if (!p->ks || p->ks->n_bwd_f32 == 0)
+    return fail(E3CONV_ERR_UNSUPPORTED, "no compiled reverse kernel for this layout");
+  const int v = p->bwd_variant < p->ks->n_bwd_f32 ? p->bwd_variant : 0;
+  e3c::BwdParams prm{static_cast<const float*>(x), static_cast<const float*>(y),
+                     static_cast<const float*>(s), src, row_ptr, g, gx, gy, gs, (int)N, (int)E,
+                     1.0f / p->avg};
+  const hipError_t err = p->ks->bwd_f32[v](prm, p->kcoef.data(), static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "backward launch");
+  return ok();
+}
+
+e3conv_status e3conv_csr_from_receivers(const int32_t* dst, int64_t E, int64_t N, int32_t* row_ptr,
+                                        void* stream) {
+  if (N < 0 || E < 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "negative size");
+  if (E >= (int64_t)1 << 31 || N >= ((int64_t)1 << 31) - 1)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "sizes must fit int32 indices");
+  if (!row_ptr || (E > 0 && !dst)) return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  const hipError_t err =
+      e3c::launch_csr_from_receivers(dst, (int)E, (int)N, row_ptr, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "csr launch");
+  return ok();
+}
+
+e3conv_status e3conv_validate_graph(const int32_t* src, const int32_t* row_ptr, int64_t N,
+                                    int64_t E, int on_device) {
+  if (N < 0 || E < 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "negative size");
+  if (E >= (int64_t)1 << 31 || N >= ((int64_t)1 << 31) - 1)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "sizes must fit int32 indices");
+  if (!row_ptr || (E > 0 && !src)) return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!on_device) {
+    if (row_ptr[0] != 0) return fail(E3CONV_ERR_GRAPH, "row_ptr[0] != 0");
+    if (row_ptr[N] != E) return fail(E3CONV_ERR_GRAPH, "row_ptr[num_nodes] != num_edges");
+    for (int64_t i = 0; i < N; ++i)
+      if (row_ptr[i + 1] < row_ptr[i] || row_ptr[i + 1] > E)
+        return fail(E3CONV_ERR_GRAPH, "row_ptr decreases or overflows at node " + std::to_string(i));
+    for (int64_t e = 0; e < E; ++e)
+      if (src[e] < 0 || src[e] >= N)
+        return fail(E3CONV_ERR_GRAPH, "sender out of range at edge " + std::to_string(e));
+    return ok();
+  }
+  int* bad = nullptr;
+  hipError_t err = hipMalloc(&bad, sizeof(int));
+  if (err != hipSuccess) return hip_fail(err, "hipMalloc");
+  int host_bad = 0;
+  err = hipMemcpy(bad, &host_bad, sizeof(int), hipMemcpyHostToDevice);
+  if (err == hipSuccess) err = e3c::launch_validate_graph(src, row_ptr, (int)N, (int)E, bad, nullptr);
+  if (err == hipSuccess) err = hipMemcpy(&host_bad, bad, sizeof(int), hipMemcpyDeviceToHost);
+  hipFree(bad);
+  if (err != hipSuccess) return hip_fail(err, "validate");
+  if (host_bad) return fail(E3CONV_ERR_GRAPH, std::to_string(host_bad) + " violations in the graph");
+  return ok();
+}
+
+}  // extern "C"

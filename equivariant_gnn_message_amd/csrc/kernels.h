@@ -1,0 +1,66 @@
+// Device-kernel registry: one set of fused kernels per compiled irrep layout.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "layout.h"
+
+namespace e3c {
+
+struct FwdParams {
+  const void* x;        // (N, NX, C) f32 or bf16 bits
+  const void* y;        // (E, NY)
+  const void* s;        // (E, NP, C)
+  const int* src;       // (E)
+  const int* row_ptr;   // (N+1)
+  float* out;           // (N, NO, C)
+  int num_nodes;
+  int num_edges;
+  float inv_avg;
+};
+
+struct BwdParams {
+  const float* x;
+  const float* y;
+  const float* s;
+  const int* src;
+  const int* row_ptr;
+  const float* g;       // (N, NO, C) cotangent of out
+  float* gx;            // (N, NX, C), zeroed by the launcher then accumulated
+  float* gy;            // (E, NY)
+  float* gs;            // (E, NP, C)
+  int num_nodes;
+  int num_edges;
+  float inv_avg;
+};
+
+using FwdLauncher = hipError_t (*)(const FwdParams&, const float* coef, hipStream_t);
+using BwdLauncher = hipError_t (*)(const BwdParams&, const float* coef, hipStream_t);
+
+struct KernelSet {
+  int channels;
+  uint32_t xcode;
+  int lmax;
+  uint32_t ocode;
+  const LayoutTables* tables;   // path / pattern enumeration the kernels use
+  const FwdLauncher* fwd_f32;
+  int n_fwd_f32;
+  const FwdLauncher* fwd_bf16;
+  int n_fwd_bf16;
+  const BwdLauncher* bwd_f32;
+  int n_bwd_f32;
+};
+
+// Returns nullptr if no kernels are compiled for the layout.
+const KernelSet* find_kernels(int channels, uint32_t xcode, int lmax, uint32_t ocode);
+
+hipError_t launch_csr_from_receivers(const int* dst, int num_edges, int num_nodes, int* row_ptr,
+                                     hipStream_t stream);
+
+// Writes into *bad (device int, pre-zeroed by the launcher) the count of violations.
+hipError_t launch_validate_graph(const int* src, const int* row_ptr, int num_nodes, int num_edges,
+                                 int* bad, hipStream_t stream);
+
+}  // namespace e3c

@@ -1,0 +1,178 @@
+/*
+ * e3conv -- equivariant message-passing convolution on AMD MI355X (gfx950).
+ *
+ * The operation (e3j "Convolution" API page, class formula and the four-step
+ * plain implementation beneath it):
+ *
+ *     out[b] = (1/N) * sum over edges e = (a -> b) of  (x[a] (x) y[e]) (.) s[e]
+ *
+ * - x  node features, shape (num_nodes, num_x, C), trailing channel axis
+ *      ("TRAILING_CHANNELS" layout of that page);
+ * - y  edge features (spherical harmonics 0..sh_lmax), shape (num_edges, num_y),
+ *      no channel axis, broadcast over channels;
+ * - s  edge scalars, shape (num_edges, num_paths, C): one value per
+ *      (path, channel), the "third source space" the page infers from x and y;
+ * - (x) the channelwise Clebsch-Gordan tensor product, one path per allowed
+ *      (x block, l2, output block) triple; (.) the per-(path, channel) mixing;
+ * - the sum runs over the incoming edges of receiver b (RECEIVER ordering of
+ *      that page: edges sorted by receiver, so aggregation is a segmented sum);
+ * - N = avg_num_neighbors ("messages are divided by this factor").
+ *
+ * Conventions (readings of the pages; the pages print no formula for them):
+ * - components: blocks in the order given, m = -l..l inside a block, real
+ *   spherical-harmonic basis with z as polar axis (l=1 is (y, z, x));
+ * - a path (l1,p1) x l2 -> (l3,p3) exists iff |l1-l2| <= l3 <= l1+l2 and
+ *   p3 = p1 (-1)^l2; paths are ordered x block, then l2 = 0..sh_lmax, then
+ *   output block, which is the order of the s scalar axis;
+ * - the CG tensor of each path is the real, orthonormal one
+ *   (sum_{m1,m2} C[m1,m2,m3] C[m1,m2,m3'] = delta), sign fixed so that its first
+ *   nonzero entry in (m1, m2, m3) order is positive ("SQRT_DIM_OUT"
+ *   normalization named on the e3j page);
+ * - paths into the same output block add up.
+ *
+ * Memory and streams: every device pointer is owned by the caller; the library
+ * never allocates device memory.  Tensors are dense, row-major, at least
+ * 16-byte aligned.  Indices are int32.  All device work is enqueued on the
+ * caller's hipStream_t (passed as void*), asynchronously, with no implicit
+ * synchronisation.  Errors are reported by status code; a human-readable
+ * message for the last error on the calling thread is available from
+ * e3conv_last_error_detail().  No C++ exception crosses this boundary.
+ */
+#ifndef E3CONV_H
+#define E3CONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct e3conv_plan_s* e3conv_plan_t;
+
+typedef enum {
+  E3CONV_OK = 0,
+  E3CONV_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad dtype */
+  E3CONV_ERR_PARSE = 2,            /* malformed irreps string                 */
+  E3CONV_ERR_UNSUPPORTED = 3,      /* no compiled kernel for this layout/dtype */
+  E3CONV_ERR_NO_PATH = 4,          /* an output block is reached by no path   */
+  E3CONV_ERR_GRAPH = 5,            /* graph failed validation                 */
+  E3CONV_ERR_WORKSPACE = 6,        /* workspace too small                     */
+  E3CONV_ERR_HIP = 7,              /* a HIP runtime call or launch failed     */
+  E3CONV_ERR_INTERNAL = 8          /* host CG table disagrees with the kernel pattern */
+} e3conv_status;
+
+typedef enum { E3CONV_F32 = 0, E3CONV_BF16 = 1 } e3conv_dtype;
+
+/* Build a plan (host only, no device call).
+ *   irreps_in   x irreps, e.g. "128x0e+128x1o" or "64x(0e+1o+2e)"; every block
+ *               must have the same multiplicity C (the channel count);
+ *   sh_lmax     edge features are spherical harmonics l = 0..sh_lmax (num_y =
+ *               (sh_lmax+1)^2), 0 <= sh_lmax <= 6;
+ *   irreps_out  output irreps (same multiplicity C); acts as the filter on
+ *               output blocks ("target" on the e3j page);
+ *   avg_num_neighbors  N > 0; pass 1 for no rescaling.
+ * Irreps have l <= 6.  Duplicate irreps, mixed multiplicities and output blocks
+ * no path reaches are rejected.  A plan whose layout has no compiled kernel is
+ * still created (its tables can be queried); e3conv_forward/_backward then
+ * return E3CONV_ERR_UNSUPPORTED.  On success *plan_out owns the plan; free it
+ * with e3conv_plan_destroy.  Plans are immutable and thread-safe. */
+e3conv_status e3conv_plan(const char* irreps_in, int sh_lmax, const char* irreps_out,
+                          float avg_num_neighbors, e3conv_plan_t* plan_out);
+
+void e3conv_plan_destroy(e3conv_plan_t plan);
+
+/* Per-channel sizes of the operands: x (N, num_x, C), y (E, num_y),
+ * s (E, num_paths, C), out (N, num_out, C).  Any pointer may be NULL. */
+e3conv_status e3conv_plan_shape(e3conv_plan_t plan, int* channels, int* num_x, int* num_y,
+                                int* num_paths, int* num_out);
+
+/* Path table, one entry per path in s-axis order: l and parity of the x block,
+ * l2 of the edge harmonic, l and parity of the output block, and the component
+ * offsets of the three blocks.  Each array has num_paths entries; any may be NULL. */
+e3conv_status e3conv_plan_paths(e3conv_plan_t plan, int* l1, int* p1, int* l2, int* l3,
+                                int* p3, int* o1, int* o2, int* o3);
+
+/* Packed coefficients (the e3j "coef" attribute read as a sparse 4-index list):
+ * out[b, iout, c] += value * x[a, ix, c] * y[e, iy] * s[e, ip, c] / N.
+ * Call with NULL arrays to get *nnz; then call again with arrays of *nnz
+ * entries.  Entries are the nonzero real CG values in fp64. */
+e3conv_status e3conv_plan_coefficients(e3conv_plan_t plan, int* nnz, int* ix, int* iy,
+                                       int* ip, int* iout, double* value);
+
+/* Whether compiled kernels exist for this plan: forward for f32 and bf16
+ * inputs, backward (f32).  Any pointer may be NULL. */
+e3conv_status e3conv_plan_supported(e3conv_plan_t plan, int* fwd_f32, int* fwd_bf16, int* bwd_f32);
+
+/* Forward convolution.
+ *   in_dtype  storage type of x, y and s (E3CONV_F32 or E3CONV_BF16: bf16 is
+ *             read as raw 16-bit words); accumulation and out are fp32;
+ *   x, y, s   device pointers, shapes above;
+ *   src       device int32[num_edges]: sender of each edge, in [0, num_nodes);
+ *   row_ptr   device int32[num_nodes + 1]: receiver CSR offsets, row_ptr[0] = 0,
+ *             row_ptr[num_nodes] = num_edges; edges of receiver b are
+ *             row_ptr[b] .. row_ptr[b+1]-1 (y and s rows in that order);
+ *   out       device float[num_nodes * num_out * C], fully overwritten (rows of
+ *             receivers without edges are set to zero);
+ *   hip_stream  hipStream_t or NULL for the default stream.
+ * Indices out of range or a non-monotone row_ptr are undefined behaviour (the
+ * fused kernels need sorted edges, as on the e3j page); check them once per
+ * graph with e3conv_validate_graph.  num_edges = 0 is valid (out is zeroed);
+ * num_nodes = 0 is a no-op.  Sizes must satisfy num_edges < 2^31 and
+ * num_nodes * num_out * C < 2^31. */
+e3conv_status e3conv_forward(e3conv_plan_t plan, e3conv_dtype in_dtype, const void* x,
+                             const void* y, const void* s, const int32_t* src,
+                             const int32_t* row_ptr, int64_t num_nodes, int64_t num_edges,
+                             float* out, void* hip_stream);
+
+/* Bytes of device workspace e3conv_backward needs (currently 0). */
+e3conv_status e3conv_backward_workspace_size(e3conv_plan_t plan, int64_t num_nodes,
+                                             int64_t num_edges, size_t* bytes);
+
+/* Reverse pass of L = <grad_out, out> (fp32 only): given grad_out (N, num_out, C)
+ * writes grad_x (N, num_x, C), grad_y (E, num_y) and grad_s (E, num_paths, C).
+ * Same graph arguments and rules as e3conv_forward.  grad_x is fully
+ * overwritten (zeroed, then accumulated across the edges leaving each node with
+ * fp32 device atomics, so its rounding may vary from run to run); grad_y and
+ * grad_s are written once per edge.  If grad_x, grad_y and grad_s are all
+ * NULL the call does nothing; otherwise grad_x and grad_out are required, and
+ * grad_y, grad_s, x, y, s and src are required when num_edges > 0 (they may
+ * be NULL for an edgeless graph).  workspace may be NULL when the size is 0. */
+e3conv_status e3conv_backward(e3conv_plan_t plan, e3conv_dtype in_dtype, const void* x,
+                              const void* y, const void* s, const int32_t* src,
+                              const int32_t* row_ptr, int64_t num_nodes, int64_t num_edges,
+                              const float* grad_out, float* grad_x, float* grad_y,
+                              float* grad_s, void* workspace, size_t workspace_bytes,
+                              void* hip_stream);
+
+/* Receiver CSR on the device: row_ptr[b] = first edge whose receiver is >= b,
+ * for b = 0..num_nodes, from the receiver of each edge (device int32[num_edges],
+ * non-decreasing).  One thread per node, binary search; asynchronous. */
+e3conv_status e3conv_csr_from_receivers(const int32_t* receivers_sorted, int64_t num_edges,
+                                        int64_t num_nodes, int32_t* row_ptr, void* hip_stream);
+
+/* Check a graph: row_ptr[0] = 0, non-decreasing, row_ptr[num_nodes] = num_edges,
+ * every src in [0, num_nodes).  on_device = 0: host pointers; 1: device
+ * pointers (runs a kernel on the default stream and waits for it).  Returns
+ * E3CONV_OK or E3CONV_ERR_GRAPH with the first offending index in the detail. */
+e3conv_status e3conv_validate_graph(const int32_t* src, const int32_t* row_ptr,
+                                    int64_t num_nodes, int64_t num_edges, int on_device);
+
+/* Tuning: select a kernel variant for this plan (0 = default).  Variants
+ * differ only in how lanes map to channels and edges; all compute the same
+ * result.  Returns E3CONV_ERR_UNSUPPORTED for an unknown variant.  Plans are
+ * otherwise immutable; set variants before sharing a plan across threads. */
+e3conv_status e3conv_plan_set_variant(e3conv_plan_t plan, int forward_variant, int backward_variant);
+
+/* Number of forward / backward variants compiled for this plan's layout. */
+e3conv_status e3conv_plan_num_variants(e3conv_plan_t plan, e3conv_dtype in_dtype,
+                                       int* forward_variants, int* backward_variants);
+
+const char* e3conv_status_string(e3conv_status status);
+const char* e3conv_last_error_detail(void);   /* thread-local, never NULL */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* E3CONV_H */

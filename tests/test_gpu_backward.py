@@ -1,0 +1,155 @@
+"""GPU parity of the fused reverse pass against the CPU oracle (through the C ABI).
+
+Bar: for each of grad_x, grad_y, grad_s, max|gpu - oracle| <= 1e-5 RMS(oracle).
+"""
+
+import numpy as np
+import pytest
+
+from oracle import conv
+from equivariant_gnn_message_amd import e3conv as E
+from equivariant_gnn_message_amd import synth
+
+from ._gpu import device_inputs, plan_for, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_layout(inp):
+    w = inp.workload
+    return conv.make_layout(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+
+
+def with_cotangent(idx, n=None):
+    inp = synth.make_inputs(idx, num_nodes=n, with_cotangent=True) if n else synth.make_inputs(idx, with_cotangent=True)
+    if inp.x.dtype == np.uint16:   # the reverse pass is fp32: feed the decoded values
+        inp.x, inp.y, inp.s = inp.as_f32("x"), inp.as_f32("y"), inp.as_f32("s")
+    return inp
+
+
+@pytest.mark.parametrize("idx,n", [(0, None), (1, None), (4, 401), (3, 201)],
+                         ids=["w0", "w1", "w4-n401", "w3f32-n201"])
+def test_backward_parity_all_variants(idx, n):
+    import torch
+    inp = with_cotangent(idx, n)
+    say(f"[backward] workload {idx} N={inp.num_nodes} E={inp.num_edges}")
+    dx_r, dy_r, ds_r = conv.backward(oracle_layout(inp), inp.x, inp.y, inp.s, inp.g, inp.senders,
+                                     inp.receivers, inp.num_nodes)
+    d = device_inputs(inp)
+    plan = plan_for(inp)
+    _, nb = plan.num_variants(E.E3CONV_F32)
+    for v in range(nb):
+        plan.set_variant(0, v)
+        say(f"  variant {v}")
+        gx, gy, gs = plan.backward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"], d["g"])
+        torch.cuda.synchronize()
+        errs = [rel_err(a.cpu().numpy(), b) for a, b in ((gx, dx_r), (gy, dy_r), (gs, ds_r))]
+        say(f"  max|err|/RMS dx {errs[0]:.3e} dy {errs[1]:.3e} ds {errs[2]:.3e}")
+        assert max(errs) <= 1e-5, (v, errs)
+
+
+def test_backward_overwrites_grad_x():
+    import torch
+    inp = with_cotangent(4, 201)
+    d = device_inputs(inp)
+    plan = plan_for(inp)
+    a = plan.backward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"], d["g"])
+    grads = tuple(torch.full_like(t, 3.0) for t in a)
+    b = plan.backward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"], d["g"], grads=grads)
+    for u, w in zip(a, b):
+        assert rel_err(w.cpu().numpy(), u.cpu().numpy()) <= 1e-6
+
+
+def test_backward_zero_edges():
+    import torch
+    inp = with_cotangent(4, 201)
+    lay = oracle_layout(inp)
+    plan = plan_for(inp)
+    N = 13
+    dst = torch.zeros(0, dtype=torch.int32, device="cuda")
+    row_ptr = E.e3conv_csr_from_receivers(dst, N)
+    x = torch.randn(N, lay.num_x, lay.channels, device="cuda")
+    g = torch.randn(N, lay.num_out, lay.channels, device="cuda")
+    y = torch.zeros(0, lay.num_y, device="cuda")
+    s = torch.zeros(0, lay.num_paths, lay.channels, device="cuda")
+    gx = torch.full_like(x, 5.0)
+    gy, gs = torch.zeros_like(y), torch.zeros_like(s)
+    plan.backward(x, y, s, dst, row_ptr, g, grads=(gx, gy, gs))
+    torch.cuda.synchronize()
+    assert float(gx.abs().max()) == 0.0
+
+
+def test_backward_full_size():
+    """Training workload at full size: sampled oracle rows and the trilinear identity."""
+    import torch
+    inp = synth.make_inputs(4)
+    say(f"[backward full size] N={inp.num_nodes} E={inp.num_edges}")
+    lay = oracle_layout(inp)
+    d = device_inputs(inp)
+    plan = plan_for(inp)
+    out = plan.forward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"])
+    gx, gy, gs = plan.backward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"], d["g"])
+    torch.cuda.synchronize()
+    # trilinear identity: <g, out> = <gx, x> = <gy, y> = <gs, s>
+    L = float((d["g"].double() * out.double()).sum())
+    for grad, arg in ((gx, d["x"]), (gy, d["y"]), (gs, d["s"])):
+        val = float((grad.double() * arg.double()).sum())
+        say(f"  <g,out> {L:.6e} vs {val:.6e}")
+        assert abs(val - L) <= 1e-5 * abs(L)
+    # sampled edges: grad_s and grad_y rows
+    rng = np.random.default_rng(11)
+    eids = np.sort(rng.choice(inp.num_edges, size=512, replace=False))
+    ds_r, dy_r, _ = conv.edge_grads(lay, inp.x, inp.y[eids], inp.s[eids], inp.g, inp.senders[eids],
+                                    inp.receivers[eids])
+    te = torch.from_numpy(eids).cuda()
+    assert rel_err(gs[te].cpu().numpy(), ds_r) <= 1e-5
+    assert rel_err(gy[te].cpu().numpy(), dy_r) <= 1e-5
+    # sampled senders: every edge leaving them
+    nodes = np.sort(rng.choice(inp.num_nodes, size=48, replace=False))
+    sel = np.flatnonzero(np.isin(inp.senders, nodes))
+    _, _, dxe = conv.edge_grads(lay, inp.x, inp.y[sel], inp.s[sel], inp.g, inp.senders[sel],
+                                inp.receivers[sel])
+    dx_r = np.zeros((inp.num_nodes, lay.num_x, lay.channels))
+    np.add.at(dx_r, inp.senders[sel], dxe)
+    got = gx[torch.from_numpy(nodes).cuda()].cpu().numpy()
+    err = rel_err(got, dx_r[nodes])
+    say(f"  sampled grad_x rows max|err|/RMS {err:.3e}")
+    assert err <= 1e-5
+
+
+def test_backward_finite_differences_subgraph():
+    """Directional central differences of the GPU forward on the 16-node subgraph."""
+    import torch
+    full = synth.make_inputs(4, num_nodes=3000)
+    nodes, eids, src, dst = synth.subgraph16(full)
+    w = full.workload
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    x, y, s, g = t(full.x[nodes]), t(full.y[eids]), t(full.s[eids]), t(full.g[nodes])
+    srcd, dstd = t(src), t(dst)
+    row_ptr = E.e3conv_csr_from_receivers(dstd, len(nodes))
+    L = lambda x_, y_, s_: float((g.double() * plan.forward(x_, y_, s_, srcd, row_ptr).double()).sum())
+    gx, gy, gs = plan.backward(x, y, s, srcd, row_ptr, g)
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    for arg, grad, which in ((x, gx, 0), (y, gy, 1), (s, gs, 2)):
+        for _ in range(4):
+            dvec = torch.randn(arg.shape, device="cuda", generator=gen)
+            args_p, args_m = [x, y, s], [x, y, s]
+            args_p[which] = arg + dvec
+            args_m[which] = arg - dvec
+            fd = (L(*args_p) - L(*args_m)) / 2
+            an = float((grad.double() * dvec.double()).sum())
+            assert abs(fd - an) <= 1e-4 * max(1.0, abs(an)), (which, fd, an)
+
+
+def test_autograd_function_matches_plan():
+    import torch
+    inp = with_cotangent(4, 201)
+    d = device_inputs(inp)
+    plan = plan_for(inp)
+    xs = [d[k].clone().requires_grad_(True) for k in ("x", "y", "s")]
+    out = E.E3ConvFunction.apply(plan, xs[0], xs[1], xs[2], d["src"], d["row_ptr"])
+    grads = torch.autograd.grad(out, xs, grad_outputs=d["g"])
+    want = plan.backward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"], d["g"])
+    for a, b in zip(grads, want):
+        assert rel_err(a.cpu().numpy(), b.cpu().numpy()) <= 1e-6
