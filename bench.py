@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--fwd-variant", type=int, default=0)
     ap.add_argument("--bwd-variant", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-order", action="store_true",
+                    help="process receivers in index order (no locality schedule)")
+    ap.add_argument("--cluster", type=int, default=512, help="receivers per locality cluster")
     ap.add_argument("--cpu-sample-edges", type=int, default=12000)
     ap.add_argument("--sweep", action="store_true",
                     help="time every compiled kernel variant (one JSON line each) and exit")
@@ -58,8 +61,8 @@ def calibrate_copy(mib, reps=5):
     print(json.dumps({"calibrate_copy_bytes": n * 4, "reps": reps}), flush=True)
 
 
-def sweep(plan, w, run_fwd, run_bwd, nbytes, reps=10):
-    """Average HIP-event time of every compiled variant."""
+def sweep(plan, w, run_fwd, run_bwd, nbytes, orders, reps=10):
+    """Average HIP-event time of every compiled variant, with each receiver order."""
     import numpy as np
     import torch
     from equivariant_gnn_message_amd import e3conv as E
@@ -67,20 +70,22 @@ def sweep(plan, w, run_fwd, run_bwd, nbytes, reps=10):
     nf, nb = plan.num_variants(dt)
     for kind, n, run, by in (("fwd", nf, run_fwd, nbytes[0]), ("bwd", nb if w.backward else 0, run_bwd, nbytes[1])):
         for v in range(n):
-            plan.set_variant(v if kind == "fwd" else 0, v if kind == "bwd" else 0)
-            run()
-            torch.cuda.synchronize()
-            ts = []
-            for _ in range(reps):
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                run()
-                b.record()
-                ts.append((a, b))
-            torch.cuda.synchronize()
-            ms = float(np.mean([a.elapsed_time(b) for a, b in ts]))
-            print(json.dumps({"workload": w.idx, "kernel": kind, "variant": v, "ms": ms,
-                              "GBps": by / ms / 1e6, "frac": by / ms / 1e6 / PEAK_HBM_GBPS}), flush=True)
+            for oname, order in orders:
+                plan.set_variant(v if kind == "fwd" else 0, v if kind == "bwd" else 0)
+                run(order)
+                torch.cuda.synchronize()
+                ts = []
+                for _ in range(reps):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    run(order)
+                    b.record()
+                    ts.append((a, b))
+                torch.cuda.synchronize()
+                ms = float(np.mean([a.elapsed_time(b) for a, b in ts]))
+                print(json.dumps({"workload": w.idx, "kernel": kind, "variant": v, "order": oname,
+                                  "ms": ms, "GBps": by / ms / 1e6,
+                                  "frac": by / ms / 1e6 / PEAK_HBM_GBPS}), flush=True)
 
 
 def alg_bytes(w, N, E, b_in):
@@ -181,12 +186,19 @@ def main():
     plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
     plan.set_variant(args.fwd_variant, args.bwd_variant)
     plan_ms = (time.perf_counter() - tp) * 1e3
+    E.e3conv_csr_from_receivers(dst, N)          # first launch loads the code object
+    torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     row_ptr = E.e3conv_csr_from_receivers(dst, N)
     ev1.record()
     torch.cuda.synchronize()
     csr_ms = ev0.elapsed_time(ev1)
+    to = time.perf_counter()
+    order_np = E.e3conv_receiver_order(row_ptr.cpu().numpy(), inp.senders, N, Ecount, args.cluster)
+    order_ms = (time.perf_counter() - to) * 1e3
+    order_dev = torch.from_numpy(order_np).to(dev)
+    order = None if args.no_order else order_dev
 
     out = torch.empty((N, w.num_out, w.channels), dtype=torch.float32, device=dev)
     grads = None
@@ -199,7 +211,7 @@ def main():
         if record:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-        plan.forward(x, y, s, src, row_ptr, out=out)
+        plan.forward(x, y, s, src, row_ptr, out=out, order=order)
         if record:
             b.record()
             fwd_ev.append((a, b))
@@ -207,16 +219,16 @@ def main():
             if record:
                 c, d = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 c.record()
-            plan.backward(x, y, s, src, row_ptr, g, grads=grads)
+            plan.backward(x, y, s, src, row_ptr, g, grads=grads, order=order)
             if record:
                 d.record()
                 bwd_ev.append((c, d))
 
     if args.sweep:
         b_in = 2 if w.dtype == "bf16" else 4
-        sweep(plan, w, lambda: plan.forward(x, y, s, src, row_ptr, out=out),
-              lambda: plan.backward(x, y, s, src, row_ptr, g, grads=grads),
-              alg_bytes(w, N, Ecount, b_in))
+        sweep(plan, w, lambda o: plan.forward(x, y, s, src, row_ptr, out=out, order=o),
+              lambda o: plan.backward(x, y, s, src, row_ptr, g, grads=grads, order=o),
+              alg_bytes(w, N, Ecount, b_in), [("index", None), ("clustered", order_dev)])
         return
 
     for _ in range(args.warmup):
@@ -257,6 +269,8 @@ def main():
         "fwd_hbm_GBps": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
         "fwd_hbm_frac": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "csr_ms": csr_ms,
+        "order_ms": order_ms,
+        "receiver_order": "index" if args.no_order else f"clustered {args.cluster}",
         "plan_ms": plan_ms,
         "variants": [args.fwd_variant, args.bwd_variant],
     }

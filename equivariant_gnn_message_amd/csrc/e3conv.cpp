@@ -279,7 +279,7 @@ static e3conv_status check_sizes(int64_t N, int64_t E, int channels, int width) 
 
 e3conv_status e3conv_forward(e3conv_plan_t p, e3conv_dtype dt, const void* x, const void* y,
                              const void* s, const int32_t* src, const int32_t* row_ptr,
-                             int64_t N, int64_t E, float* out, void* stream) {
+                             const int32_t* order, int64_t N, int64_t E, float* out, void* stream) {
   if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (dt != E3CONV_F32 && dt != E3CONV_BF16) return fail(E3CONV_ERR_INVALID_ARGUMENT, "bad dtype");
   e3conv_status st = check_sizes(N, E, p->channels, p->num_out > p->num_x ? p->num_out : p->num_x);
@@ -292,7 +292,7 @@ e3conv_status e3conv_forward(e3conv_plan_t p, e3conv_dtype dt, const void* x, co
   if (n == 0) return fail(E3CONV_ERR_UNSUPPORTED, "no compiled kernel for this dtype");
   const e3c::FwdLauncher* L = dt == E3CONV_F32 ? p->ks->fwd_f32 : p->ks->fwd_bf16;
   const int v = p->fwd_variant < n ? p->fwd_variant : 0;
-  e3c::FwdParams prm{x, y, s, src, row_ptr, out, (int)N, (int)E, 1.0f / p->avg};
+  e3c::FwdParams prm{x, y, s, src, row_ptr, order, out, (int)N, (int)E, 1.0f / p->avg};
   const hipError_t err = L[v](prm, p->kcoef.data(), static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "forward launch");
   return ok();
@@ -307,7 +307,8 @@ e3conv_status e3conv_backward_workspace_size(e3conv_plan_t p, int64_t N, int64_t
 
 e3conv_status e3conv_backward(e3conv_plan_t p, e3conv_dtype dt, const void* x, const void* y,
                               const void* s, const int32_t* src, const int32_t* row_ptr,
-                              int64_t N, int64_t E, const float* g, float* gx, float* gy,
+                              const int32_t* order, int64_t N, int64_t E, const float* g,
+                              float* gx, float* gy,
                               float* gs, void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
@@ -323,7 +324,7 @@ e3conv_status e3conv_backward(e3conv_plan_t p, e3conv_dtype dt, const void* x, c
     return fail(E3CONV_ERR_UNSUPPORTED, "no compiled reverse kernel for this layout");
   const int v = p->bwd_variant < p->ks->n_bwd_f32 ? p->bwd_variant : 0;
   e3c::BwdParams prm{static_cast<const float*>(x), static_cast<const float*>(y),
-                     static_cast<const float*>(s), src, row_ptr, g, gx, gy, gs, (int)N, (int)E,
+                     static_cast<const float*>(s), src, row_ptr, order, g, gx, gy, gs, (int)N, (int)E,
                      1.0f / p->avg};
   const hipError_t err = p->ks->bwd_f32[v](prm, p->kcoef.data(), static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "backward launch");
@@ -339,6 +340,20 @@ e3conv_status e3conv_csr_from_receivers(const int32_t* dst, int64_t E, int64_t N
   const hipError_t err =
       e3c::launch_csr_from_receivers(dst, (int)E, (int)N, row_ptr, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "csr launch");
+  return ok();
+}
+
+e3conv_status e3conv_receiver_order(const int32_t* row_ptr, const int32_t* src, int64_t N,
+                                    int64_t E, int cluster, int32_t* order) {
+  if (N < 0 || E < 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "negative size");
+  if (E >= (int64_t)1 << 31 || N >= ((int64_t)1 << 31) - 1)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "sizes must fit int32 indices");
+  if (cluster <= 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "cluster must be positive");
+  if (N == 0) return ok();
+  if (!row_ptr || !order || (E > 0 && !src)) return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL pointer");
+  const e3conv_status st = e3conv_validate_graph(src, row_ptr, N, E, 0);
+  if (st != E3CONV_OK) return st;
+  e3c::receiver_order(row_ptr, src, (int)N, cluster, order);
   return ok();
 }
 

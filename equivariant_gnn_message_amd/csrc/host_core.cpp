@@ -251,4 +251,35 @@ bool real_cg(int l1, int l2, int l3, std::vector<double>* out) {
   return true;
 }
 
+// ---------------------------------------------------------- scheduling --
+
+void receiver_order(const int* row_ptr, const int* src, int num_nodes, int cluster, int* order) {
+  std::vector<char> seen((size_t)num_nodes, 0);
+  std::vector<int> queue;
+  queue.reserve((size_t)cluster * 64);
+  int out = 0;
+  for (int seed = 0; seed < num_nodes; ++seed) {
+    if (seen[seed]) continue;
+    queue.clear();
+    queue.push_back(seed);
+    seen[seed] = 1;
+    int taken = 0;
+    size_t head = 0;
+    while (head < queue.size() && taken < cluster) {
+      const int v = queue[head++];
+      order[out++] = v;
+      ++taken;
+      for (int e = row_ptr[v]; e < row_ptr[v + 1]; ++e) {
+        const int a = src[e];
+        if (!seen[a]) {
+          seen[a] = 1;
+          queue.push_back(a);
+        }
+      }
+    }
+    // nodes queued but not taken go back to the pool
+    for (size_t i = head; i < queue.size(); ++i) seen[queue[i]] = 0;
+  }
+}
+
 }  // namespace e3c

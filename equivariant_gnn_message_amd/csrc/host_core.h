@@ -34,4 +34,9 @@ std::vector<HostPath> enumerate_paths(const std::vector<Irrep>& xin, int lmax,
 // rule; returns false otherwise.
 bool real_cg(int l1, int l2, int l3, std::vector<double>* out);
 
+// Receiver processing order for gather locality: greedy breadth-first clusters
+// of about `cluster` receivers over the in-neighbour graph (CSR row_ptr/src),
+// seeds taken in index order.  Writes a permutation of 0..N-1 into order.
+void receiver_order(const int* row_ptr, const int* src, int num_nodes, int cluster, int* order);
+
 }  // namespace e3c

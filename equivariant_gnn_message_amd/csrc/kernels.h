@@ -15,6 +15,7 @@ struct FwdParams {
   const void* s;        // (E, NP, C)
   const int* src;       // (E)
   const int* row_ptr;   // (N+1)
+  const int* order;     // (N) receiver processing order, or nullptr for 0..N-1
   float* out;           // (N, NO, C)
   int num_nodes;
   int num_edges;
@@ -27,6 +28,7 @@ struct BwdParams {
   const float* s;
   const int* src;
   const int* row_ptr;
+  const int* order;     // (N) or nullptr
   const float* g;       // (N, NO, C) cotangent of out
   float* gx;            // (N, NX, C), zeroed by the launcher then accumulated
   float* gy;            // (E, NY)

@@ -75,6 +75,18 @@ struct CoefPack {
   float v[NNZ > 0 ? NNZ : 1];
 };
 
+// Wave index in processing order.  Work-groups are dealt round-robin to the
+// 8 XCDs (8 L2 caches); remapping so that XCD k runs a contiguous range of
+// logical blocks keeps receivers that are processed together (neighbours in
+// the receiver order) on one L2, where their shared senders' rows are reused.
+// The grid is a multiple of 8 work-groups of 4 waves.
+__device__ __forceinline__ int logical_wave() {
+  const int per_xcd = (int)(gridDim.x >> 3);
+  const int bid = (int)blockIdx.x;
+  const int lb = (bid & 7) * per_xcd + (bid >> 3);
+  return __builtin_amdgcn_readfirstlane(lb * 4 + (int)(threadIdx.x >> 6));
+}
+
 // --------------------------------------------------------------- loads ------
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -201,9 +213,9 @@ __global__ void __launch_bounds__(256) conv_fwd(FwdParams prm, CoefPack<LY::NNZ>
   const int grp = lane / LPG;
   const int gi = grp % GPR;
   const int slot = grp / GPR;
-  const int wave = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6));
-  const int b = wave * RPW + slot;
-  const bool valid = b < prm.num_nodes;
+  const int bl = logical_wave() * RPW + slot;
+  const bool valid = bl < prm.num_nodes;
+  const int b = valid ? (prm.order ? prm.order[bl] : bl) : 0;
 
   float acc[NO][CPL];
 #pragma unroll
@@ -289,6 +301,229 @@ __global__ void __launch_bounds__(256) conv_fwd(FwdParams prm, CoefPack<LY::NNZ>
   }
 }
 
+// ------------------------------------------------- pipelined forward --------
+//
+// Same mapping as conv_fwd, with the edge loop software-pipelined: the loads
+// of edge i+1 (y row, s rows, gathered x row) are in flight while edge i is
+// computed, and the sender index is fetched two edges ahead so the gather's
+// address is known when its loads are issued.  Two register buffers alternate
+// (the loop body is unrolled twice), so no per-edge register copies.  Raw
+// values (bf16 words) are kept until use.  Per path the contraction is
+// reassociated as acc[o3+m3] += sum_m1 K[m3][m1] (s[p] x[o1+m1]), which needs
+// (2 l1 + 1) products per path instead of (2 l3 + 1) mixing FMAs.
+
+template <typename IN, int N>
+struct RawVec;
+
+template <int N>
+struct RawVec<float, N> {
+  float v[N];
+  __device__ __forceinline__ float get(int i) const { return v[i]; }
+};
+
+template <int N>
+struct RawVec<bf16_bits, N> {
+  unsigned w[(N + 1) / 2];
+  __device__ __forceinline__ float get(int i) const {
+    return (i & 1) ? bf_hi(w[i >> 1]) : bf_lo(w[i >> 1]);
+  }
+};
+
+// N consecutive elements at p into raw registers (p aligned to the row size).
+template <typename IN, int N, bool NT>
+__device__ __forceinline__ void load_raw(const IN* p, RawVec<IN, N>& r) {
+  if constexpr (std::is_same<IN, float>::value) {
+    constexpr int bytes = N * 4;
+    if constexpr (bytes % 16 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 4; ++i) {
+        const f32x4 t = ld<f32x4, NT>(reinterpret_cast<const f32x4*>(p) + i);
+        r.v[4 * i] = t.x; r.v[4 * i + 1] = t.y; r.v[4 * i + 2] = t.z; r.v[4 * i + 3] = t.w;
+      }
+    } else if constexpr (bytes % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) {
+        const f32x2 t = ld<f32x2, NT>(reinterpret_cast<const f32x2*>(p) + i);
+        r.v[2 * i] = t.x; r.v[2 * i + 1] = t.y;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) r.v[i] = ld<float, NT>(p + i);
+    }
+  } else {
+    constexpr int bytes = N * 2;
+    if constexpr (bytes % 16 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 8; ++i) {
+        const u32x4 t = ld<u32x4, NT>(reinterpret_cast<const u32x4*>(p) + i);
+        r.w[4 * i] = t.x; r.w[4 * i + 1] = t.y; r.w[4 * i + 2] = t.z; r.w[4 * i + 3] = t.w;
+      }
+    } else if constexpr (bytes % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 4; ++i) {
+        const u32x2 t = ld<u32x2, NT>(reinterpret_cast<const u32x2*>(p) + i);
+        r.w[2 * i] = t.x; r.w[2 * i + 1] = t.y;
+      }
+    } else if constexpr (bytes % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 2; ++i) r.w[i] = ld<unsigned, NT>(reinterpret_cast<const unsigned*>(p) + i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < (N + 1) / 2; ++i) r.w[i] = 0u;
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        r.w[i >> 1] |= static_cast<unsigned>(ld<bf16_bits, NT>(p + i)) << (16 * (i & 1));
+    }
+  }
+}
+
+template <class LY, typename IN, int CPL>
+struct EdgeBuf {
+  RawVec<IN, LY::NY> y;
+  RawVec<IN, CPL> x[LY::NX];
+  RawVec<IN, CPL> s[LY::NP];
+};
+
+template <class LY, typename IN, int CPL>
+__device__ __forceinline__ void load_edge(EdgeBuf<LY, IN, CPL>& buf, const IN* __restrict__ x,
+                                          const IN* __restrict__ y, const IN* __restrict__ s, int e,
+                                          int a, int c0) {
+  constexpr int C = LY::C, NX = LY::NX, NY = LY::NY, NP = LY::NP;
+  load_raw<IN, NY, true>(y + (size_t)e * NY, buf.y);
+  const IN* srow = s + (size_t)e * NP * C + c0;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) load_raw<IN, CPL, true>(srow + p * C, buf.s[p]);
+  const IN* xrow = x + (size_t)a * NX * C + c0;
+#pragma unroll
+  for (int i = 0; i < NX; ++i) load_raw<IN, CPL, false>(xrow + i * C, buf.x[i]);
+}
+
+template <class LY, typename IN, int CPL, int NNZ>
+__device__ __forceinline__ void edge_accumulate(const EdgeBuf<LY, IN, CPL>& buf,
+                                                const CoefPack<NNZ>& cf,
+                                                float (&acc)[LY::NO][CPL]) {
+  constexpr int NY = LY::NY, NP = LY::NP;
+  float yv[NY];
+#pragma unroll
+  for (int j = 0; j < NY; ++j) yv[j] = buf.y.get(j);
+  sfor<0, NP>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    constexpr PathInfo P = LY::T.path[p];
+    constexpr int D1 = 2 * P.l1 + 1, D3 = 2 * P.l3 + 1;
+    float K[D3][D1];
+    build_k<LY, p, D3, D1>(cf, yv, K);
+    float u[D1][CPL];
+    sfor<0, D1>([&](auto m1c) {
+      constexpr int m1 = decltype(m1c)::value;
+      if constexpr (first_m3(LY::T, p, m1) >= 0) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) u[m1][c] = buf.s[p].get(c) * buf.x[P.o1 + m1].get(c);
+      }
+    });
+    sfor<0, D3>([&](auto m3c) {
+      constexpr int m3 = decltype(m3c)::value;
+      sfor<0, D1>([&](auto m1c) {
+        constexpr int m1 = decltype(m1c)::value;
+        if constexpr (k_nonzero(LY::T, p, m3, m1)) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+            acc[P.o3 + m3][c] = __builtin_fmaf(K[m3][m1], u[m1][c], acc[P.o3 + m3][c]);
+        }
+      });
+    });
+  });
+}
+
+template <class LY, typename IN, int CPL, int GPR>
+__global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm, CoefPack<LY::NNZ> cf) {
+  constexpr int C = LY::C, NO = LY::NO;
+  constexpr int LPG = C / CPL;
+  static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
+  constexpr int G = 64 / LPG;
+  static_assert(G % GPR == 0, "groups per receiver must divide groups per wave");
+  constexpr int RPW = G / GPR;
+
+  const IN* __restrict__ x = static_cast<const IN*>(prm.x);
+  const IN* __restrict__ y = static_cast<const IN*>(prm.y);
+  const IN* __restrict__ s = static_cast<const IN*>(prm.s);
+  const int* __restrict__ src = prm.src;
+  const int* __restrict__ row_ptr = prm.row_ptr;
+
+  const int lane = threadIdx.x & 63;
+  const int li = lane % LPG;
+  const int grp = lane / LPG;
+  const int gi = grp % GPR;
+  const int slot = grp / GPR;
+  const int bl = logical_wave() * RPW + slot;
+  const bool valid = bl < prm.num_nodes;
+  const int b = valid ? (prm.order ? prm.order[bl] : bl) : 0;
+  const int c0 = li * CPL;
+
+  float acc[NO][CPL];
+#pragma unroll
+  for (int o = 0; o < NO; ++o)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[o][c] = 0.0f;
+
+  int beg = 0, end = 0;
+  if (valid) {
+    beg = row_ptr[b];
+    end = row_ptr[b + 1];
+  }
+
+  EdgeBuf<LY, IN, CPL> b0, b1;
+  int e = beg + gi;
+  if (e < end) load_edge<LY, IN, CPL>(b0, x, y, s, e, src[e], c0);
+  int en = e + GPR;
+  int an = en < end ? src[en] : 0;
+  while (e < end) {
+    if (en < end) load_edge<LY, IN, CPL>(b1, x, y, s, en, an, c0);
+    int en2 = en + GPR;
+    int an2 = en2 < end ? src[en2] : 0;
+    edge_accumulate<LY, IN, CPL>(b0, cf, acc);
+    e = en;
+    en = en2;
+    an = an2;
+    if (e >= end) break;
+    if (en < end) load_edge<LY, IN, CPL>(b0, x, y, s, en, an, c0);
+    en2 = en + GPR;
+    an2 = en2 < end ? src[en2] : 0;
+    edge_accumulate<LY, IN, CPL>(b1, cf, acc);
+    e = en;
+    en = en2;
+    an = an2;
+  }
+
+  if constexpr (GPR > 1) {
+#pragma unroll
+    for (int o = 0; o < NO; ++o)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int d = LPG; d < LPG * GPR; d <<= 1) acc[o][c] += __shfl_xor(acc[o][c], d, 64);
+  }
+
+  if (valid) {
+    float* orow = prm.out + (size_t)b * NO * C + c0;
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+      if (o % GPR != gi) continue;
+      float* dst = orow + (size_t)o * C;
+      if constexpr (CPL == 4) {
+        f32x4 v = {acc[o][0] * prm.inv_avg, acc[o][1] * prm.inv_avg, acc[o][2] * prm.inv_avg,
+                   acc[o][3] * prm.inv_avg};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+      } else if constexpr (CPL == 2) {
+        f32x2 v = {acc[o][0] * prm.inv_avg, acc[o][1] * prm.inv_avg};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x2*>(dst));
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) __builtin_nontemporal_store(acc[o][c] * prm.inv_avg, dst + c);
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------- backward -------
 //
 // Reverse pass of L = <g, out>, receiver ordered: the cotangent row g[b] is
@@ -324,9 +559,9 @@ __global__ void __launch_bounds__(256) conv_bwd(BwdParams prm, CoefPack<LY::NNZ>
   const int grp = lane / LPG;
   const int gi = grp % GPR;
   const int slot = grp / GPR;
-  const int wave = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6));
-  const int b = wave * RPW + slot;
-  if (b >= prm.num_nodes) return;   // whole slots only: no cross-lane work follows an early exit
+  const int bl = logical_wave() * RPW + slot;
+  if (bl >= prm.num_nodes) return;   // whole slots only: no cross-lane work follows an early exit
+  const int b = prm.order ? prm.order[bl] : bl;
 
   const int beg = row_ptr[b];
   const int end = row_ptr[b + 1];
@@ -505,8 +740,19 @@ hipError_t launch_fwd(const FwdParams& p, const float* coef, hipStream_t st) {
   constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
   if (p.num_nodes <= 0) return hipSuccess;
   const long waves = (p.num_nodes + RPW - 1) / RPW;
-  const long blocks = (waves + 3) / 4;
+  const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
   hipLaunchKernelGGL((conv_fwd<LY, IN, CPL, GPR>), dim3((unsigned)blocks), dim3(256), 0, st, p,
+                     pack<LY>(coef));
+  return hipGetLastError();
+}
+
+template <class LY, typename IN, int CPL, int GPR>
+hipError_t launch_fwd_pipe(const FwdParams& p, const float* coef, hipStream_t st) {
+  constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
+  if (p.num_nodes <= 0) return hipSuccess;
+  const long waves = (p.num_nodes + RPW - 1) / RPW;
+  const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
+  hipLaunchKernelGGL((conv_fwd_pipe<LY, IN, CPL, GPR>), dim3((unsigned)blocks), dim3(256), 0, st, p,
                      pack<LY>(coef));
   return hipGetLastError();
 }
@@ -521,7 +767,7 @@ hipError_t launch_bwd(const BwdParams& p, const float* coef, hipStream_t st) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const long waves = (p.num_nodes + RPW - 1) / RPW;
-  const long blocks = (waves + 3) / 4;
+  const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
   hipLaunchKernelGGL((conv_bwd<LY, CPL, GPR>), dim3((unsigned)blocks), dim3(256), 0, st, p,
                      pack<LY>(coef));
   return hipGetLastError();
@@ -539,24 +785,29 @@ constexpr LayoutTables kGateT = LGate::T;
 constexpr LayoutTables kMaceT = LMace::T;
 constexpr LayoutTables kBigT = LBig::T;
 
-const FwdLauncher kTinyF32[] = {launch_fwd<LTiny, float, 4, 4>, launch_fwd<LTiny, float, 2, 2>,
-                                launch_fwd<LTiny, float, 1, 1>};
-const FwdLauncher kTinyBF[] = {launch_fwd<LTiny, bf16_bits, 4, 4>};
+// Variant 0 of each list is the default (the fastest measured on MI355X for
+// the workload of that layout); the others stay selectable for comparison.
+const FwdLauncher kTinyF32[] = {launch_fwd_pipe<LTiny, float, 4, 4>, launch_fwd<LTiny, float, 4, 4>,
+                                launch_fwd<LTiny, float, 2, 2>, launch_fwd_pipe<LTiny, float, 2, 2>};
+const FwdLauncher kTinyBF[] = {launch_fwd_pipe<LTiny, bf16_bits, 4, 4>, launch_fwd<LTiny, bf16_bits, 4, 4>};
 const BwdLauncher kTinyB[] = {launch_bwd<LTiny, 2, 4>, launch_bwd<LTiny, 1, 1>};
 
-const FwdLauncher kGateF32[] = {launch_fwd<LGate, float, 4, 4>, launch_fwd<LGate, float, 2, 2>,
-                                launch_fwd<LGate, float, 4, 2>, launch_fwd<LGate, float, 1, 1>};
-const FwdLauncher kGateBF[] = {launch_fwd<LGate, bf16_bits, 4, 4>};
-const BwdLauncher kGateB[] = {launch_bwd<LGate, 1, 2>, launch_bwd<LGate, 2, 4>};
+const FwdLauncher kGateF32[] = {launch_fwd_pipe<LGate, float, 4, 4>, launch_fwd<LGate, float, 4, 4>,
+                                launch_fwd_pipe<LGate, float, 4, 2>, launch_fwd_pipe<LGate, float, 2, 2>};
+const FwdLauncher kGateBF[] = {launch_fwd_pipe<LGate, bf16_bits, 4, 4>, launch_fwd<LGate, bf16_bits, 4, 4>};
+const BwdLauncher kGateB[] = {launch_bwd<LGate, 2, 4>, launch_bwd<LGate, 1, 2>};
 
-const FwdLauncher kMaceF32[] = {launch_fwd<LMace, float, 2, 1>, launch_fwd<LMace, float, 4, 2>,
-                                launch_fwd<LMace, float, 4, 1>};
-const FwdLauncher kMaceBF[] = {launch_fwd<LMace, bf16_bits, 2, 1>, launch_fwd<LMace, bf16_bits, 4, 2>};
-const BwdLauncher kMaceB[] = {launch_bwd<LMace, 2, 1>, launch_bwd<LMace, 4, 2>};
+const FwdLauncher kMaceF32[] = {launch_fwd_pipe<LMace, float, 4, 2>, launch_fwd<LMace, float, 2, 1>,
+                                launch_fwd_pipe<LMace, float, 2, 1>, launch_fwd_pipe<LMace, float, 4, 1>};
+const FwdLauncher kMaceBF[] = {launch_fwd_pipe<LMace, bf16_bits, 4, 2>, launch_fwd<LMace, bf16_bits, 2, 1>,
+                               launch_fwd_pipe<LMace, bf16_bits, 2, 1>};
+const BwdLauncher kMaceB[] = {launch_bwd<LMace, 4, 2>, launch_bwd<LMace, 2, 1>};
 
-const FwdLauncher kBigF32[] = {launch_fwd<LBig, float, 4, 4>, launch_fwd<LBig, float, 2, 2>};
-const FwdLauncher kBigBF[] = {launch_fwd<LBig, bf16_bits, 4, 4>, launch_fwd<LBig, bf16_bits, 2, 2>,
-                              launch_fwd<LBig, bf16_bits, 8, 8>, launch_fwd<LBig, bf16_bits, 4, 2>};
+const FwdLauncher kBigF32[] = {launch_fwd_pipe<LBig, float, 2, 2>, launch_fwd<LBig, float, 4, 4>,
+                               launch_fwd_pipe<LBig, float, 4, 4>};
+const FwdLauncher kBigBF[] = {launch_fwd_pipe<LBig, bf16_bits, 2, 2>, launch_fwd<LBig, bf16_bits, 4, 4>,
+                              launch_fwd_pipe<LBig, bf16_bits, 4, 4>, launch_fwd_pipe<LBig, bf16_bits, 4, 2>,
+                              launch_fwd_pipe<LBig, bf16_bits, 2, 1>};
 const BwdLauncher kBigB[] = {launch_bwd<LBig, 2, 2>};
 
 #define E3C_N(a) (int)(sizeof(a) / sizeof((a)[0]))

@@ -30,7 +30,8 @@ EXPORTED = [
     "e3conv_plan", "e3conv_plan_destroy", "e3conv_plan_shape", "e3conv_plan_paths",
     "e3conv_plan_coefficients", "e3conv_plan_supported", "e3conv_forward",
     "e3conv_backward_workspace_size", "e3conv_backward", "e3conv_csr_from_receivers",
-    "e3conv_validate_graph", "e3conv_plan_set_variant", "e3conv_plan_num_variants",
+    "e3conv_validate_graph", "e3conv_receiver_order", "e3conv_plan_set_variant",
+    "e3conv_plan_num_variants",
     "e3conv_status_string", "e3conv_last_error_detail",
 ]
 
@@ -67,11 +68,12 @@ def load_library(path=LIB_PATH):
         "e3conv_plan_coefficients": ([P, I32P, I32P, I32P, I32P, I32P,
                                       ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "e3conv_plan_supported": ([P, I32P, I32P, I32P], ctypes.c_int),
-        "e3conv_forward": ([P, ctypes.c_int, P, P, P, P, P, I64, I64, P, P], ctypes.c_int),
+        "e3conv_forward": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, P, P], ctypes.c_int),
         "e3conv_backward_workspace_size": ([P, I64, I64, ctypes.POINTER(ctypes.c_size_t)],
                                            ctypes.c_int),
-        "e3conv_backward": ([P, ctypes.c_int, P, P, P, P, P, I64, I64, P, P, P, P, P,
+        "e3conv_backward": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, P, P, P, P, P,
                              ctypes.c_size_t, P], ctypes.c_int),
+        "e3conv_receiver_order": ([P, P, I64, I64, ctypes.c_int, P], ctypes.c_int),
         "e3conv_csr_from_receivers": ([P, I64, I64, P, P], ctypes.c_int),
         "e3conv_validate_graph": ([P, P, I64, I64, ctypes.c_int], ctypes.c_int),
         "e3conv_plan_set_variant": ([P, ctypes.c_int, ctypes.c_int], ctypes.c_int),
@@ -180,7 +182,7 @@ def e3conv_plan_set_variant(handle, forward_variant=0, backward_variant=0):
     _check(load_library().e3conv_plan_set_variant(handle, int(forward_variant), int(backward_variant)))
 
 
-def e3conv_forward(handle, x, y, s, src, row_ptr, num_nodes, num_edges, out, stream=None):
+def e3conv_forward(handle, x, y, s, src, row_ptr, num_nodes, num_edges, out, order=None, stream=None):
     import torch
     dt = _dtype_code(x)
     for t, n in ((x, "x"), (y, "y"), (s, "s")):
@@ -188,9 +190,11 @@ def e3conv_forward(handle, x, y, s, src, row_ptr, num_nodes, num_edges, out, str
     _need(src, "src", torch.int32)
     _need(row_ptr, "row_ptr", torch.int32)
     _need(out, "out", torch.float32)
+    if order is not None:
+        _need(order, "order", torch.int32)
     _check(load_library().e3conv_forward(handle, dt, _ptr(x), _ptr(y), _ptr(s), _ptr(src),
-                                         _ptr(row_ptr), int(num_nodes), int(num_edges), _ptr(out),
-                                         _stream(stream)))
+                                         _ptr(row_ptr), _ptr(order), int(num_nodes), int(num_edges),
+                                         _ptr(out), _stream(stream)))
     return out
 
 
@@ -202,16 +206,18 @@ def e3conv_backward_workspace_size(handle, num_nodes, num_edges):
 
 
 def e3conv_backward(handle, x, y, s, src, row_ptr, num_nodes, num_edges, grad_out, grad_x,
-                    grad_y, grad_s, workspace=None, stream=None):
+                    grad_y, grad_s, workspace=None, order=None, stream=None):
     import torch
     for t, n in ((x, "x"), (y, "y"), (s, "s"), (grad_out, "grad_out"), (grad_x, "grad_x"),
                  (grad_y, "grad_y"), (grad_s, "grad_s")):
         _need(t, n, torch.float32)
     _need(src, "src", torch.int32)
     _need(row_ptr, "row_ptr", torch.int32)
+    if order is not None:
+        _need(order, "order", torch.int32)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load_library().e3conv_backward(handle, E3CONV_F32, _ptr(x), _ptr(y), _ptr(s), _ptr(src),
-                                          _ptr(row_ptr), int(num_nodes), int(num_edges),
+                                          _ptr(row_ptr), _ptr(order), int(num_nodes), int(num_edges),
                                           _ptr(grad_out), _ptr(grad_x), _ptr(grad_y), _ptr(grad_s),
                                           _ptr(workspace), wbytes, _stream(stream)))
 
@@ -225,6 +231,18 @@ def e3conv_csr_from_receivers(receivers, num_nodes, row_ptr=None, stream=None):
     _check(load_library().e3conv_csr_from_receivers(_ptr(receivers), receivers.numel(),
                                                     int(num_nodes), _ptr(row_ptr), _stream(stream)))
     return row_ptr
+
+
+def e3conv_receiver_order(row_ptr, src, num_nodes, num_edges, cluster=512):
+    """Host-side receiver order (numpy int32 permutation) for gather locality."""
+    import numpy as np
+    r = np.ascontiguousarray(np.asarray(row_ptr), dtype=np.int32)
+    s = np.ascontiguousarray(np.asarray(src), dtype=np.int32)
+    order = np.empty(int(num_nodes), dtype=np.int32)
+    _check(load_library().e3conv_receiver_order(r.ctypes.data_as(P), s.ctypes.data_as(P),
+                                                int(num_nodes), int(num_edges), int(cluster),
+                                                order.ctypes.data_as(P)))
+    return order
 
 
 def e3conv_validate_graph(src, row_ptr, num_nodes, num_edges):
@@ -292,14 +310,16 @@ class Plan:
             raise ValueError("src must have E entries and row_ptr N+1")
         return N, E
 
-    def forward(self, x, y, s, src, row_ptr, out=None, stream=None):
+    def forward(self, x, y, s, src, row_ptr, out=None, order=None, stream=None):
         import torch
         N, E = self._check_shapes(x, y, s, src, row_ptr)
+        if order is not None and order.numel() != N:
+            raise ValueError("order must have N entries")
         if out is None:
             out = torch.empty((N, self.num_out, self.channels), dtype=torch.float32, device=x.device)
-        return e3conv_forward(self.handle, x, y, s, src, row_ptr, N, E, out, stream)
+        return e3conv_forward(self.handle, x, y, s, src, row_ptr, N, E, out, order, stream)
 
-    def backward(self, x, y, s, src, row_ptr, grad_out, stream=None, grads=None):
+    def backward(self, x, y, s, src, row_ptr, grad_out, stream=None, grads=None, order=None):
         import torch
         N, E = self._check_shapes(x, y, s, src, row_ptr)
         if tuple(grad_out.shape) != (N, self.num_out, self.channels):
@@ -311,8 +331,10 @@ class Plan:
         for gt, ref, name in ((gx, x, "grad_x"), (gy, y, "grad_y"), (gs, s, "grad_s")):
             if tuple(gt.shape) != tuple(ref.shape):
                 raise ValueError(f"{name} must have shape {tuple(ref.shape)}, got {tuple(gt.shape)}")
+        if order is not None and order.numel() != N:
+            raise ValueError("order must have N entries")
         e3conv_backward(self.handle, x, y, s, src, row_ptr, N, E, grad_out.contiguous(), gx, gy, gs,
-                        None, stream)
+                        None, order, stream)
         return gx, gy, gs
 
 

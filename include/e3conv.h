@@ -112,6 +112,10 @@ e3conv_status e3conv_plan_supported(e3conv_plan_t plan, int* fwd_f32, int* fwd_b
  *   row_ptr   device int32[num_nodes + 1]: receiver CSR offsets, row_ptr[0] = 0,
  *             row_ptr[num_nodes] = num_edges; edges of receiver b are
  *             row_ptr[b] .. row_ptr[b+1]-1 (y and s rows in that order);
+ *   order     device int32[num_nodes], a permutation of 0..num_nodes-1 giving
+ *             the order in which receivers are processed (for cache reuse of
+ *             the gathered sender rows, see e3conv_receiver_order), or NULL
+ *             for 0..num_nodes-1.  The result does not depend on it (bitwise);
  *   out       device float[num_nodes * num_out * C], fully overwritten (rows of
  *             receivers without edges are set to zero);
  *   hip_stream  hipStream_t or NULL for the default stream.
@@ -122,8 +126,8 @@ e3conv_status e3conv_plan_supported(e3conv_plan_t plan, int* fwd_f32, int* fwd_b
  * num_nodes * num_out * C < 2^31. */
 e3conv_status e3conv_forward(e3conv_plan_t plan, e3conv_dtype in_dtype, const void* x,
                              const void* y, const void* s, const int32_t* src,
-                             const int32_t* row_ptr, int64_t num_nodes, int64_t num_edges,
-                             float* out, void* hip_stream);
+                             const int32_t* row_ptr, const int32_t* order, int64_t num_nodes,
+                             int64_t num_edges, float* out, void* hip_stream);
 
 /* Bytes of device workspace e3conv_backward needs (currently 0). */
 e3conv_status e3conv_backward_workspace_size(e3conv_plan_t plan, int64_t num_nodes,
@@ -140,8 +144,9 @@ e3conv_status e3conv_backward_workspace_size(e3conv_plan_t plan, int64_t num_nod
  * be NULL for an edgeless graph).  workspace may be NULL when the size is 0. */
 e3conv_status e3conv_backward(e3conv_plan_t plan, e3conv_dtype in_dtype, const void* x,
                               const void* y, const void* s, const int32_t* src,
-                              const int32_t* row_ptr, int64_t num_nodes, int64_t num_edges,
-                              const float* grad_out, float* grad_x, float* grad_y,
+                              const int32_t* row_ptr, const int32_t* order, int64_t num_nodes,
+                              int64_t num_edges, const float* grad_out, float* grad_x,
+                              float* grad_y,
                               float* grad_s, void* workspace, size_t workspace_bytes,
                               void* hip_stream);
 
@@ -150,6 +155,16 @@ e3conv_status e3conv_backward(e3conv_plan_t plan, e3conv_dtype in_dtype, const v
  * non-decreasing).  One thread per node, binary search; asynchronous. */
 e3conv_status e3conv_csr_from_receivers(const int32_t* receivers_sorted, int64_t num_edges,
                                         int64_t num_nodes, int32_t* row_ptr, void* hip_stream);
+
+/* Receiver processing order that improves cache reuse of the gathered sender
+ * rows (host only; once per graph, like the CSR).  From the host CSR (row_ptr,
+ * src) it grows breadth-first clusters of about `cluster` receivers over the
+ * in-neighbour graph (seeds in index order) and writes their concatenation, a
+ * permutation of 0..num_nodes-1, to the host array order[num_nodes].  The
+ * graph is validated first (E3CONV_ERR_GRAPH on failure).  Pass the result,
+ * copied to the device, as `order` to e3conv_forward / e3conv_backward. */
+e3conv_status e3conv_receiver_order(const int32_t* row_ptr, const int32_t* src, int64_t num_nodes,
+                                    int64_t num_edges, int cluster, int32_t* order);
 
 /* Check a graph: row_ptr[0] = 0, non-decreasing, row_ptr[num_nodes] = num_edges,
  * every src in [0, num_nodes).  on_device = 0: host pointers; 1: device

@@ -56,8 +56,29 @@ def test_backward_overwrites_grad_x():
     a = plan.backward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"], d["g"])
     grads = tuple(torch.full_like(t, 3.0) for t in a)
     b = plan.backward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"], d["g"], grads=grads)
+    # grad_x is accumulated with fp32 atomics in a run-dependent order, so two
+    # runs agree to rounding only; a stale 3.0 would be off by far more
     for u, w in zip(a, b):
-        assert rel_err(w.cpu().numpy(), u.cpu().numpy()) <= 1e-6
+        err = rel_err(w.cpu().numpy(), u.cpu().numpy())
+        assert err <= 1e-5, err
+
+
+def test_backward_receiver_order():
+    """grad_s and grad_y are unchanged bit for bit; grad_x to the atomics' rounding."""
+    import torch
+    inp = with_cotangent(4, 401)
+    d = device_inputs(inp)
+    plan = plan_for(inp)
+    order = torch.from_numpy(E.e3conv_receiver_order(d["row_ptr"].cpu().numpy(), inp.senders,
+                                                     inp.num_nodes, inp.num_edges, 64)).cuda()
+    _, nb = plan.num_variants(E.E3CONV_F32)
+    for v in range(nb):
+        plan.set_variant(0, v)
+        a = plan.backward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"], d["g"])
+        b = plan.backward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"], d["g"], order=order)
+        torch.cuda.synchronize()
+        assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+        assert rel_err(b[0].cpu().numpy(), a[0].cpu().numpy()) <= 1e-5
 
 
 def test_backward_zero_edges():
@@ -152,4 +173,5 @@ def test_autograd_function_matches_plan():
     grads = torch.autograd.grad(out, xs, grad_outputs=d["g"])
     want = plan.backward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"], d["g"])
     for a, b in zip(grads, want):
-        assert rel_err(a.cpu().numpy(), b.cpu().numpy()) <= 1e-6
+        err = rel_err(a.cpu().numpy(), b.cpu().numpy())
+        assert err <= 1e-5, err

@@ -113,6 +113,26 @@ def test_forward_deterministic(small):
     assert torch.equal(a, b)
 
 
+def test_forward_receiver_order_bitwise(small):
+    """Processing receivers in another order changes nothing, bit for bit."""
+    import torch
+    inp, d, _ = small
+    plan = plan_for(inp)
+    dt = E.E3CONV_BF16 if inp.workload.dtype == "bf16" else E.E3CONV_F32
+    order = E.e3conv_receiver_order(d["row_ptr"].cpu().numpy(), inp.senders, inp.num_nodes,
+                                    inp.num_edges, 64)
+    perm = torch.from_numpy(order).cuda()
+    rev = torch.flip(torch.arange(inp.num_nodes, dtype=torch.int32, device="cuda"), [0])
+    nf, _ = plan.num_variants(dt)
+    for v in range(nf):
+        plan.set_variant(v, 0)
+        a = plan.forward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"])
+        b = plan.forward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"], order=perm)
+        c = plan.forward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"], order=rev.contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(a, b) and torch.equal(a, c), v
+
+
 def test_forward_on_side_stream(small):
     import torch
     inp, d, _ = small

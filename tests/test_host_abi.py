@@ -117,7 +117,7 @@ def test_layout_without_kernel_is_a_valid_plan():
     p = E.Plan("4x2e+4x0e+4x1o", 2, "4x1o+4x0e")
     assert p.supported() == (False, False, False)
     fake = ctypes.c_void_p(0x1000)    # never dereferenced: the call fails before any launch
-    st = E.load_library().e3conv_forward(p.handle, 0, fake, fake, fake, fake, fake, 4, 4, fake, None)
+    st = E.load_library().e3conv_forward(p.handle, 0, fake, fake, fake, fake, fake, None, 4, 4, fake, None)
     assert st == 3  # E3CONV_ERR_UNSUPPORTED
 
 
@@ -153,17 +153,17 @@ def test_forward_backward_argument_errors(lib):
     f = ctypes.c_void_p(0x1000)
     n = ctypes.c_void_p(0)
     h = p.handle
-    assert lib.e3conv_forward(None, 0, f, f, f, f, f, 4, 4, f, None) == 1
-    assert lib.e3conv_forward(h, 5, f, f, f, f, f, 4, 4, f, None) == 1       # bad dtype
-    assert lib.e3conv_forward(h, 0, f, f, f, f, f, -1, 4, f, None) == 1      # negative size
-    assert lib.e3conv_forward(h, 0, f, f, f, f, f, 4, -4, f, None) == 1
-    assert lib.e3conv_forward(h, 0, f, f, f, f, f, 4, 1 << 31, f, None) == 1
-    assert lib.e3conv_forward(h, 0, n, f, f, f, f, 4, 4, f, None) == 1       # null x
-    assert lib.e3conv_forward(h, 0, f, f, f, f, n, 4, 4, f, None) == 1       # null row_ptr
-    assert lib.e3conv_forward(h, 0, n, n, n, n, n, 0, 0, n, None) == 0       # num_nodes = 0: no-op
-    assert lib.e3conv_backward(h, 1, f, f, f, f, f, 4, 4, f, f, f, f, n, 0, None) == 3   # bf16 reverse
-    assert lib.e3conv_backward(h, 0, f, f, f, f, f, 4, 4, f, n, f, f, n, 0, None) == 1   # partial outputs
-    assert lib.e3conv_backward(h, 0, f, f, f, f, f, 4, 4, f, n, n, n, n, 0, None) == 0   # nothing to do
+    assert lib.e3conv_forward(None, 0, f, f, f, f, f, None, 4, 4, f, None) == 1
+    assert lib.e3conv_forward(h, 5, f, f, f, f, f, None, 4, 4, f, None) == 1       # bad dtype
+    assert lib.e3conv_forward(h, 0, f, f, f, f, f, None, -1, 4, f, None) == 1      # negative size
+    assert lib.e3conv_forward(h, 0, f, f, f, f, f, None, 4, -4, f, None) == 1
+    assert lib.e3conv_forward(h, 0, f, f, f, f, f, None, 4, 1 << 31, f, None) == 1
+    assert lib.e3conv_forward(h, 0, n, f, f, f, f, None, 4, 4, f, None) == 1       # null x
+    assert lib.e3conv_forward(h, 0, f, f, f, f, n, None, 4, 4, f, None) == 1       # null row_ptr
+    assert lib.e3conv_forward(h, 0, n, n, n, n, n, None, 0, 0, n, None) == 0       # num_nodes = 0: no-op
+    assert lib.e3conv_backward(h, 1, f, f, f, f, f, None, 4, 4, f, f, f, f, n, 0, None) == 3   # bf16 reverse
+    assert lib.e3conv_backward(h, 0, f, f, f, f, f, None, 4, 4, f, n, f, f, n, 0, None) == 1   # partial outputs
+    assert lib.e3conv_backward(h, 0, f, f, f, f, f, None, 4, 4, f, n, n, n, n, 0, None) == 0   # nothing to do
     sz = ctypes.c_size_t(123)
     assert lib.e3conv_backward_workspace_size(h, 10, 10, ctypes.byref(sz)) == 0 and sz.value == 0
     assert lib.e3conv_csr_from_receivers(f, -1, 4, f, None) == 1
@@ -199,3 +199,33 @@ def test_validate_graph_workload_csr():
     inp = synth.make_inputs(1)
     row_ptr = np.searchsorted(inp.receivers, np.arange(inp.num_nodes + 1)).astype(np.int32)
     E.e3conv_validate_graph(inp.senders, row_ptr, inp.num_nodes, inp.num_edges)
+
+
+def test_receiver_order_is_a_permutation():
+    for idx, n in ((1, None), (2, 1500)):
+        inp = synth.make_inputs(idx, num_nodes=n) if n else synth.make_inputs(idx)
+        row_ptr = np.searchsorted(inp.receivers, np.arange(inp.num_nodes + 1)).astype(np.int32)
+        for cluster in (1, 64, 512, 10 ** 6):
+            order = E.e3conv_receiver_order(row_ptr, inp.senders, inp.num_nodes, inp.num_edges, cluster)
+            np.testing.assert_array_equal(np.sort(order), np.arange(inp.num_nodes))
+    with pytest.raises(E.E3ConvError) as ei:
+        E.e3conv_receiver_order(np.array([0, 2, 1], np.int32), np.array([0, 1], np.int32), 2, 2, 8)
+    assert ei.value.status == 5
+    with pytest.raises(E.E3ConvError) as ei:
+        E.e3conv_receiver_order(np.array([0, 1], np.int32), np.array([0], np.int32), 1, 1, 0)
+    assert ei.value.status == 1
+
+
+def test_receiver_order_clusters_are_connected():
+    """Each cluster of the order is grown breadth-first: a member after the seed has an
+    in-neighbour earlier in the same cluster (when the graph is connected there)."""
+    inp = synth.make_inputs(2, num_nodes=1500)
+    row_ptr = np.searchsorted(inp.receivers, np.arange(inp.num_nodes + 1)).astype(np.int32)
+    cluster = 64
+    order = E.e3conv_receiver_order(row_ptr, inp.senders, inp.num_nodes, inp.num_edges, cluster)
+    pos = np.empty_like(order)
+    pos[order] = np.arange(len(order))
+    first = order[:cluster]
+    for v in first[1:]:
+        nbrs = inp.senders[row_ptr[v]:row_ptr[v + 1]]
+        assert np.any(pos[nbrs] < pos[v])    # the radius graph is symmetric
