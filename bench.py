@@ -50,7 +50,11 @@ def parse():
 
 
 def calibrate_copy(mib, reps=5):
-    """A plain device-to-device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    """A plain device-to-device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE.
+
+    Also reports the streaming rates this device attains outside the
+    convolution: the copy (read + write) and a read-only reduction.
+    """
     import torch
     n = mib * (1 << 20) // 4
     a = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -58,7 +62,28 @@ def calibrate_copy(mib, reps=5):
     for _ in range(reps):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps({"calibrate_copy_bytes": n * 4, "reps": reps}), flush=True)
+    from equivariant_gnn_message_amd import e3conv as E
+    for _ in range(reps):
+        E.e3conv_stream_reference(a, b)
+        E.e3conv_stream_reference(a)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    for _ in range(reps):
+        b.copy_(a)
+    ev[1].record()
+    for _ in range(reps):
+        E.e3conv_stream_reference(a, b)
+    ev[2].record()
+    for _ in range(reps):
+        E.e3conv_stream_reference(a)
+    ev[3].record()
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) / reps for i in range(3)]
+    print(json.dumps({"calibrate_copy_bytes": n * 4, "reps": reps,
+                      "runtime_copy_GBps": 2 * n * 4 / ms[0] / 1e6,
+                      "stream_copy_GBps": 2 * n * 4 / ms[1] / 1e6,
+                      "stream_read_GBps": n * 4 / ms[2] / 1e6}), flush=True)
 
 
 def sweep(plan, w, run_fwd, run_bwd, nbytes, orders, reps=10):

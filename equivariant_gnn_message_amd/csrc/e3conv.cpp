@@ -30,7 +30,6 @@ struct e3conv_plan_s {
   std::vector<double> val;
   // compiled kernels (nullptr if none) and their coefficient vector
   const e3c::KernelSet* ks = nullptr;
-  std::vector<float> kcoef;
   int fwd_variant = 0;
   int bwd_variant = 0;
 };
@@ -78,7 +77,7 @@ bool bind_kernels(e3conv_plan_s* p, std::string* why) {
     *why = "kernel layout tables disagree with the host path enumeration";
     return false;
   }
-  std::vector<float> coef(T.nnz, 0.0f);
+  std::vector<double> coef(T.nnz, 0.0);
   for (int q = 0; q < T.num_paths; ++q) {
     const e3c::PathInfo& P = T.path[q];
     const HostPath& H = p->paths[q];
@@ -93,7 +92,7 @@ bool bind_kernels(e3conv_plan_s* p, std::string* why) {
     for (int e = P.nnz_begin; e < P.nnz_end; ++e) {
       const e3c::Entry& en = T.entry[e];
       const size_t idx = ((size_t)en.m1 * n2 + en.m2) * n3 + en.m3;
-      coef[e] = (float)C[idx];
+      coef[e] = C[idx];
       covered[idx] = 1;
     }
     for (size_t i = 0; i < C.size(); ++i) {
@@ -103,8 +102,15 @@ bool bind_kernels(e3conv_plan_s* p, std::string* why) {
       }
     }
   }
+  // the kernels' compile-time values must equal the runtime tables (fp32 rounding)
+  for (int e = 0; e < T.nnz; ++e) {
+    const double d = std::fabs((double)ks->cg_values[e] - coef[e]);
+    if (d > 1e-7 * std::fabs(coef[e]) + 1e-12) {
+      *why = "compiled CG value " + std::to_string(e) + " disagrees with the plan's table";
+      return false;
+    }
+  }
   p->ks = ks;
-  p->kcoef.swap(coef);
   return true;
 }
 
@@ -293,7 +299,7 @@ e3conv_status e3conv_forward(e3conv_plan_t p, e3conv_dtype dt, const void* x, co
   const e3c::FwdLauncher* L = dt == E3CONV_F32 ? p->ks->fwd_f32 : p->ks->fwd_bf16;
   const int v = p->fwd_variant < n ? p->fwd_variant : 0;
   e3c::FwdParams prm{x, y, s, src, row_ptr, order, out, (int)N, (int)E, 1.0f / p->avg};
-  const hipError_t err = L[v](prm, p->kcoef.data(), static_cast<hipStream_t>(stream));
+  const hipError_t err = L[v](prm, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "forward launch");
   return ok();
 }
@@ -326,7 +332,7 @@ e3conv_status e3conv_backward(e3conv_plan_t p, e3conv_dtype dt, const void* x, c
   e3c::BwdParams prm{static_cast<const float*>(x), static_cast<const float*>(y),
                      static_cast<const float*>(s), src, row_ptr, order, g, gx, gy, gs, (int)N, (int)E,
                      1.0f / p->avg};
-  const hipError_t err = p->ks->bwd_f32[v](prm, p->kcoef.data(), static_cast<hipStream_t>(stream));
+  const hipError_t err = p->ks->bwd_f32[v](prm, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "backward launch");
   return ok();
 }
@@ -357,6 +363,15 @@ e3conv_status e3conv_receiver_order(const int32_t* row_ptr, const int32_t* src, 
   return ok();
 }
 
+e3conv_status e3conv_stream_reference(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || bytes % 16 != 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "src NULL or bytes not a multiple of 16");
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
+  const hipError_t err = e3c::launch_stream(src, dst, bytes, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "stream launch");
+  return ok();
+}
+
 e3conv_status e3conv_validate_graph(const int32_t* src, const int32_t* row_ptr, int64_t N,
                                     int64_t E, int on_device) {
   if (N < 0 || E < 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "negative size");
@@ -381,7 +396,7 @@ e3conv_status e3conv_validate_graph(const int32_t* src, const int32_t* row_ptr, 
   err = hipMemcpy(bad, &host_bad, sizeof(int), hipMemcpyHostToDevice);
   if (err == hipSuccess) err = e3c::launch_validate_graph(src, row_ptr, (int)N, (int)E, bad, nullptr);
   if (err == hipSuccess) err = hipMemcpy(&host_bad, bad, sizeof(int), hipMemcpyDeviceToHost);
-  hipFree(bad);
+  (void)hipFree(bad);
   if (err != hipSuccess) return hip_fail(err, "validate");
   if (host_bad) return fail(E3CONV_ERR_GRAPH, std::to_string(host_bad) + " violations in the graph");
   return ok();

@@ -38,8 +38,8 @@ struct BwdParams {
   float inv_avg;
 };
 
-using FwdLauncher = hipError_t (*)(const FwdParams&, const float* coef, hipStream_t);
-using BwdLauncher = hipError_t (*)(const BwdParams&, const float* coef, hipStream_t);
+using FwdLauncher = hipError_t (*)(const FwdParams&, hipStream_t);
+using BwdLauncher = hipError_t (*)(const BwdParams&, hipStream_t);
 
 struct KernelSet {
   int channels;
@@ -47,6 +47,7 @@ struct KernelSet {
   int lmax;
   uint32_t ocode;
   const LayoutTables* tables;   // path / pattern enumeration the kernels use
+  const float* cg_values;       // compile-time CG values, one per pattern entry
   const FwdLauncher* fwd_f32;
   int n_fwd_f32;
   const FwdLauncher* fwd_bf16;
@@ -57,6 +58,9 @@ struct KernelSet {
 
 // Returns nullptr if no kernels are compiled for the layout.
 const KernelSet* find_kernels(int channels, uint32_t xcode, int lmax, uint32_t ocode);
+
+// Streaming reference kernels (copy when dst != nullptr, else read only).
+hipError_t launch_stream(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 hipError_t launch_csr_from_receivers(const int* dst, int num_edges, int num_nodes, int* row_ptr,
                                      hipStream_t stream);

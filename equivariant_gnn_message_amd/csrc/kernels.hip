@@ -70,10 +70,6 @@ constexpr int ilog2(int v) {
   return r;
 }
 
-template <int NNZ>
-struct CoefPack {
-  float v[NNZ > 0 ? NNZ : 1];
-};
 
 // Wave index in processing order.  Work-groups are dealt round-robin to the
 // 8 XCDs (8 L2 caches); remapping so that XCD k runs a contiguous range of
@@ -174,14 +170,13 @@ __device__ __forceinline__ void load_row(const IN* p, float (&v)[N]) {
 // ----------------------------------------------------- shared edge math -----
 
 // K^p[m3][m1] = sum_m2 C^p[m1,m2,m3] y[o2+m2] over the compile-time pattern.
-template <class LY, int p, int D3, int D1, int NNZ>
-__device__ __forceinline__ void build_k(const CoefPack<NNZ>& cf, const float (&yv)[LY::NY],
-                                        float (&K)[D3][D1]) {
+template <class LY, int p, int D3, int D1>
+__device__ __forceinline__ void build_k(const float (&yv)[LY::NY], float (&K)[D3][D1]) {
   constexpr PathInfo P = LY::T.path[p];
   sfor<P.nnz_begin, P.nnz_end>([&](auto qc) {
     constexpr int q = decltype(qc)::value;
     constexpr Entry en = LY::T.entry[q];
-    const float c = cf.v[q];
+    constexpr float c = LY::CG.v[q];
     const float yy = yv[P.o2 + en.m2];
     if constexpr (first_term(LY::T, p, q)) {
       K[en.m3][en.m1] = c * yy;
@@ -194,7 +189,7 @@ __device__ __forceinline__ void build_k(const CoefPack<NNZ>& cf, const float (&y
 // ------------------------------------------------------------ forward -------
 
 template <class LY, typename IN, int CPL, int GPR>
-__global__ void __launch_bounds__(256) conv_fwd(FwdParams prm, CoefPack<LY::NNZ> cf) {
+__global__ void __launch_bounds__(256) conv_fwd(FwdParams prm) {
   constexpr int C = LY::C, NX = LY::NX, NY = LY::NY, NO = LY::NO, NP = LY::NP;
   constexpr int LPG = C / CPL;
   static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
@@ -246,7 +241,7 @@ __global__ void __launch_bounds__(256) conv_fwd(FwdParams prm, CoefPack<LY::NNZ>
       float sv[CPL];
       load_ch<IN, CPL, true>(srow + p * C, sv);
       float K[D3][D1];
-      build_k<LY, p, D3, D1>(cf, yv, K);
+      build_k<LY, p, D3, D1>(yv, K);
       sfor<0, D3>([&](auto m3c) {
         constexpr int m3 = decltype(m3c)::value;
         static_assert(first_m1(LY::T, p, m3) >= 0, "every output row has a term");
@@ -398,9 +393,8 @@ __device__ __forceinline__ void load_edge(EdgeBuf<LY, IN, CPL>& buf, const IN* _
   for (int i = 0; i < NX; ++i) load_raw<IN, CPL, false>(xrow + i * C, buf.x[i]);
 }
 
-template <class LY, typename IN, int CPL, int NNZ>
+template <class LY, typename IN, int CPL>
 __device__ __forceinline__ void edge_accumulate(const EdgeBuf<LY, IN, CPL>& buf,
-                                                const CoefPack<NNZ>& cf,
                                                 float (&acc)[LY::NO][CPL]) {
   constexpr int NY = LY::NY, NP = LY::NP;
   float yv[NY];
@@ -411,7 +405,7 @@ __device__ __forceinline__ void edge_accumulate(const EdgeBuf<LY, IN, CPL>& buf,
     constexpr PathInfo P = LY::T.path[p];
     constexpr int D1 = 2 * P.l1 + 1, D3 = 2 * P.l3 + 1;
     float K[D3][D1];
-    build_k<LY, p, D3, D1>(cf, yv, K);
+    build_k<LY, p, D3, D1>(yv, K);
     float u[D1][CPL];
     sfor<0, D1>([&](auto m1c) {
       constexpr int m1 = decltype(m1c)::value;
@@ -435,7 +429,7 @@ __device__ __forceinline__ void edge_accumulate(const EdgeBuf<LY, IN, CPL>& buf,
 }
 
 template <class LY, typename IN, int CPL, int GPR>
-__global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm, CoefPack<LY::NNZ> cf) {
+__global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm) {
   constexpr int C = LY::C, NO = LY::NO;
   constexpr int LPG = C / CPL;
   static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
@@ -480,7 +474,7 @@ __global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm, CoefPack<LY:
     if (en < end) load_edge<LY, IN, CPL>(b1, x, y, s, en, an, c0);
     int en2 = en + GPR;
     int an2 = en2 < end ? src[en2] : 0;
-    edge_accumulate<LY, IN, CPL>(b0, cf, acc);
+    edge_accumulate<LY, IN, CPL>(b0, acc);
     e = en;
     en = en2;
     an = an2;
@@ -488,7 +482,7 @@ __global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm, CoefPack<LY:
     if (en < end) load_edge<LY, IN, CPL>(b0, x, y, s, en, an, c0);
     en2 = en + GPR;
     an2 = en2 < end ? src[en2] : 0;
-    edge_accumulate<LY, IN, CPL>(b1, cf, acc);
+    edge_accumulate<LY, IN, CPL>(b1, acc);
     e = en;
     en = en2;
     an = an2;
@@ -538,7 +532,7 @@ __global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm, CoefPack<LY:
 // a group touches consecutive floats.
 
 template <class LY, int CPL, int GPR>
-__global__ void __launch_bounds__(256) conv_bwd(BwdParams prm, CoefPack<LY::NNZ> cf) {
+__global__ void __launch_bounds__(256) conv_bwd(BwdParams prm) {
   constexpr int C = LY::C, NX = LY::NX, NY = LY::NY, NO = LY::NO, NP = LY::NP;
   constexpr int LPG = C / CPL;
   static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
@@ -603,7 +597,7 @@ __global__ void __launch_bounds__(256) conv_bwd(BwdParams prm, CoefPack<LY::NNZ>
 #pragma unroll
       for (int c = 0; c < CPL; ++c) sv[c] = __builtin_nontemporal_load(srow + p * C + c * LPG);
       float K[D3][D1];
-      build_k<LY, p, D3, D1>(cf, yv, K);
+      build_k<LY, p, D3, D1>(yv, K);
 
       // t = K x, grad_s = <g, t>
       float ds[CPL];
@@ -668,7 +662,7 @@ __global__ void __launch_bounds__(256) conv_bwd(BwdParams prm, CoefPack<LY::NNZ>
               constexpr int qi = decltype(ec)::value;
               constexpr Entry en = LY::T.entry[qi];
               if constexpr (en.m1 == m1 && en.m3 == m3) {
-                dyp[P.o2 + en.m2] = __builtin_fmaf(cf.v[qi], q, dyp[P.o2 + en.m2]);
+                dyp[P.o2 + en.m2] = __builtin_fmaf(LY::CG.v[qi], q, dyp[P.o2 + en.m2]);
               }
             });
           }
@@ -720,6 +714,226 @@ __global__ void __launch_bounds__(256) conv_bwd(BwdParams prm, CoefPack<LY::NNZ>
   }
 }
 
+// ------------------------------------------------- pipelined backward -------
+//
+// conv_bwd with the edge loop software-pipelined like conv_fwd_pipe: the next
+// edge's y, s and gathered x values are loaded while the current edge is
+// processed.  Same per-edge arithmetic and output writes as conv_bwd.
+
+template <class LY, int CPL>
+struct BwdBuf {
+  float y[LY::NY];
+  float x[LY::NX][CPL];
+  float s[LY::NP][CPL];
+};
+
+template <class LY, int CPL, int LPG>
+__device__ __forceinline__ void load_bwd_edge(BwdBuf<LY, CPL>& buf, const float* __restrict__ x,
+                                              const float* __restrict__ y,
+                                              const float* __restrict__ s, int e, int a, int li) {
+  constexpr int C = LY::C, NX = LY::NX, NY = LY::NY, NP = LY::NP;
+  load_row<float, NY>(y + (size_t)e * NY, buf.y);
+  const float* xrow = x + (size_t)a * NX * C + li;
+#pragma unroll
+  for (int i = 0; i < NX; ++i)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) buf.x[i][c] = xrow[i * C + c * LPG];
+  const float* srow = s + (size_t)e * NP * C + li;
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) buf.s[p][c] = __builtin_nontemporal_load(srow + p * C + c * LPG);
+}
+
+template <class LY, int CPL, int LPG>
+__device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float (&gv)[LY::NO][CPL],
+                                         const BwdParams& prm, int e, int a, int li) {
+  constexpr int C = LY::C, NX = LY::NX, NY = LY::NY, NP = LY::NP;
+  constexpr int NYP = pow2_ceil(NY);
+  constexpr int STEPS = ilog2(LPG);
+  float dxp[NX][CPL];
+#pragma unroll
+  for (int i = 0; i < NX; ++i)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) dxp[i][c] = 0.0f;
+  float dyp[NYP];
+#pragma unroll
+  for (int j = 0; j < NYP; ++j) dyp[j] = 0.0f;
+  float* gsrow = prm.gs + (size_t)e * NP * C + li;
+
+  // Per path, with w = K^T g (g already divided by N):
+  //   grad_s = sum_m1 x[o1+m1] w[m1]            (= <g, K x>)
+  //   grad_x += s w                             (= K^T (s g))
+  //   grad_y[o2+m2] += sum_{m1,m3} C[m1,m2,m3] sum_c (s x[o1+m1]) g[o3+m3]
+  sfor<0, NP>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    constexpr PathInfo P = LY::T.path[p];
+    constexpr int D1 = 2 * P.l1 + 1, D3 = 2 * P.l3 + 1;
+    float K[D3][D1];
+    build_k<LY, p, D3, D1>(buf.y, K);
+    float ds[CPL];
+    sfor<0, D1>([&](auto m1c) {
+      constexpr int m1 = decltype(m1c)::value;
+      float w[CPL];
+      sfor<0, D3>([&](auto m3c) {
+        constexpr int m3 = decltype(m3c)::value;
+        if constexpr (k_nonzero(LY::T, p, m3, m1)) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            if constexpr (first_m3(LY::T, p, m1) == m3) {
+              w[c] = K[m3][m1] * gv[P.o3 + m3][c];
+            } else {
+              w[c] = __builtin_fmaf(K[m3][m1], gv[P.o3 + m3][c], w[c]);
+            }
+          }
+        }
+      });
+      if constexpr (first_m3(LY::T, p, m1) >= 0) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          if constexpr (m1 == 0) {
+            ds[c] = buf.x[P.o1][c] * w[c];
+          } else {
+            ds[c] = __builtin_fmaf(buf.x[P.o1 + m1][c], w[c], ds[c]);
+          }
+          dxp[P.o1 + m1][c] = __builtin_fmaf(buf.s[p][c], w[c], dxp[P.o1 + m1][c]);
+        }
+      } else if constexpr (m1 == 0) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) ds[c] = 0.0f;
+      }
+    });
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) __builtin_nontemporal_store(ds[c], gsrow + p * C + c * LPG);
+
+    sfor<0, D1>([&](auto m1c) {
+      constexpr int m1 = decltype(m1c)::value;
+      if constexpr (first_m3(LY::T, p, m1) >= 0) {
+        float u[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) u[c] = buf.s[p][c] * buf.x[P.o1 + m1][c];
+        sfor<0, D3>([&](auto m3c) {
+          constexpr int m3 = decltype(m3c)::value;
+          if constexpr (k_nonzero(LY::T, p, m3, m1)) {
+            float q = u[0] * gv[P.o3 + m3][0];
+#pragma unroll
+            for (int c = 1; c < CPL; ++c) q = __builtin_fmaf(u[c], gv[P.o3 + m3][c], q);
+            sfor<P.nnz_begin, P.nnz_end>([&](auto ec) {
+              constexpr int qi = decltype(ec)::value;
+              constexpr Entry en = LY::T.entry[qi];
+              if constexpr (en.m1 == m1 && en.m3 == m3) {
+                dyp[P.o2 + en.m2] = __builtin_fmaf(LY::CG.v[qi], q, dyp[P.o2 + en.m2]);
+              }
+            });
+          }
+        });
+      }
+    });
+  });
+
+#pragma unroll
+  for (int i = 0; i < NX; ++i)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      unsafeAtomicAdd(prm.gx + ((size_t)a * NX + i) * C + li + c * LPG, dxp[i][c]);
+
+  sfor<0, STEPS>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int d = LPG >> (k + 1);
+    constexpr int n = (NYP >> k) > 1 ? (NYP >> k) : 1;
+    if constexpr (n > 1) {
+      const bool upper = (li & d) != 0;
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) {
+        const float send = upper ? dyp[i] : dyp[i + n / 2];
+        const float keep = upper ? dyp[i + n / 2] : dyp[i];
+        dyp[i] = keep + __shfl_xor(send, d, 64);
+      }
+    } else {
+      dyp[0] += __shfl_xor(dyp[0], d, 64);
+    }
+  });
+  constexpr int NF = (NYP >> STEPS) > 1 ? (NYP >> STEPS) : 1;
+  constexpr int REP = LPG > NYP ? LPG / NYP : 1;
+  if ((li & (REP - 1)) == 0) {
+    int base = 0;
+#pragma unroll
+    for (int k = 0; k < STEPS; ++k) {
+      const int d = LPG >> (k + 1);
+      const int n = (NYP >> k) > 1 ? (NYP >> k) : 1;
+      if (n > 1 && (li & d)) base += n / 2;
+    }
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const int comp = base + j;
+      if (comp < NY) prm.gy[(size_t)e * NY + comp] = dyp[j];
+    }
+  }
+}
+
+template <class LY, int CPL, int GPR>
+__global__ void __launch_bounds__(256) conv_bwd_pipe(BwdParams prm) {
+  constexpr int C = LY::C, NO = LY::NO;
+  constexpr int LPG = C / CPL;
+  static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
+  constexpr int G = 64 / LPG;
+  static_assert(G % GPR == 0, "groups per receiver must divide groups per wave");
+  constexpr int RPW = G / GPR;
+
+  const float* __restrict__ x = prm.x;
+  const float* __restrict__ y = prm.y;
+  const float* __restrict__ s = prm.s;
+  const int* __restrict__ src = prm.src;
+
+  const int lane = threadIdx.x & 63;
+  const int li = lane % LPG;
+  const int grp = lane / LPG;
+  const int gi = grp % GPR;
+  const int slot = grp / GPR;
+  const int bl = logical_wave() * RPW + slot;
+  if (bl >= prm.num_nodes) return;   // whole slots only: no cross-lane work follows an early exit
+  const int b = prm.order ? prm.order[bl] : bl;
+
+  const int beg = prm.row_ptr[b];
+  const int end = prm.row_ptr[b + 1];
+
+  float gv[NO][CPL];
+#pragma unroll
+  for (int o = 0; o < NO; ++o)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      gv[o][c] = prm.g[((size_t)b * NO + o) * C + li + c * LPG] * prm.inv_avg;
+
+  BwdBuf<LY, CPL> b0, b1;
+  int e = beg + gi;
+  int a = 0;
+  if (e < end) {
+    a = src[e];
+    load_bwd_edge<LY, CPL, LPG>(b0, x, y, s, e, a, li);
+  }
+  int en = e + GPR;
+  int an = en < end ? src[en] : 0;
+  while (e < end) {
+    if (en < end) load_bwd_edge<LY, CPL, LPG>(b1, x, y, s, en, an, li);
+    int en2 = en + GPR;
+    int an2 = en2 < end ? src[en2] : 0;
+    bwd_edge<LY, CPL, LPG>(b0, gv, prm, e, a, li);
+    e = en;
+    a = an;
+    en = en2;
+    an = an2;
+    if (e >= end) break;
+    if (en < end) load_bwd_edge<LY, CPL, LPG>(b0, x, y, s, en, an, li);
+    en2 = en + GPR;
+    an2 = en2 < end ? src[en2] : 0;
+    bwd_edge<LY, CPL, LPG>(b1, gv, prm, e, a, li);
+    e = en;
+    a = an;
+    en = en2;
+    an = an2;
+  }
+}
+
 __global__ void fill_zero(float* __restrict__ p, size_t n) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -728,37 +942,29 @@ __global__ void fill_zero(float* __restrict__ p, size_t n) {
 
 // ------------------------------------------------------------- launchers ----
 
-template <class LY>
-CoefPack<LY::NNZ> pack(const float* coef) {
-  CoefPack<LY::NNZ> cp;
-  for (int i = 0; i < LY::NNZ; ++i) cp.v[i] = coef[i];
-  return cp;
-}
 
 template <class LY, typename IN, int CPL, int GPR>
-hipError_t launch_fwd(const FwdParams& p, const float* coef, hipStream_t st) {
+hipError_t launch_fwd(const FwdParams& p, hipStream_t st) {
   constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
   if (p.num_nodes <= 0) return hipSuccess;
   const long waves = (p.num_nodes + RPW - 1) / RPW;
   const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
-  hipLaunchKernelGGL((conv_fwd<LY, IN, CPL, GPR>), dim3((unsigned)blocks), dim3(256), 0, st, p,
-                     pack<LY>(coef));
+  hipLaunchKernelGGL((conv_fwd<LY, IN, CPL, GPR>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 template <class LY, typename IN, int CPL, int GPR>
-hipError_t launch_fwd_pipe(const FwdParams& p, const float* coef, hipStream_t st) {
+hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t st) {
   constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
   if (p.num_nodes <= 0) return hipSuccess;
   const long waves = (p.num_nodes + RPW - 1) / RPW;
   const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
-  hipLaunchKernelGGL((conv_fwd_pipe<LY, IN, CPL, GPR>), dim3((unsigned)blocks), dim3(256), 0, st, p,
-                     pack<LY>(coef));
+  hipLaunchKernelGGL((conv_fwd_pipe<LY, IN, CPL, GPR>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 template <class LY, int CPL, int GPR>
-hipError_t launch_bwd(const BwdParams& p, const float* coef, hipStream_t st) {
+hipError_t launch_bwd(const BwdParams& p, hipStream_t st) {
   constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
   if (p.num_nodes <= 0) return hipSuccess;
   const size_t nx = (size_t)p.num_nodes * LY::NX * LY::C;
@@ -768,8 +974,22 @@ hipError_t launch_bwd(const BwdParams& p, const float* coef, hipStream_t st) {
   if (err != hipSuccess) return err;
   const long waves = (p.num_nodes + RPW - 1) / RPW;
   const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
-  hipLaunchKernelGGL((conv_bwd<LY, CPL, GPR>), dim3((unsigned)blocks), dim3(256), 0, st, p,
-                     pack<LY>(coef));
+  hipLaunchKernelGGL((conv_bwd<LY, CPL, GPR>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+template <class LY, int CPL, int GPR>
+hipError_t launch_bwd_pipe(const BwdParams& p, hipStream_t st) {
+  constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
+  if (p.num_nodes <= 0) return hipSuccess;
+  const size_t nx = (size_t)p.num_nodes * LY::NX * LY::C;
+  const unsigned zb = (unsigned)((nx + 255) / 256 < 8192 ? (nx + 255) / 256 : 8192);
+  hipLaunchKernelGGL(fill_zero, dim3(zb), dim3(256), 0, st, p.gx, nx);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const long waves = (p.num_nodes + RPW - 1) / RPW;
+  const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
+  hipLaunchKernelGGL((conv_bwd_pipe<LY, CPL, GPR>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
@@ -784,42 +1004,49 @@ constexpr LayoutTables kTinyT = LTiny::T;
 constexpr LayoutTables kGateT = LGate::T;
 constexpr LayoutTables kMaceT = LMace::T;
 constexpr LayoutTables kBigT = LBig::T;
+constexpr CGValues<LTiny::NNZ> kTinyCG = LTiny::CG;
+constexpr CGValues<LGate::NNZ> kGateCG = LGate::CG;
+constexpr CGValues<LMace::NNZ> kMaceCG = LMace::CG;
+constexpr CGValues<LBig::NNZ> kBigCG = LBig::CG;
 
 // Variant 0 of each list is the default (the fastest measured on MI355X for
 // the workload of that layout); the others stay selectable for comparison.
 const FwdLauncher kTinyF32[] = {launch_fwd_pipe<LTiny, float, 4, 4>, launch_fwd<LTiny, float, 4, 4>,
                                 launch_fwd<LTiny, float, 2, 2>, launch_fwd_pipe<LTiny, float, 2, 2>};
 const FwdLauncher kTinyBF[] = {launch_fwd_pipe<LTiny, bf16_bits, 4, 4>, launch_fwd<LTiny, bf16_bits, 4, 4>};
-const BwdLauncher kTinyB[] = {launch_bwd<LTiny, 2, 4>, launch_bwd<LTiny, 1, 1>};
+const BwdLauncher kTinyB[] = {launch_bwd<LTiny, 2, 4>, launch_bwd<LTiny, 1, 1>,
+                              launch_bwd_pipe<LTiny, 2, 4>};
 
 const FwdLauncher kGateF32[] = {launch_fwd_pipe<LGate, float, 4, 4>, launch_fwd<LGate, float, 4, 4>,
                                 launch_fwd_pipe<LGate, float, 4, 2>, launch_fwd_pipe<LGate, float, 2, 2>};
 const FwdLauncher kGateBF[] = {launch_fwd_pipe<LGate, bf16_bits, 4, 4>, launch_fwd<LGate, bf16_bits, 4, 4>};
-const BwdLauncher kGateB[] = {launch_bwd<LGate, 2, 4>, launch_bwd<LGate, 1, 2>};
+const BwdLauncher kGateB[] = {launch_bwd<LGate, 2, 4>, launch_bwd<LGate, 1, 2>,
+                              launch_bwd_pipe<LGate, 2, 4>};
 
 const FwdLauncher kMaceF32[] = {launch_fwd_pipe<LMace, float, 4, 2>, launch_fwd<LMace, float, 2, 1>,
                                 launch_fwd_pipe<LMace, float, 2, 1>, launch_fwd_pipe<LMace, float, 4, 1>};
 const FwdLauncher kMaceBF[] = {launch_fwd_pipe<LMace, bf16_bits, 4, 2>, launch_fwd<LMace, bf16_bits, 2, 1>,
                                launch_fwd_pipe<LMace, bf16_bits, 2, 1>};
-const BwdLauncher kMaceB[] = {launch_bwd<LMace, 4, 2>, launch_bwd<LMace, 2, 1>};
+const BwdLauncher kMaceB[] = {launch_bwd_pipe<LMace, 2, 1>, launch_bwd<LMace, 4, 2>,
+                              launch_bwd<LMace, 2, 1>, launch_bwd_pipe<LMace, 4, 2>};
 
 const FwdLauncher kBigF32[] = {launch_fwd_pipe<LBig, float, 2, 2>, launch_fwd<LBig, float, 4, 4>,
                                launch_fwd_pipe<LBig, float, 4, 4>};
 const FwdLauncher kBigBF[] = {launch_fwd_pipe<LBig, bf16_bits, 2, 2>, launch_fwd<LBig, bf16_bits, 4, 4>,
                               launch_fwd_pipe<LBig, bf16_bits, 4, 4>, launch_fwd_pipe<LBig, bf16_bits, 4, 2>,
                               launch_fwd_pipe<LBig, bf16_bits, 2, 1>};
-const BwdLauncher kBigB[] = {launch_bwd<LBig, 2, 2>};
+const BwdLauncher kBigB[] = {launch_bwd<LBig, 2, 2>, launch_bwd_pipe<LBig, 2, 2>};
 
 #define E3C_N(a) (int)(sizeof(a) / sizeof((a)[0]))
 
 const KernelSet kSets[] = {
-    {8, natural_code(1), 2, natural_code(2), &kTinyT, kTinyF32, E3C_N(kTinyF32), kTinyBF,
+    {8, natural_code(1), 2, natural_code(2), &kTinyT, kTinyCG.v, kTinyF32, E3C_N(kTinyF32), kTinyBF,
      E3C_N(kTinyBF), kTinyB, E3C_N(kTinyB)},
-    {32, natural_code(1), 3, natural_code(2), &kGateT, kGateF32, E3C_N(kGateF32), kGateBF,
+    {32, natural_code(1), 3, natural_code(2), &kGateT, kGateCG.v, kGateF32, E3C_N(kGateF32), kGateBF,
      E3C_N(kGateBF), kGateB, E3C_N(kGateB)},
-    {128, natural_code(1), 3, natural_code(3), &kMaceT, kMaceF32, E3C_N(kMaceF32), kMaceBF,
+    {128, natural_code(1), 3, natural_code(3), &kMaceT, kMaceCG.v, kMaceF32, E3C_N(kMaceF32), kMaceBF,
      E3C_N(kMaceBF), kMaceB, E3C_N(kMaceB)},
-    {64, natural_code(2), 3, natural_code(3), &kBigT, kBigF32, E3C_N(kBigF32), kBigBF,
+    {64, natural_code(2), 3, natural_code(3), &kBigT, kBigCG.v, kBigF32, E3C_N(kBigF32), kBigBF,
      E3C_N(kBigBF), kBigB, E3C_N(kBigB)},
 };
 
@@ -854,7 +1081,53 @@ __global__ void validate_kernel(const int* __restrict__ src, const int* __restri
   }
 }
 
+__global__ void __launch_bounds__(256) stream_copy_kernel(const f32x4* __restrict__ src,
+                                                         f32x4* __restrict__ dst, size_t n4) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n4; i += 4 * stride) {
+    const f32x4 a = __builtin_nontemporal_load(src + i);
+    const f32x4 b = __builtin_nontemporal_load(src + i + stride);
+    const f32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const f32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+    __builtin_nontemporal_store(a, dst + i);
+    __builtin_nontemporal_store(b, dst + i + stride);
+    __builtin_nontemporal_store(c, dst + i + 2 * stride);
+    __builtin_nontemporal_store(d, dst + i + 3 * stride);
+  }
+  for (; i < n4; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+__global__ void __launch_bounds__(256) stream_read_kernel(const f32x4* __restrict__ src, size_t n4,
+                                                         float* __restrict__ out) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (; i + 3 * stride < n4; i += 4 * stride) {
+    acc += __builtin_nontemporal_load(src + i);
+    acc += __builtin_nontemporal_load(src + i + stride);
+    acc += __builtin_nontemporal_load(src + i + 2 * stride);
+    acc += __builtin_nontemporal_load(src + i + 3 * stride);
+  }
+  for (; i < n4; i += stride) acc += __builtin_nontemporal_load(src + i);
+  const float v = acc.x + acc.y + acc.z + acc.w;
+  if (v == 1234.5678f) out[0] = v;   // keeps the loads alive; never true for the calibration data
+}
+
 }  // namespace
+
+hipError_t launch_stream(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+  const size_t n4 = bytes / 16;
+  const unsigned blocks = 256 * 16;
+  if (dst) {
+    hipLaunchKernelGGL(stream_copy_kernel, dim3(blocks), dim3(256), 0, stream,
+                       static_cast<const f32x4*>(src), static_cast<f32x4*>(dst), n4);
+  } else {
+    hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, stream,
+                       static_cast<const f32x4*>(src), n4, const_cast<float*>(static_cast<const float*>(src)));
+  }
+  return hipGetLastError();
+}
 
 const KernelSet* find_kernels(int channels, uint32_t xcode, int lmax, uint32_t ocode) {
   for (const KernelSet& k : kSets)

@@ -17,8 +17,9 @@
 // the values and checks that nothing outside the pattern is nonzero).
 //
 // Everything here is constexpr so that kernels can be fully unrolled with the
-// pattern known at compile time, while the coefficient VALUES are produced at
-// run time by the host builder in exactly this enumeration order.
+// pattern and the coefficient values known at compile time; the host plan
+// builder produces the same values at run time, in this enumeration order, and
+// checks the two tables against each other.
 #pragma once
 
 #include <cstdint>
@@ -121,6 +122,139 @@ constexpr bool k_nonzero(const LayoutTables& t, int p, int m3, int m1) {
   return false;
 }
 
+// ------------------------------------------------ compile-time CG values --
+//
+// The kernels take the real CG values as compile-time constants (instruction
+// literals), evaluated here from the same definitions the host plan builder
+// uses: Racah's formula in binomial form (exact 64-bit integer sums), the
+// complex -> real spherical-harmonic basis change (Y_real = U Y_complex,
+// Condon-Shortley phases), one global phase, and the sign rule (first nonzero
+// entry in (m1, m2, m3) order positive).  The plan checks these tables against
+// its runtime tables before binding a layout to its kernels.
+
+constexpr double cx_sqrt(double v) {
+  if (!(v > 0.0)) return 0.0;
+  double r = v > 1.0 ? v : 1.0;
+  for (int i = 0; i < 200; ++i) {
+    const double n = 0.5 * (r + v / r);
+    if (n == r) break;
+    r = n;
+  }
+  return r;
+}
+
+constexpr int64_t cx_binom(int n, int k) {
+  if (k < 0 || k > n) return 0;
+  if (k > n - k) k = n - k;
+  int64_t r = 1;
+  for (int i = 1; i <= k; ++i) r = r * (n - k + i) / i;
+  return r;
+}
+
+constexpr double cx_complex_cg(int j1, int m1, int j2, int m2, int J, int M) {
+  if (M != m1 + m2 || J < iabs(j1 - j2) || J > j1 + j2) return 0.0;
+  if (iabs(m1) > j1 || iabs(m2) > j2 || iabs(M) > J) return 0.0;
+  const int a = j1 + j2 - J, b = j1 - j2 + J, c = -j1 + j2 + J;
+  int64_t S = 0;
+  for (int k = 0; k <= a; ++k) {
+    const int i1 = j1 - m1 - k, i2 = j2 + m2 - k;
+    if (i1 < 0 || i1 > b || i2 < 0 || i2 > c) continue;
+    const int64_t term = cx_binom(a, k) * cx_binom(b, i1) * cx_binom(c, i2);
+    S += (k & 1) ? -term : term;
+  }
+  const int64_t num = (2 * J + 1) * cx_binom(2 * j1, a) * cx_binom(2 * j2, a);
+  const int64_t den = (int64_t)(a + b + c + 1) * cx_binom(a + b + c, a) * cx_binom(2 * j1, j1 - m1) *
+                      cx_binom(2 * j2, j2 - m2) * cx_binom(2 * J, J - M);
+  return (double)S * cx_sqrt((double)num / (double)den);
+}
+
+struct Cplx {
+  double re, im;
+};
+constexpr Cplx cmul(Cplx a, Cplx b) { return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re}; }
+constexpr Cplx cconj(Cplx a) { return {a.re, -a.im}; }
+
+// Row m of U (Y_real = U Y_complex): up to two (mu, value) entries.
+struct BasisRow {
+  int n;
+  int mu[2];
+  Cplx v[2];
+};
+
+constexpr BasisRow basis_row(int m) {
+  const double r = 0.70710678118654752440;
+  BasisRow row{};
+  if (m == 0) {
+    row.n = 1;
+    row.mu[0] = 0;
+    row.v[0] = {1.0, 0.0};
+    return row;
+  }
+  const double sgn = (iabs(m) & 1) ? -1.0 : 1.0;
+  row.n = 2;
+  if (m > 0) {
+    row.mu[0] = m;  row.v[0] = {sgn * r, 0.0};
+    row.mu[1] = -m; row.v[1] = {r, 0.0};
+  } else {
+    row.mu[0] = m;  row.v[0] = {0.0, r};
+    row.mu[1] = -m; row.v[1] = {0.0, -sgn * r};
+  }
+  return row;
+}
+
+constexpr Cplx real_cg_complex_entry(int l1, int l2, int l3, int i, int j, int k) {
+  const BasisRow r1 = basis_row(i - l1), r2 = basis_row(j - l2), r3 = basis_row(k - l3);
+  Cplx s{0.0, 0.0};
+  for (int x = 0; x < r1.n; ++x)
+    for (int y = 0; y < r2.n; ++y)
+      for (int z = 0; z < r3.n; ++z) {
+        const double cg = cx_complex_cg(l1, r1.mu[x], l2, r2.mu[y], l3, r3.mu[z]);
+        if (cg == 0.0) continue;
+        const Cplx t = cmul(cmul(r3.v[z], cconj(r1.v[x])), cconj(r2.v[y]));
+        s.re += cg * t.re;
+        s.im += cg * t.im;
+      }
+  return s;
+}
+
+template <int NNZ>
+struct CGValues {
+  float v[NNZ > 0 ? NNZ : 1];
+};
+
+// Real CG values of every pattern entry, path by path.  The pattern lists
+// (m1, m2, m3) in lexicographic order and contains every nonzero entry, so
+// the global phase (from the largest entry) and the sign (first nonzero entry
+// positive) can be taken over the pattern alone.
+template <int NNZ>
+constexpr CGValues<NNZ> make_cg_values(const LayoutTables& t) {
+  CGValues<NNZ> out{};
+  Cplx z[kMaxNnz]{};
+  for (int p = 0; p < t.num_paths; ++p) {
+    const PathInfo& P = t.path[p];
+    Cplx big{0.0, 0.0};
+    double amax = 0.0;
+    for (int q = P.nnz_begin; q < P.nnz_end; ++q) {
+      z[q] = real_cg_complex_entry(P.l1, P.l2, P.l3, t.entry[q].m1, t.entry[q].m2, t.entry[q].m3);
+      const double m2 = z[q].re * z[q].re + z[q].im * z[q].im;
+      if (m2 > amax) { amax = m2; big = z[q]; }
+    }
+    const double mag = cx_sqrt(amax);
+    const Cplx unphase{big.re / mag, -big.im / mag};
+    double sign = 0.0;
+    for (int q = P.nnz_begin; q < P.nnz_end && sign == 0.0; ++q) {
+      const double v = cmul(z[q], unphase).re;
+      if (v > 1e-14 * mag) sign = 1.0;
+      if (v < -1e-14 * mag) sign = -1.0;
+    }
+    for (int q = P.nnz_begin; q < P.nnz_end; ++q) {
+      const double v = cmul(z[q], unphase).re;
+      out.v[q] = (v > -1e-14 * mag && v < 1e-14 * mag) ? 0.0f : (float)(sign * v);
+    }
+  }
+  return out;
+}
+
 // Compile-time layout: channels and block codes.
 template <int C_, uint32_t XCODE_, int L_, uint32_t OCODE_>
 struct Layout {
@@ -134,6 +268,7 @@ struct Layout {
   static constexpr int NO = T.num_out;
   static constexpr int NP = T.num_paths;
   static constexpr int NNZ = T.nnz;
+  static constexpr CGValues<NNZ> CG = make_cg_values<NNZ>(T);
 };
 
 // natural-parity block code for l = 0..lmax (0e + 1o + 2e + ...)

@@ -30,7 +30,8 @@ EXPORTED = [
     "e3conv_plan", "e3conv_plan_destroy", "e3conv_plan_shape", "e3conv_plan_paths",
     "e3conv_plan_coefficients", "e3conv_plan_supported", "e3conv_forward",
     "e3conv_backward_workspace_size", "e3conv_backward", "e3conv_csr_from_receivers",
-    "e3conv_validate_graph", "e3conv_receiver_order", "e3conv_plan_set_variant",
+    "e3conv_validate_graph", "e3conv_receiver_order", "e3conv_stream_reference",
+    "e3conv_plan_set_variant",
     "e3conv_plan_num_variants",
     "e3conv_status_string", "e3conv_last_error_detail",
 ]
@@ -74,6 +75,7 @@ def load_library(path=LIB_PATH):
         "e3conv_backward": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, P, P, P, P, P,
                              ctypes.c_size_t, P], ctypes.c_int),
         "e3conv_receiver_order": ([P, P, I64, I64, ctypes.c_int, P], ctypes.c_int),
+        "e3conv_stream_reference": ([P, P, ctypes.c_size_t, P], ctypes.c_int),
         "e3conv_csr_from_receivers": ([P, I64, I64, P, P], ctypes.c_int),
         "e3conv_validate_graph": ([P, P, I64, I64, ctypes.c_int], ctypes.c_int),
         "e3conv_plan_set_variant": ([P, ctypes.c_int, ctypes.c_int], ctypes.c_int),
@@ -256,6 +258,14 @@ def e3conv_validate_graph(src, row_ptr, num_nodes, num_edges):
     r = np.ascontiguousarray(np.asarray(row_ptr), dtype=np.int32)
     _check(lib.e3conv_validate_graph(s.ctypes.data_as(P), r.ctypes.data_as(P), int(num_nodes),
                                      int(num_edges), 0))
+
+
+def e3conv_stream_reference(src, dst=None, stream=None):
+    """Streaming reference: copy src into dst (same size), or read src only if dst is None."""
+    nbytes = src.numel() * src.element_size()
+    if dst is not None and dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst sizes differ")
+    _check(load_library().e3conv_stream_reference(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
 
 def e3conv_status_string(status):

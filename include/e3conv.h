@@ -173,6 +173,16 @@ e3conv_status e3conv_receiver_order(const int32_t* row_ptr, const int32_t* src, 
 e3conv_status e3conv_validate_graph(const int32_t* src, const int32_t* row_ptr,
                                     int64_t num_nodes, int64_t num_edges, int on_device);
 
+/* Streaming reference (measurement aid, not part of the convolution): copies
+ * `bytes` from src to dst with 16-byte non-temporal loads and stores, or, with
+ * dst = NULL, only reads src.  It measures the bandwidth this device attains
+ * for plain streaming, the practical ceiling beside the published HBM peak,
+ * and serves as the known-size kernel that scales memory counters.  bytes must
+ * be a multiple of 16 and both buffers 16-byte aligned; asynchronous on
+ * hip_stream.  A read-only pass never writes src unless its data sums to
+ * 1234.5678 in some lane (calibration data must avoid that value). */
+e3conv_status e3conv_stream_reference(const void* src, void* dst, size_t bytes, void* hip_stream);
+
 /* Tuning: select a kernel variant for this plan (0 = default).  Variants
  * differ only in how lanes map to channels and edges; all compute the same
  * result.  Returns E3CONV_ERR_UNSUPPORTED for an unknown variant.  Plans are
