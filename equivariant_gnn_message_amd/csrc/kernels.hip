@@ -305,7 +305,8 @@ __global__ void __launch_bounds__(256) conv_fwd(FwdParams prm) {
 // (the loop body is unrolled twice), so no per-edge register copies.  Raw
 // values (bf16 words) are kept until use.  Per path the contraction is
 // reassociated as acc[o3+m3] += sum_m1 K[m3][m1] (s[p] x[o1+m1]), which needs
-// (2 l1 + 1) products per path instead of (2 l3 + 1) mixing FMAs.
+// (2 l1 + 1) products per path instead of (2 l3 + 1) mixing FMAs; paths with
+// l1 > l3 keep the mixing form, which is then the cheaper one.
 
 template <typename IN, int N>
 struct RawVec;
@@ -406,25 +407,50 @@ __device__ __forceinline__ void edge_accumulate(const EdgeBuf<LY, IN, CPL>& buf,
     constexpr int D1 = 2 * P.l1 + 1, D3 = 2 * P.l3 + 1;
     float K[D3][D1];
     build_k<LY, p, D3, D1>(yv, K);
-    float u[D1][CPL];
-    sfor<0, D1>([&](auto m1c) {
-      constexpr int m1 = decltype(m1c)::value;
-      if constexpr (first_m3(LY::T, p, m1) >= 0) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) u[m1][c] = buf.s[p].get(c) * buf.x[P.o1 + m1].get(c);
-      }
-    });
-    sfor<0, D3>([&](auto m3c) {
-      constexpr int m3 = decltype(m3c)::value;
+    if constexpr (D1 <= D3) {
+      // acc += K (s x): 2 l1 + 1 products per channel
+      float u[D1][CPL];
       sfor<0, D1>([&](auto m1c) {
         constexpr int m1 = decltype(m1c)::value;
-        if constexpr (k_nonzero(LY::T, p, m3, m1)) {
+        if constexpr (first_m3(LY::T, p, m1) >= 0) {
 #pragma unroll
-          for (int c = 0; c < CPL; ++c)
-            acc[P.o3 + m3][c] = __builtin_fmaf(K[m3][m1], u[m1][c], acc[P.o3 + m3][c]);
+          for (int c = 0; c < CPL; ++c) u[m1][c] = buf.s[p].get(c) * buf.x[P.o1 + m1].get(c);
         }
       });
-    });
+      sfor<0, D3>([&](auto m3c) {
+        constexpr int m3 = decltype(m3c)::value;
+        sfor<0, D1>([&](auto m1c) {
+          constexpr int m1 = decltype(m1c)::value;
+          if constexpr (k_nonzero(LY::T, p, m3, m1)) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+              acc[P.o3 + m3][c] = __builtin_fmaf(K[m3][m1], u[m1][c], acc[P.o3 + m3][c]);
+          }
+        });
+      });
+    } else {
+      // acc += s (K x): 2 l3 + 1 mixing products per channel
+      sfor<0, D3>([&](auto m3c) {
+        constexpr int m3 = decltype(m3c)::value;
+        float tv[CPL];
+        sfor<0, D1>([&](auto m1c) {
+          constexpr int m1 = decltype(m1c)::value;
+          if constexpr (k_nonzero(LY::T, p, m3, m1)) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+              if constexpr (first_m1(LY::T, p, m3) == m1) {
+                tv[c] = K[m3][m1] * buf.x[P.o1 + m1].get(c);
+              } else {
+                tv[c] = __builtin_fmaf(K[m3][m1], buf.x[P.o1 + m1].get(c), tv[c]);
+              }
+            }
+          }
+        });
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          acc[P.o3 + m3][c] = __builtin_fmaf(buf.s[p].get(c), tv[c], acc[P.o3 + m3][c]);
+      });
+    }
   });
 }
 
