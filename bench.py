@@ -121,9 +121,16 @@ def alg_bytes(w, N, E, b_in):
     return fwd, bwd
 
 
+def kernel_source_files():
+    csrc = os.path.join(ROOT, "equivariant_gnn_message_amd", "csrc")
+    return sorted(f for f in os.listdir(csrc) if f.endswith(".hip") or f in
+                  ("conv_kernels.h", "kernels.h", "layout.h"))
+
+
 def kernel_source_hash():
+    """sha256[:16] of the device sources (every .hip file and the kernel headers)."""
     h = hashlib.sha256()
-    for f in ("kernels.hip", "layout.h", "kernels.h"):
+    for f in kernel_source_files():
         with open(os.path.join(ROOT, "equivariant_gnn_message_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -28,8 +28,10 @@ struct e3conv_plan_s {
   // sparse export
   std::vector<int> ix, iy, ip, iout;
   std::vector<double> val;
-  // compiled kernels (nullptr if none) and their coefficient vector
+  e3conv_ordering ordering = E3CONV_RECEIVER;
+  // compiled kernels of the layout (nullptr if none) and of the plan's ordering
   const e3c::KernelSet* ks = nullptr;
+  const e3c::OrderingKernels* kk = nullptr;
   int fwd_variant = 0;
   int bwd_variant = 0;
 };
@@ -111,6 +113,7 @@ bool bind_kernels(e3conv_plan_s* p, std::string* why) {
     }
   }
   p->ks = ks;
+  p->kk = p->ordering == E3CONV_SENDER ? &ks->sender : &ks->receiver;
   return true;
 }
 
@@ -137,8 +140,17 @@ const char* e3conv_last_error_detail(void) { return g_last_error.c_str(); }
 
 e3conv_status e3conv_plan(const char* irreps_in, int sh_lmax, const char* irreps_out,
                           float avg_num_neighbors, e3conv_plan_t* plan_out) {
+  return e3conv_plan_ordered(irreps_in, sh_lmax, irreps_out, avg_num_neighbors, E3CONV_RECEIVER,
+                             plan_out);
+}
+
+e3conv_status e3conv_plan_ordered(const char* irreps_in, int sh_lmax, const char* irreps_out,
+                                  float avg_num_neighbors, e3conv_ordering ordering,
+                                  e3conv_plan_t* plan_out) {
   if (!plan_out) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan_out is NULL");
   *plan_out = nullptr;
+  if (ordering != E3CONV_RECEIVER && ordering != E3CONV_SENDER)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "ordering must be RECEIVER or SENDER");
   if (!irreps_in || !irreps_out) return fail(E3CONV_ERR_INVALID_ARGUMENT, "irreps string is NULL");
   if (sh_lmax < 0 || sh_lmax > 6) return fail(E3CONV_ERR_INVALID_ARGUMENT, "sh_lmax must be in 0..6");
   if (!(avg_num_neighbors > 0.0f) || !std::isfinite(avg_num_neighbors))
@@ -166,6 +178,7 @@ e3conv_status e3conv_plan(const char* irreps_in, int sh_lmax, const char* irreps
   p->channels = C;
   p->lmax = sh_lmax;
   p->avg = avg_num_neighbors;
+  p->ordering = ordering;
   for (const Irrep& b : p->xin) p->num_x += 2 * b.l + 1;
   for (const Irrep& b : p->out) p->num_out += 2 * b.l + 1;
   p->num_y = (sh_lmax + 1) * (sh_lmax + 1);
@@ -247,27 +260,33 @@ e3conv_status e3conv_plan_coefficients(e3conv_plan_t p, int* nnz, int* ix, int* 
   return ok();
 }
 
+e3conv_status e3conv_plan_ordering(e3conv_plan_t p, e3conv_ordering* ordering) {
+  if (!p || !ordering) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan or ordering is NULL");
+  *ordering = p->ordering;
+  return ok();
+}
+
 e3conv_status e3conv_plan_supported(e3conv_plan_t p, int* fwd_f32, int* fwd_bf16, int* bwd_f32) {
   if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
-  if (fwd_f32) *fwd_f32 = p->ks && p->ks->n_fwd_f32 > 0;
-  if (fwd_bf16) *fwd_bf16 = p->ks && p->ks->n_fwd_bf16 > 0;
-  if (bwd_f32) *bwd_f32 = p->ks && p->ks->n_bwd_f32 > 0;
+  if (fwd_f32) *fwd_f32 = p->kk && p->kk->n_fwd_f32 > 0;
+  if (fwd_bf16) *fwd_bf16 = p->kk && p->kk->n_fwd_bf16 > 0;
+  if (bwd_f32) *bwd_f32 = p->kk && p->kk->n_bwd_f32 > 0;
   return ok();
 }
 
 e3conv_status e3conv_plan_num_variants(e3conv_plan_t p, e3conv_dtype dt, int* nf, int* nb) {
   if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (dt != E3CONV_F32 && dt != E3CONV_BF16) return fail(E3CONV_ERR_INVALID_ARGUMENT, "bad dtype");
-  if (nf) *nf = p->ks ? (dt == E3CONV_F32 ? p->ks->n_fwd_f32 : p->ks->n_fwd_bf16) : 0;
-  if (nb) *nb = p->ks ? (dt == E3CONV_F32 ? p->ks->n_bwd_f32 : 0) : 0;
+  if (nf) *nf = p->kk ? (dt == E3CONV_F32 ? p->kk->n_fwd_f32 : p->kk->n_fwd_bf16) : 0;
+  if (nb) *nb = p->kk ? (dt == E3CONV_F32 ? p->kk->n_bwd_f32 : 0) : 0;
   return ok();
 }
 
 e3conv_status e3conv_plan_set_variant(e3conv_plan_t p, int fv, int bv) {
   if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
-  if (!p->ks) return fail(E3CONV_ERR_UNSUPPORTED, "no kernels for this layout");
-  const int maxf = p->ks->n_fwd_f32 > p->ks->n_fwd_bf16 ? p->ks->n_fwd_f32 : p->ks->n_fwd_bf16;
-  if (fv < 0 || fv >= maxf || bv < 0 || bv >= (p->ks->n_bwd_f32 > 0 ? p->ks->n_bwd_f32 : 1))
+  if (!p->kk) return fail(E3CONV_ERR_UNSUPPORTED, "no kernels for this layout");
+  const int maxf = p->kk->n_fwd_f32 > p->kk->n_fwd_bf16 ? p->kk->n_fwd_f32 : p->kk->n_fwd_bf16;
+  if (fv < 0 || fv >= maxf || bv < 0 || bv >= (p->kk->n_bwd_f32 > 0 ? p->kk->n_bwd_f32 : 1))
     return fail(E3CONV_ERR_UNSUPPORTED, "unknown kernel variant");
   p->fwd_variant = fv;
   p->bwd_variant = bv;
@@ -286,21 +305,52 @@ static e3conv_status check_sizes(int64_t N, int64_t E, int channels, int width) 
 e3conv_status e3conv_forward(e3conv_plan_t p, e3conv_dtype dt, const void* x, const void* y,
                              const void* s, const int32_t* src, const int32_t* row_ptr,
                              const int32_t* order, int64_t N, int64_t E, float* out, void* stream) {
+  return e3conv_forward_masked(p, dt, x, y, s, src, row_ptr, order, N, E, N, out, stream);
+}
+
+e3conv_status e3conv_forward_masked(e3conv_plan_t p, e3conv_dtype dt, const void* x, const void* y,
+                                    const void* s, const int32_t* src, const int32_t* row_ptr,
+                                    const int32_t* order, int64_t N, int64_t E,
+                                    int64_t num_real_nodes, float* out, void* stream) {
+  if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (dt != E3CONV_F32 && dt != E3CONV_BF16) return fail(E3CONV_ERR_INVALID_ARGUMENT, "bad dtype");
+  e3conv_status st = check_sizes(N, E, p->channels, p->num_out > p->num_x ? p->num_out : p->num_x);
+  if (st != E3CONV_OK) return st;
+  if (num_real_nodes < 0 || num_real_nodes > N)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "num_real_nodes must be in [0, num_nodes]");
+  if (N == 0) return ok();
+  if (!out || !row_ptr || (E > 0 && (!x || !y || !s || !src)))
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  if (!p->kk) return fail(E3CONV_ERR_UNSUPPORTED, "no compiled kernel for this layout");
+  const int n = dt == E3CONV_F32 ? p->kk->n_fwd_f32 : p->kk->n_fwd_bf16;
+  if (n == 0) return fail(E3CONV_ERR_UNSUPPORTED, "no compiled kernel for this dtype");
+  const e3c::FwdLauncher* L = dt == E3CONV_F32 ? p->kk->fwd_f32 : p->kk->fwd_bf16;
+  const int v = p->fwd_variant < n ? p->fwd_variant : 0;
+  e3c::FwdParams prm{x, y, s, src, row_ptr, order, out, (int)N, (int)E, 1.0f / p->avg,
+                     (int)num_real_nodes};
+  const hipError_t err = L[v](prm, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "forward launch");
+  return ok();
+}
+
+e3conv_status e3conv_jvp(e3conv_plan_t p, e3conv_dtype dt, const void* x, const void* y,
+                         const void* s, const void* dx, const void* dy, const void* ds,
+                         const int32_t* src, const int32_t* row_ptr, const int32_t* order,
+                         int64_t N, int64_t E, float* out, float* out_dot, void* stream) {
   if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (dt != E3CONV_F32 && dt != E3CONV_BF16) return fail(E3CONV_ERR_INVALID_ARGUMENT, "bad dtype");
   e3conv_status st = check_sizes(N, E, p->channels, p->num_out > p->num_x ? p->num_out : p->num_x);
   if (st != E3CONV_OK) return st;
   if (N == 0) return ok();
-  if (!out || !row_ptr || (E > 0 && (!x || !y || !s || !src)))
+  if (!out_dot || !row_ptr || (E > 0 && (!x || !y || !s || !dx || !dy || !ds || !src)))
     return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
-  if (!p->ks) return fail(E3CONV_ERR_UNSUPPORTED, "no compiled kernel for this layout");
-  const int n = dt == E3CONV_F32 ? p->ks->n_fwd_f32 : p->ks->n_fwd_bf16;
-  if (n == 0) return fail(E3CONV_ERR_UNSUPPORTED, "no compiled kernel for this dtype");
-  const e3c::FwdLauncher* L = dt == E3CONV_F32 ? p->ks->fwd_f32 : p->ks->fwd_bf16;
-  const int v = p->fwd_variant < n ? p->fwd_variant : 0;
-  e3c::FwdParams prm{x, y, s, src, row_ptr, order, out, (int)N, (int)E, 1.0f / p->avg};
-  const hipError_t err = L[v](prm, static_cast<hipStream_t>(stream));
-  if (err != hipSuccess) return hip_fail(err, "forward launch");
+  if (!p->kk) return fail(E3CONV_ERR_UNSUPPORTED, "no compiled kernel for this layout");
+  const e3c::JvpLauncher L = dt == E3CONV_F32 ? p->kk->jvp_f32 : p->kk->jvp_bf16;
+  if (!L) return fail(E3CONV_ERR_UNSUPPORTED, "no compiled forward-mode kernel for this dtype");
+  e3c::JvpParams prm{x, y, s, dx, dy, ds, src, row_ptr, order, out, out_dot,
+                     (int)N, (int)E, 1.0f / p->avg, (int)N};
+  const hipError_t err = L(prm, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "jvp launch");
   return ok();
 }
 
@@ -316,23 +366,35 @@ e3conv_status e3conv_backward(e3conv_plan_t p, e3conv_dtype dt, const void* x, c
                               const int32_t* order, int64_t N, int64_t E, const float* g,
                               float* gx, float* gy,
                               float* gs, void* workspace, size_t workspace_bytes, void* stream) {
+  return e3conv_backward_masked(p, dt, x, y, s, src, row_ptr, order, N, E, N, g, gx, gy, gs,
+                                workspace, workspace_bytes, stream);
+}
+
+e3conv_status e3conv_backward_masked(e3conv_plan_t p, e3conv_dtype dt, const void* x, const void* y,
+                                     const void* s, const int32_t* src, const int32_t* row_ptr,
+                                     const int32_t* order, int64_t N, int64_t E,
+                                     int64_t num_real_nodes, const float* g, float* gx, float* gy,
+                                     float* gs, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
   (void)workspace;
   (void)workspace_bytes;
   if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (dt != E3CONV_F32) return fail(E3CONV_ERR_UNSUPPORTED, "the reverse pass is fp32 only");
   e3conv_status st = check_sizes(N, E, p->channels, p->num_out > p->num_x ? p->num_out : p->num_x);
   if (st != E3CONV_OK) return st;
+  if (num_real_nodes < 0 || num_real_nodes > N)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "num_real_nodes must be in [0, num_nodes]");
   if (!gx && !gy && !gs) return ok();
   if (N == 0) return ok();
   if (!gx || !g || !row_ptr || (E > 0 && (!x || !y || !s || !src || !gy || !gs)))
     return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
-  if (!p->ks || p->ks->n_bwd_f32 == 0)
+  if (!p->kk || p->kk->n_bwd_f32 == 0)
     return fail(E3CONV_ERR_UNSUPPORTED, "no compiled reverse kernel for this layout");
-  const int v = p->bwd_variant < p->ks->n_bwd_f32 ? p->bwd_variant : 0;
+  const int v = p->bwd_variant < p->kk->n_bwd_f32 ? p->bwd_variant : 0;
   e3c::BwdParams prm{static_cast<const float*>(x), static_cast<const float*>(y),
                      static_cast<const float*>(s), src, row_ptr, order, g, gx, gy, gs, (int)N, (int)E,
-                     1.0f / p->avg};
-  const hipError_t err = p->ks->bwd_f32[v](prm, static_cast<hipStream_t>(stream));
+                     1.0f / p->avg, (int)num_real_nodes};
+  const hipError_t err = p->kk->bwd_f32[v](prm, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "backward launch");
   return ok();
 }

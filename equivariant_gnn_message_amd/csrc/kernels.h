@@ -20,6 +20,7 @@ struct FwdParams {
   int num_nodes;
   int num_edges;
   float inv_avg;
+  int num_real;         // receivers b >= num_real are padding: zero rows, no messages
 };
 
 struct BwdParams {
@@ -36,10 +37,45 @@ struct BwdParams {
   int num_nodes;
   int num_edges;
   float inv_avg;
+  int num_real;         // edges into receivers b >= num_real get zero grad_y / grad_s
+};
+
+struct JvpParams {
+  const void* x;        // primal operands, as in FwdParams
+  const void* y;
+  const void* s;
+  const void* dx;       // tangents, same shapes and dtype as x, y, s
+  const void* dy;
+  const void* ds;
+  const int* src;
+  const int* row_ptr;
+  const int* order;
+  float* out;           // (N, NO, C) primal output, or nullptr
+  float* out_dot;       // (N, NO, C) tangent output
+  int num_nodes;
+  int num_edges;
+  float inv_avg;
+  int num_real;
 };
 
 using FwdLauncher = hipError_t (*)(const FwdParams&, hipStream_t);
 using BwdLauncher = hipError_t (*)(const BwdParams&, hipStream_t);
+using JvpLauncher = hipError_t (*)(const JvpParams&, hipStream_t);
+
+// Kernels of one graph ordering: RECEIVER (edges grouped by receiver, x
+// gathered at the sender) or SENDER (edges grouped by sender, x gathered at
+// the receiver, odd-l edge-feature blocks negated: the reverse edge's
+// features under the graded symmetry y_ab = (-1)^l y_ba).
+struct OrderingKernels {
+  const FwdLauncher* fwd_f32;   // variant lists, [0] is the default
+  int n_fwd_f32;
+  const FwdLauncher* fwd_bf16;
+  int n_fwd_bf16;
+  const BwdLauncher* bwd_f32;
+  int n_bwd_f32;
+  JvpLauncher jvp_f32;
+  JvpLauncher jvp_bf16;
+};
 
 struct KernelSet {
   int channels;
@@ -48,16 +84,18 @@ struct KernelSet {
   uint32_t ocode;
   const LayoutTables* tables;   // path / pattern enumeration the kernels use
   const float* cg_values;       // compile-time CG values, one per pattern entry
-  const FwdLauncher* fwd_f32;
-  int n_fwd_f32;
-  const FwdLauncher* fwd_bf16;
-  int n_fwd_bf16;
-  const BwdLauncher* bwd_f32;
-  int n_bwd_f32;
+  OrderingKernels receiver;
+  OrderingKernels sender;
 };
 
 // Returns nullptr if no kernels are compiled for the layout.
 const KernelSet* find_kernels(int channels, uint32_t xcode, int lmax, uint32_t ocode);
+
+// One per compiled layout (defined in the layout_*.hip files).
+const KernelSet* kernels_tiny();
+const KernelSet* kernels_gate();
+const KernelSet* kernels_mace();
+const KernelSet* kernels_big();
 
 // Streaming reference kernels (copy when dst != nullptr, else read only).
 hipError_t launch_stream(const void* src, void* dst, size_t bytes, hipStream_t stream);

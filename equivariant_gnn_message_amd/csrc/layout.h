@@ -271,6 +271,27 @@ struct Layout {
   static constexpr CGValues<NNZ> CG = make_cg_values<NNZ>(T);
 };
 
+// SENDER graph ordering (e3j Convolution page, note on graph_ordering): with
+// the edges grouped by sender, node b's message is assembled from its
+// outgoing edges e = (b -> a) as (x_a (x) p.y_e) (.) s_e, i.e. from the
+// reverse edges' features under the page's symmetry assumptions
+// y_ab = (-1)^l y_ba (per l block) and s_ab = s_ba.  The parity (-1)^l2 of the
+// edge-feature block is folded into the path's CG constants; everything else
+// is the RECEIVER kernel with the roles of the two endpoints exchanged.
+template <int NNZ>
+constexpr CGValues<NNZ> parity_flipped(const LayoutTables& t, const CGValues<NNZ>& cg) {
+  CGValues<NNZ> r = cg;
+  for (int p = 0; p < t.num_paths; ++p)
+    if (t.path[p].l2 & 1)
+      for (int q = t.path[p].nnz_begin; q < t.path[p].nnz_end; ++q) r.v[q] = -r.v[q];
+  return r;
+}
+
+template <class LY>
+struct SenderOrdered : LY {
+  static constexpr CGValues<LY::NNZ> CG = parity_flipped<LY::NNZ>(LY::T, LY::CG);
+};
+
 // natural-parity block code for l = 0..lmax (0e + 1o + 2e + ...)
 constexpr uint32_t natural_code(int lmax) {
   uint32_t c = 0;

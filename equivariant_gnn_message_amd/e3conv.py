@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libe3conv.so")
 E3CONV_OK = 0
 E3CONV_F32 = 0
 E3CONV_BF16 = 1
+E3CONV_RECEIVER = 0
+E3CONV_SENDER = 1
 
 STATUS_NAMES = {
     0: "E3CONV_OK", 1: "E3CONV_ERR_INVALID_ARGUMENT", 2: "E3CONV_ERR_PARSE",
@@ -27,9 +29,11 @@ STATUS_NAMES = {
 
 # every symbol include/e3conv.h declares
 EXPORTED = [
-    "e3conv_plan", "e3conv_plan_destroy", "e3conv_plan_shape", "e3conv_plan_paths",
-    "e3conv_plan_coefficients", "e3conv_plan_supported", "e3conv_forward",
-    "e3conv_backward_workspace_size", "e3conv_backward", "e3conv_csr_from_receivers",
+    "e3conv_plan", "e3conv_plan_ordered", "e3conv_plan_ordering", "e3conv_plan_destroy",
+    "e3conv_plan_shape", "e3conv_plan_paths",
+    "e3conv_plan_coefficients", "e3conv_plan_supported", "e3conv_forward", "e3conv_forward_masked",
+    "e3conv_jvp", "e3conv_backward_workspace_size", "e3conv_backward", "e3conv_backward_masked",
+    "e3conv_csr_from_receivers",
     "e3conv_validate_graph", "e3conv_receiver_order", "e3conv_stream_reference",
     "e3conv_plan_set_variant",
     "e3conv_plan_num_variants",
@@ -63,6 +67,9 @@ def load_library(path=LIB_PATH):
     sig = {
         "e3conv_plan": ([ctypes.c_char_p, ctypes.c_int, ctypes.c_char_p, ctypes.c_float,
                          ctypes.POINTER(P)], ctypes.c_int),
+        "e3conv_plan_ordered": ([ctypes.c_char_p, ctypes.c_int, ctypes.c_char_p, ctypes.c_float,
+                                 ctypes.c_int, ctypes.POINTER(P)], ctypes.c_int),
+        "e3conv_plan_ordering": ([P, I32P], ctypes.c_int),
         "e3conv_plan_destroy": ([P], None),
         "e3conv_plan_shape": ([P, I32P, I32P, I32P, I32P, I32P], ctypes.c_int),
         "e3conv_plan_paths": ([P] + [I32P] * 8, ctypes.c_int),
@@ -70,10 +77,15 @@ def load_library(path=LIB_PATH):
                                       ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "e3conv_plan_supported": ([P, I32P, I32P, I32P], ctypes.c_int),
         "e3conv_forward": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, P, P], ctypes.c_int),
+        "e3conv_forward_masked": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P, P],
+                                  ctypes.c_int),
+        "e3conv_jvp": ([P, ctypes.c_int, P, P, P, P, P, P, P, P, P, I64, I64, P, P, P], ctypes.c_int),
         "e3conv_backward_workspace_size": ([P, I64, I64, ctypes.POINTER(ctypes.c_size_t)],
                                            ctypes.c_int),
         "e3conv_backward": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, P, P, P, P, P,
                              ctypes.c_size_t, P], ctypes.c_int),
+        "e3conv_backward_masked": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P, P, P, P, P,
+                                    ctypes.c_size_t, P], ctypes.c_int),
         "e3conv_receiver_order": ([P, P, I64, I64, ctypes.c_int, P], ctypes.c_int),
         "e3conv_stream_reference": ([P, P, ctypes.c_size_t, P], ctypes.c_int),
         "e3conv_csr_from_receivers": ([P, I64, I64, P, P], ctypes.c_int),
@@ -138,6 +150,21 @@ def e3conv_plan(irreps_in, sh_lmax, irreps_out, avg_num_neighbors=1.0):
     return h
 
 
+def e3conv_plan_ordered(irreps_in, sh_lmax, irreps_out, avg_num_neighbors=1.0,
+                        ordering=E3CONV_RECEIVER):
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _check(lib.e3conv_plan_ordered(irreps_in.encode(), int(sh_lmax), irreps_out.encode(),
+                                   float(avg_num_neighbors), int(ordering), ctypes.byref(h)))
+    return h
+
+
+def e3conv_plan_ordering(handle):
+    v = ctypes.c_int()
+    _check(load_library().e3conv_plan_ordering(handle, ctypes.byref(v)))
+    return v.value
+
+
 def e3conv_plan_destroy(handle):
     if handle:
         load_library().e3conv_plan_destroy(handle)
@@ -184,20 +211,56 @@ def e3conv_plan_set_variant(handle, forward_variant=0, backward_variant=0):
     _check(load_library().e3conv_plan_set_variant(handle, int(forward_variant), int(backward_variant)))
 
 
+def _check_graph_args(src, row_ptr, order):
+    import torch
+    _need(src, "src", torch.int32)
+    _need(row_ptr, "row_ptr", torch.int32)
+    if order is not None:
+        _need(order, "order", torch.int32)
+
+
 def e3conv_forward(handle, x, y, s, src, row_ptr, num_nodes, num_edges, out, order=None, stream=None):
     import torch
     dt = _dtype_code(x)
     for t, n in ((x, "x"), (y, "y"), (s, "s")):
         _need(t, n, x.dtype)
-    _need(src, "src", torch.int32)
-    _need(row_ptr, "row_ptr", torch.int32)
+    _check_graph_args(src, row_ptr, order)
     _need(out, "out", torch.float32)
-    if order is not None:
-        _need(order, "order", torch.int32)
     _check(load_library().e3conv_forward(handle, dt, _ptr(x), _ptr(y), _ptr(s), _ptr(src),
                                          _ptr(row_ptr), _ptr(order), int(num_nodes), int(num_edges),
                                          _ptr(out), _stream(stream)))
     return out
+
+
+def e3conv_forward_masked(handle, x, y, s, src, row_ptr, num_nodes, num_edges, num_real_nodes, out,
+                          order=None, stream=None):
+    import torch
+    dt = _dtype_code(x)
+    for t, n in ((x, "x"), (y, "y"), (s, "s")):
+        _need(t, n, x.dtype)
+    _check_graph_args(src, row_ptr, order)
+    _need(out, "out", torch.float32)
+    _check(load_library().e3conv_forward_masked(handle, dt, _ptr(x), _ptr(y), _ptr(s), _ptr(src),
+                                                _ptr(row_ptr), _ptr(order), int(num_nodes),
+                                                int(num_edges), int(num_real_nodes), _ptr(out),
+                                                _stream(stream)))
+    return out
+
+
+def e3conv_jvp(handle, x, y, s, dx, dy, ds, src, row_ptr, num_nodes, num_edges, out, out_dot,
+               order=None, stream=None):
+    import torch
+    dt = _dtype_code(x)
+    for t, n in ((x, "x"), (y, "y"), (s, "s"), (dx, "dx"), (dy, "dy"), (ds, "ds")):
+        _need(t, n, x.dtype)
+    _check_graph_args(src, row_ptr, order)
+    _need(out_dot, "out_dot", torch.float32)
+    if out is not None:
+        _need(out, "out", torch.float32)
+    _check(load_library().e3conv_jvp(handle, dt, _ptr(x), _ptr(y), _ptr(s), _ptr(dx), _ptr(dy),
+                                     _ptr(ds), _ptr(src), _ptr(row_ptr), _ptr(order), int(num_nodes),
+                                     int(num_edges), _ptr(out), _ptr(out_dot), _stream(stream)))
+    return out, out_dot
 
 
 def e3conv_backward_workspace_size(handle, num_nodes, num_edges):
@@ -209,19 +272,22 @@ def e3conv_backward_workspace_size(handle, num_nodes, num_edges):
 
 def e3conv_backward(handle, x, y, s, src, row_ptr, num_nodes, num_edges, grad_out, grad_x,
                     grad_y, grad_s, workspace=None, order=None, stream=None):
+    return e3conv_backward_masked(handle, x, y, s, src, row_ptr, num_nodes, num_edges, num_nodes,
+                                  grad_out, grad_x, grad_y, grad_s, workspace, order, stream)
+
+
+def e3conv_backward_masked(handle, x, y, s, src, row_ptr, num_nodes, num_edges, num_real_nodes,
+                           grad_out, grad_x, grad_y, grad_s, workspace=None, order=None, stream=None):
     import torch
     for t, n in ((x, "x"), (y, "y"), (s, "s"), (grad_out, "grad_out"), (grad_x, "grad_x"),
                  (grad_y, "grad_y"), (grad_s, "grad_s")):
         _need(t, n, torch.float32)
-    _need(src, "src", torch.int32)
-    _need(row_ptr, "row_ptr", torch.int32)
-    if order is not None:
-        _need(order, "order", torch.int32)
+    _check_graph_args(src, row_ptr, order)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(load_library().e3conv_backward(handle, E3CONV_F32, _ptr(x), _ptr(y), _ptr(s), _ptr(src),
-                                          _ptr(row_ptr), _ptr(order), int(num_nodes), int(num_edges),
-                                          _ptr(grad_out), _ptr(grad_x), _ptr(grad_y), _ptr(grad_s),
-                                          _ptr(workspace), wbytes, _stream(stream)))
+    _check(load_library().e3conv_backward_masked(
+        handle, E3CONV_F32, _ptr(x), _ptr(y), _ptr(s), _ptr(src), _ptr(row_ptr), _ptr(order),
+        int(num_nodes), int(num_edges), int(num_real_nodes), _ptr(grad_out), _ptr(grad_x),
+        _ptr(grad_y), _ptr(grad_s), _ptr(workspace), wbytes, _stream(stream)))
 
 
 def e3conv_csr_from_receivers(receivers, num_nodes, row_ptr=None, stream=None):
@@ -281,8 +347,10 @@ def e3conv_last_error_detail():
 class Plan:
     """Owns a plan handle; shapes, forward and backward on torch tensors."""
 
-    def __init__(self, irreps_in, sh_lmax, irreps_out, avg_num_neighbors=1.0):
-        self.handle = e3conv_plan(irreps_in, sh_lmax, irreps_out, avg_num_neighbors)
+    def __init__(self, irreps_in, sh_lmax, irreps_out, avg_num_neighbors=1.0,
+                 ordering=E3CONV_RECEIVER):
+        self.handle = e3conv_plan_ordered(irreps_in, sh_lmax, irreps_out, avg_num_neighbors, ordering)
+        self.ordering = e3conv_plan_ordering(self.handle)
         (self.channels, self.num_x, self.num_y, self.num_paths,
          self.num_out) = e3conv_plan_shape(self.handle)
         self.avg_num_neighbors = float(avg_num_neighbors)
@@ -320,16 +388,37 @@ class Plan:
             raise ValueError("src must have E entries and row_ptr N+1")
         return N, E
 
-    def forward(self, x, y, s, src, row_ptr, out=None, order=None, stream=None):
+    def forward(self, x, y, s, src, row_ptr, out=None, order=None, stream=None, num_real_nodes=None):
+        """out (N, num_out, C) fp32.  num_real_nodes: nodes from there on are padding."""
         import torch
         N, E = self._check_shapes(x, y, s, src, row_ptr)
         if order is not None and order.numel() != N:
             raise ValueError("order must have N entries")
         if out is None:
             out = torch.empty((N, self.num_out, self.channels), dtype=torch.float32, device=x.device)
-        return e3conv_forward(self.handle, x, y, s, src, row_ptr, N, E, out, order, stream)
+        nr = N if num_real_nodes is None else int(num_real_nodes)
+        return e3conv_forward_masked(self.handle, x, y, s, src, row_ptr, N, E, nr, out, order, stream)
 
-    def backward(self, x, y, s, src, row_ptr, grad_out, stream=None, grads=None, order=None):
+    def jvp(self, x, y, s, dx, dy, ds, src, row_ptr, out=None, out_dot=None, order=None,
+            stream=None, want_out=True):
+        """(out, out_dot): the convolution and its derivative along (dx, dy, ds)."""
+        import torch
+        N, E = self._check_shapes(x, y, s, src, row_ptr)
+        for t, ref, name in ((dx, x, "dx"), (dy, y, "dy"), (ds, s, "ds")):
+            if tuple(t.shape) != tuple(ref.shape):
+                raise ValueError(f"{name} must have shape {tuple(ref.shape)}, got {tuple(t.shape)}")
+        if order is not None and order.numel() != N:
+            raise ValueError("order must have N entries")
+        shape = (N, self.num_out, self.channels)
+        if out_dot is None:
+            out_dot = torch.empty(shape, dtype=torch.float32, device=x.device)
+        if want_out and out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=x.device)
+        return e3conv_jvp(self.handle, x, y, s, dx, dy, ds, src, row_ptr, N, E,
+                          out if want_out else None, out_dot, order, stream)
+
+    def backward(self, x, y, s, src, row_ptr, grad_out, stream=None, grads=None, order=None,
+                 num_real_nodes=None):
         import torch
         N, E = self._check_shapes(x, y, s, src, row_ptr)
         if tuple(grad_out.shape) != (N, self.num_out, self.channels):
@@ -343,8 +432,9 @@ class Plan:
                 raise ValueError(f"{name} must have shape {tuple(ref.shape)}, got {tuple(gt.shape)}")
         if order is not None and order.numel() != N:
             raise ValueError("order must have N entries")
-        e3conv_backward(self.handle, x, y, s, src, row_ptr, N, E, grad_out.contiguous(), gx, gy, gs,
-                        None, order, stream)
+        nr = N if num_real_nodes is None else int(num_real_nodes)
+        e3conv_backward_masked(self.handle, x, y, s, src, row_ptr, N, E, nr, grad_out.contiguous(),
+                               gx, gy, gs, None, order, stream)
         return gx, gy, gs
 
 

@@ -333,3 +333,32 @@ def subgraph16(inp):
     relabel = -np.ones(inp.num_nodes, dtype=np.int64)
     relabel[nodes] = np.arange(len(nodes))
     return nodes, eids, relabel[src[eids]].astype(np.int32), relabel[dst[eids]].astype(np.int32)
+
+
+# ------------------------------------------------ graph-ordering helpers ----
+
+def sender_sorted(senders, receivers):
+    """Permutation that sorts edges by (sender, receiver)."""
+    return np.lexsort((np.asarray(receivers), np.asarray(senders)))
+
+
+def symmetric_normal(senders, receivers, shape_tail, seed):
+    """Per-edge N(0,1) arrays that agree on an edge and its reverse.
+
+    One draw per unordered node pair {a, b}; both directed edges get it (the
+    symmetric edge scalars s_ab = s_ba of the e3j SENDER ordering).
+    """
+    a = np.asarray(senders, dtype=np.int64)
+    b = np.asarray(receivers, dtype=np.int64)
+    lo, hi = np.minimum(a, b), np.maximum(a, b)
+    n = int(max(hi.max(initial=0), 0)) + 1
+    key = lo * n + hi
+    uniq, inv = np.unique(key, return_inverse=True)
+    draw = np.random.default_rng(seed).standard_normal((len(uniq),) + tuple(shape_tail))
+    return draw[inv]
+
+
+def edge_vectors(pos, senders, receivers):
+    """Receiver minus sender position of each edge."""
+    pos = np.asarray(pos, dtype=np.float64)
+    return pos[np.asarray(receivers)] - pos[np.asarray(senders)]

@@ -64,6 +64,18 @@ typedef enum {
 
 typedef enum { E3CONV_F32 = 0, E3CONV_BF16 = 1 } e3conv_dtype;
 
+/* Graph ordering (e3j Convolution page, graph_ordering parameter and its note
+ * on the fused kernels).  RECEIVER: edges grouped by receiver; out[b] sums
+ * the incoming edges of b directly.  SENDER: edges grouped by sender; out[b]
+ * is assembled from the outgoing edges e = (b -> a) of b as
+ * (1/N) sum_e (x[a] (x) P y[e]) (.) s[e], where P negates the odd-l blocks of
+ * y.  Under the page's assumptions for SENDER ordering (every edge (a, b) has
+ * its reverse, y[b->a] = (-1)^l y[a->b] per l block, s[b->a] = s[a->b]) this
+ * equals the RECEIVER result; the library computes the formula above
+ * whether or not they hold, and its reverse pass is the exact derivative of
+ * that formula. */
+typedef enum { E3CONV_RECEIVER = 0, E3CONV_SENDER = 1 } e3conv_ordering;
+
 /* Build a plan (host only, no device call).
  *   irreps_in   x irreps, e.g. "128x0e+128x1o" or "64x(0e+1o+2e)"; every block
  *               must have the same multiplicity C (the channel count);
@@ -79,6 +91,19 @@ typedef enum { E3CONV_F32 = 0, E3CONV_BF16 = 1 } e3conv_dtype;
  * with e3conv_plan_destroy.  Plans are immutable and thread-safe. */
 e3conv_status e3conv_plan(const char* irreps_in, int sh_lmax, const char* irreps_out,
                           float avg_num_neighbors, e3conv_plan_t* plan_out);
+
+/* As e3conv_plan, with the graph ordering chosen explicitly (e3conv_plan is
+ * RECEIVER).  For a SENDER plan every call takes, in place of the receiver
+ * CSR and the senders, the sender CSR (row_ptr: edges of sender b are
+ * row_ptr[b] .. row_ptr[b+1]-1) and src[e] = the receiver of edge e, the node
+ * whose features are gathered; the y, s, grad_y and grad_s rows follow that
+ * edge order.  E3CONV_ERR_INVALID_ARGUMENT for another ordering value. */
+e3conv_status e3conv_plan_ordered(const char* irreps_in, int sh_lmax, const char* irreps_out,
+                                  float avg_num_neighbors, e3conv_ordering ordering,
+                                  e3conv_plan_t* plan_out);
+
+/* The plan's graph ordering. */
+e3conv_status e3conv_plan_ordering(e3conv_plan_t plan, e3conv_ordering* ordering);
 
 void e3conv_plan_destroy(e3conv_plan_t plan);
 
@@ -129,6 +154,34 @@ e3conv_status e3conv_forward(e3conv_plan_t plan, e3conv_dtype in_dtype, const vo
                              const int32_t* row_ptr, const int32_t* order, int64_t num_nodes,
                              int64_t num_edges, float* out, void* hip_stream);
 
+/* Forward with padding nodes (e3j Convolution page, node_mask argument: True
+ * for real nodes, False for padding nodes, which lie at the tail; padding
+ * edges only connect padding nodes).  The mask is given as its count of real
+ * nodes: nodes num_real_nodes .. num_nodes-1 are padding.  Rows of padding
+ * nodes are set to zero and their edges are not read; real rows equal
+ * e3conv_forward's.  0 <= num_real_nodes <= num_nodes, else
+ * E3CONV_ERR_INVALID_ARGUMENT.  Other arguments as e3conv_forward (the
+ * unmasked call is num_real_nodes = num_nodes). */
+e3conv_status e3conv_forward_masked(e3conv_plan_t plan, e3conv_dtype in_dtype, const void* x,
+                                    const void* y, const void* s, const int32_t* src,
+                                    const int32_t* row_ptr, const int32_t* order,
+                                    int64_t num_nodes, int64_t num_edges, int64_t num_real_nodes,
+                                    float* out, void* hip_stream);
+
+/* Forward-mode derivative (Jacobian-vector product; e3nn_mlx page, "JVP and
+ * generated-kernel boundary").  The convolution is trilinear, so along the
+ * tangent (dx, dy, ds)
+ *     out_dot = conv(dx, y, s) + conv(x, dy, s) + conv(x, y, ds),
+ * computed in one pass that also yields out = conv(x, y, s).  dx, dy, ds have
+ * the shapes and in_dtype of x, y, s; out (may be NULL when not wanted) and
+ * out_dot are fp32 (num_nodes, num_out, C), fully overwritten.  Graph
+ * arguments, ordering and rules as e3conv_forward. */
+e3conv_status e3conv_jvp(e3conv_plan_t plan, e3conv_dtype in_dtype, const void* x, const void* y,
+                         const void* s, const void* dx, const void* dy, const void* ds,
+                         const int32_t* src, const int32_t* row_ptr, const int32_t* order,
+                         int64_t num_nodes, int64_t num_edges, float* out, float* out_dot,
+                         void* hip_stream);
+
 /* Bytes of device workspace e3conv_backward needs (currently 0). */
 e3conv_status e3conv_backward_workspace_size(e3conv_plan_t plan, int64_t num_nodes,
                                              int64_t num_edges, size_t* bytes);
@@ -150,9 +203,22 @@ e3conv_status e3conv_backward(e3conv_plan_t plan, e3conv_dtype in_dtype, const v
                               float* grad_s, void* workspace, size_t workspace_bytes,
                               void* hip_stream);
 
+/* Reverse pass of e3conv_forward_masked: as e3conv_backward, except that the
+ * edges of padding receivers (b >= num_real_nodes) get zero grad_y and grad_s
+ * rows and contribute nothing to grad_x. */
+e3conv_status e3conv_backward_masked(e3conv_plan_t plan, e3conv_dtype in_dtype, const void* x,
+                                     const void* y, const void* s, const int32_t* src,
+                                     const int32_t* row_ptr, const int32_t* order,
+                                     int64_t num_nodes, int64_t num_edges, int64_t num_real_nodes,
+                                     const float* grad_out, float* grad_x, float* grad_y,
+                                     float* grad_s, void* workspace, size_t workspace_bytes,
+                                     void* hip_stream);
+
 /* Receiver CSR on the device: row_ptr[b] = first edge whose receiver is >= b,
  * for b = 0..num_nodes, from the receiver of each edge (device int32[num_edges],
- * non-decreasing).  One thread per node, binary search; asynchronous. */
+ * non-decreasing).  One thread per node, binary search; asynchronous.  For a
+ * SENDER plan pass the (non-decreasing) senders instead: the result is the
+ * sender CSR. */
 e3conv_status e3conv_csr_from_receivers(const int32_t* receivers_sorted, int64_t num_edges,
                                         int64_t num_nodes, int32_t* row_ptr, void* hip_stream);
 

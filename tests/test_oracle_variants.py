@@ -1,0 +1,155 @@
+"""Pins for the oracle's SENDER ordering, node_mask padding and JVP (CPU only).
+
+* SENDER ordering (e3j Convolution page, note on graph_ordering): under the
+  page's symmetry assumptions it must reproduce the RECEIVER result; on any
+  directed graph it must equal the RECEIVER convolution of the reversed graph
+  whose edge features are recomputed from the reversed edge vectors (so the
+  parity of the harmonics, not a sign table, decides the flip).
+* node_mask (same page, __call__): padding nodes at the tail, padding edges
+  among padding nodes only; real rows must equal the unpadded graph's rows.
+* JVP (e3nn_mlx page, JVP section): for a trilinear map f and a tangent d,
+  f(p + d) - f(p - d) = 2 J_p d + 2 f(d) exactly, which ties the tangent to
+  three plain forward evaluations.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import conv, variants
+from equivariant_gnn_message_amd import synth
+
+from ._util import rel_max_err
+
+
+def layout_of(idx, C=3):
+    w = synth.WORKLOADS[idx]
+    irin = w.irreps_in.replace(f"{w.channels}x", f"{C}x")
+    irout = w.irreps_out.replace(f"{w.channels}x", f"{C}x")
+    return conv.make_layout(irin, w.lmax, irout, w.avg_num_neighbors)
+
+
+def symmetric_case(idx, seed=0, n=40, side=3.0, r=1.4, C=3):
+    """Radius graph (both directions), geometric y, pair-symmetric s."""
+    lay = layout_of(idx, C)
+    rng = np.random.default_rng(seed)
+    pos = rng.uniform(0.0, side, (n, 3))
+    src, dst = synth.radius_graph(pos, r)
+    vec = synth.edge_vectors(pos, src, dst)
+    y = synth.spherical_harmonics(lay.lmax, vec)
+    s = synth.symmetric_normal(src, dst, (lay.num_paths, C), seed + 1)
+    x = rng.standard_normal((n, lay.num_x, C))
+    g = rng.standard_normal((n, lay.num_out, C))
+    return lay, pos, x, y, s, g, src, dst, n
+
+
+@pytest.mark.parametrize("idx", [0, 2, 3])
+def test_sender_equals_receiver_under_symmetry(idx):
+    lay, pos, x, y, s, g, src, dst, n = symmetric_case(idx)
+    assert len(src) > 50
+    ref = conv.forward(lay, x, y, s, src, dst, n)
+    perm = synth.sender_sorted(src, dst)
+    got = variants.forward_sender(lay, x, y[perm], s[perm], src[perm], dst[perm], n)
+    assert rel_max_err(got, ref) < 1e-12
+
+
+@pytest.mark.parametrize("idx", [0, 3])
+def test_sender_is_receiver_of_reversed_graph(idx):
+    lay = layout_of(idx)
+    rng = np.random.default_rng(7)
+    n, E = 15, 60
+    pos = rng.standard_normal((n, 3))
+    src = rng.integers(0, n, E)
+    dst = (src + rng.integers(1, n, E)) % n          # directed, no reverse guaranteed
+    x = rng.standard_normal((n, lay.num_x, lay.channels))
+    s = rng.standard_normal((E, lay.num_paths, lay.channels))
+    y = synth.spherical_harmonics(lay.lmax, synth.edge_vectors(pos, src, dst))
+    y_back = synth.spherical_harmonics(lay.lmax, synth.edge_vectors(pos, dst, src))
+    ref = conv.forward(lay, x, y_back, s, dst, src, n)
+    got = variants.forward_sender(lay, x, y, s, src, dst, n)
+    assert rel_max_err(got, ref) < 1e-12
+    # and it is not the RECEIVER result of the graph as given
+    plain = conv.forward(lay, x, y, s, src, dst, n)
+    assert rel_max_err(got, plain) > 1e-2
+
+
+def _directional(f, point, direction, h=1.0):
+    """Central difference; exact for polynomials of degree <= 2 in h."""
+    plus = f(*[p + h * d for p, d in zip(point, direction)])
+    minus = f(*[p - h * d for p, d in zip(point, direction)])
+    return (plus - minus) / (2 * h)
+
+
+@pytest.mark.parametrize("idx", [0, 3])
+def test_sender_backward_matches_directional_derivative(idx):
+    lay, pos, x, y, s, g, src, dst, n = symmetric_case(idx, seed=3, n=20, r=1.8)
+    rng = np.random.default_rng(11)
+    dx, dy, ds = (rng.standard_normal(a.shape) for a in (x, y, s))
+    L = lambda a, b, c: np.vdot(g, variants.forward_sender(lay, a, b, c, src, dst, n))
+    # L is trilinear: the central difference leaves the cubic term f(d) (h = 1)
+    cubic = np.vdot(g, variants.forward_sender(lay, dx, dy, ds, src, dst, n))
+    deriv = _directional(L, (x, y, s), (dx, dy, ds)) - cubic
+    gx, gy, gs = variants.backward_sender(lay, x, y, s, g, src, dst, n)
+    pred = np.vdot(gx, dx) + np.vdot(gy, dy) + np.vdot(gs, ds)
+    assert abs(pred - deriv) <= 1e-10 * (abs(deriv) + 1.0)
+
+
+def padded_case(idx, seed=5, n_real=14, n_pad=6, e_real=50, e_pad=20):
+    lay = layout_of(idx)
+    rng = np.random.default_rng(seed)
+    n = n_real + n_pad
+    src = np.concatenate([rng.integers(0, n_real, e_real), rng.integers(n_real, n, e_pad)])
+    dst = np.concatenate([rng.integers(0, n_real, e_real), rng.integers(n_real, n, e_pad)])
+    order = np.argsort(dst, kind="stable")
+    src, dst = src[order], dst[order]
+    E = len(src)
+    x = rng.standard_normal((n, lay.num_x, lay.channels))
+    y = synth.spherical_harmonics(lay.lmax, rng.standard_normal((E, 3)))
+    s = rng.standard_normal((E, lay.num_paths, lay.channels))
+    g = rng.standard_normal((n, lay.num_out, lay.channels))
+    return lay, x, y, s, g, src, dst, n, n_real
+
+
+@pytest.mark.parametrize("idx", [0, 2])
+def test_masked_forward_equals_unpadded_graph(idx):
+    lay, x, y, s, g, src, dst, n, n_real = padded_case(idx)
+    real = dst < n_real
+    ref = conv.forward(lay, x[:n_real], y[real], s[real], src[real], dst[real], n_real)
+    got = variants.forward_masked(lay, x, y, s, src, dst, n, n_real)
+    assert rel_max_err(got[:n_real], ref) < 1e-12
+    assert np.all(got[n_real:] == 0.0)
+    # without padding the mask is the identity
+    full = variants.forward_masked(lay, x, y, s, src, dst, n, n)
+    assert rel_max_err(full, conv.forward(lay, x, y, s, src, dst, n)) < 1e-12
+
+
+@pytest.mark.parametrize("idx", [0, 2])
+def test_masked_backward_equals_unpadded_graph(idx):
+    lay, x, y, s, g, src, dst, n, n_real = padded_case(idx)
+    real = dst < n_real
+    rx, ry, rs = conv.backward(lay, x[:n_real], y[real], s[real], g[:n_real], src[real],
+                               dst[real], n_real)
+    gx, gy, gs = variants.backward_masked(lay, x, y, s, g, src, dst, n, n_real)
+    assert rel_max_err(gx[:n_real], rx) < 1e-12
+    assert np.all(gx[n_real:] == 0.0)
+    assert rel_max_err(gy[real], ry) < 1e-12 and rel_max_err(gs[real], rs) < 1e-12
+    assert np.all(gy[~real] == 0.0) and np.all(gs[~real] == 0.0)
+
+
+@pytest.mark.parametrize("idx", [0, 1, 3])
+def test_jvp_polarization_identity(idx):
+    lay = layout_of(idx)
+    rng = np.random.default_rng(idx + 20)
+    n, E = 12, 45
+    src, dst = rng.integers(0, n, E), rng.integers(0, n, E)
+    x = rng.standard_normal((n, lay.num_x, lay.channels))
+    y = synth.spherical_harmonics(lay.lmax, rng.standard_normal((E, 3)))
+    s = rng.standard_normal((E, lay.num_paths, lay.channels))
+    dx, dy, ds = rng.standard_normal(x.shape), rng.standard_normal(y.shape), rng.standard_normal(s.shape)
+    f = lambda a, b, c: conv.forward(lay, a, b, c, src, dst, n)
+    expect = (f(x + dx, y + dy, s + ds) - f(x - dx, y - dy, s - ds)) / 2 - f(dx, dy, ds)
+    out, out_dot = variants.jvp(lay, x, y, s, dx, dy, ds, src, dst, n)
+    assert rel_max_err(out, f(x, y, s)) == 0.0
+    assert rel_max_err(out_dot, expect) < 1e-12
+    # a tangent along one operand only is that operand's linear map
+    _, only_s = variants.jvp(lay, x, y, s, 0 * dx, 0 * dy, ds, src, dst, n)
+    assert rel_max_err(only_s, f(x, y, ds)) < 1e-12
