@@ -696,9 +696,13 @@ template <class LY>
 __device__ __forceinline__ void zero_edge_grads(const BwdParams& prm, int e0, int end, int step,
                                                 int li, int lpg) {
   constexpr int PC = LY::NP * LY::C, NY = LY::NY;
+  const bool zs = prm.gs && !(prm.flags & kAccumulateS);   // an accumulated zero is a no-op
+  const bool zy = prm.gy && !(prm.flags & kAccumulateY);
   for (int e = e0; e < end; e += step) {
-    for (int k = li; k < PC; k += lpg) __builtin_nontemporal_store(0.0f, prm.gs + (size_t)e * PC + k);
-    for (int k = li; k < NY; k += lpg) prm.gy[(size_t)e * NY + k] = 0.0f;
+    if (zs)
+      for (int k = li; k < PC; k += lpg) __builtin_nontemporal_store(0.0f, prm.gs + (size_t)e * PC + k);
+    if (zy)
+      for (int k = li; k < NY; k += lpg) prm.gy[(size_t)e * NY + k] = 0.0f;
   }
 }
 //
@@ -931,7 +935,9 @@ __device__ __forceinline__ void load_bwd_edge(BwdBuf<LY, CPL>& buf, const float*
     for (int c = 0; c < CPL; ++c) buf.s[p][c] = __builtin_nontemporal_load(srow + p * C + c * LPG);
 }
 
-template <class LY, int CPL, int LPG>
+// GEN: honour optional outputs (nullptr: not computed) and accumulation flags;
+// the default instantiations assume all three outputs, overwritten.
+template <class LY, int CPL, int LPG, bool GEN = false>
 __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float (&gv)[LY::NO][CPL],
                                          const BwdParams& prm, int e, int a, int li) {
   constexpr int C = LY::C, NX = LY::NX, NY = LY::NY, NP = LY::NP;
@@ -945,7 +951,10 @@ __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float
   float dyp[NYP];
 #pragma unroll
   for (int j = 0; j < NYP; ++j) dyp[j] = 0.0f;
-  float* gsrow = prm.gs + (size_t)e * NP * C + li;
+  const bool want_s = !GEN || prm.gs;
+  const bool want_y = !GEN || prm.gy;
+  const bool want_x = !GEN || prm.gx;
+  float* gsrow = want_s ? prm.gs + (size_t)e * NP * C + li : nullptr;
 
   // Per path, with w = K^T g (g already divided by N):
   //   grad_s = sum_m1 x[o1+m1] w[m1]            (= <g, K x>)
@@ -989,10 +998,20 @@ __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float
         for (int c = 0; c < CPL; ++c) ds[c] = 0.0f;
       }
     });
+    if constexpr (GEN) {
+      if (want_s) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) __builtin_nontemporal_store(ds[c], gsrow + p * C + c * LPG);
+        for (int c = 0; c < CPL; ++c) {
+          float* dst = gsrow + p * C + c * LPG;
+          __builtin_nontemporal_store((prm.flags & kAccumulateS) ? ds[c] + *dst : ds[c], dst);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) __builtin_nontemporal_store(ds[c], gsrow + p * C + c * LPG);
+    }
 
-    sfor<0, D1>([&](auto m1c) {
+    if (want_y) sfor<0, D1>([&](auto m1c) {
       constexpr int m1 = decltype(m1c)::value;
       if constexpr (first_m3(LY::T, p, m1) >= 0) {
         float u[CPL];
@@ -1017,11 +1036,14 @@ __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float
     });
   });
 
+  if (want_x) {
 #pragma unroll
-  for (int i = 0; i < NX; ++i)
+    for (int i = 0; i < NX; ++i)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c)
-      unsafeAtomicAdd(prm.gx + ((size_t)a * NX + i) * C + li + c * LPG, dxp[i][c]);
+      for (int c = 0; c < CPL; ++c)
+        unsafeAtomicAdd(prm.gx + ((size_t)a * NX + i) * C + li + c * LPG, dxp[i][c]);
+  }
+  if (!want_y) return;
 
   sfor<0, STEPS>([&](auto kc) {
     constexpr int k = decltype(kc)::value;
@@ -1052,12 +1074,15 @@ __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
       const int comp = base + j;
-      if (comp < NY) prm.gy[(size_t)e * NY + comp] = dyp[j];
+      if (comp < NY) {
+        float* dst = prm.gy + (size_t)e * NY + comp;
+        *dst = (GEN && (prm.flags & kAccumulateY)) ? dyp[j] + *dst : dyp[j];
+      }
     }
   }
 }
 
-template <class LY, int CPL, int GPR>
+template <class LY, int CPL, int GPR, bool GEN = false>
 __global__ void __launch_bounds__(256) conv_bwd_pipe(BwdParams prm) {
   constexpr int C = LY::C, NO = LY::NO;
   constexpr int LPG = C / CPL;
@@ -1107,7 +1132,7 @@ __global__ void __launch_bounds__(256) conv_bwd_pipe(BwdParams prm) {
     if (en < end) load_bwd_edge<LY, CPL, LPG>(b1, x, y, s, en, an, li);
     int en2 = en + GPR;
     int an2 = en2 < end ? src[en2] : 0;
-    bwd_edge<LY, CPL, LPG>(b0, gv, prm, e, a, li);
+    bwd_edge<LY, CPL, LPG, GEN>(b0, gv, prm, e, a, li);
     e = en;
     a = an;
     en = en2;
@@ -1116,7 +1141,7 @@ __global__ void __launch_bounds__(256) conv_bwd_pipe(BwdParams prm) {
     if (en < end) load_bwd_edge<LY, CPL, LPG>(b0, x, y, s, en, an, li);
     en2 = en + GPR;
     an2 = en2 < end ? src[en2] : 0;
-    bwd_edge<LY, CPL, LPG>(b1, gv, prm, e, a, li);
+    bwd_edge<LY, CPL, LPG, GEN>(b1, gv, prm, e, a, li);
     e = en;
     a = an;
     en = en2;
@@ -1168,18 +1193,20 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <class LY, int CPL, int GPR>
+template <class LY, int CPL, int GPR, bool GEN = false>
 hipError_t launch_bwd_pipe(const BwdParams& p, hipStream_t st) {
   constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
   if (p.num_nodes <= 0) return hipSuccess;
-  const size_t nx = (size_t)p.num_nodes * LY::NX * LY::C;
-  const unsigned zb = (unsigned)((nx + 255) / 256 < 8192 ? (nx + 255) / 256 : 8192);
-  hipLaunchKernelGGL(fill_zero, dim3(zb), dim3(256), 0, st, p.gx, nx);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (p.gx && !(p.flags & kAccumulateX)) {
+    const size_t nx = (size_t)p.num_nodes * LY::NX * LY::C;
+    const unsigned zb = (unsigned)((nx + 255) / 256 < 8192 ? (nx + 255) / 256 : 8192);
+    hipLaunchKernelGGL(fill_zero, dim3(zb), dim3(256), 0, st, p.gx, nx);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   const long waves = (p.num_nodes + RPW - 1) / RPW;
   const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
-  hipLaunchKernelGGL((conv_bwd_pipe<LY, CPL, GPR>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((conv_bwd_pipe<LY, CPL, GPR, GEN>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -336,11 +336,14 @@ e3conv_status e3conv_forward_masked(e3conv_plan_t p, e3conv_dtype dt, const void
 e3conv_status e3conv_jvp(e3conv_plan_t p, e3conv_dtype dt, const void* x, const void* y,
                          const void* s, const void* dx, const void* dy, const void* ds,
                          const int32_t* src, const int32_t* row_ptr, const int32_t* order,
-                         int64_t N, int64_t E, float* out, float* out_dot, void* stream) {
+                         int64_t N, int64_t E, int64_t num_real_nodes, float* out, float* out_dot,
+                         void* stream) {
   if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (dt != E3CONV_F32 && dt != E3CONV_BF16) return fail(E3CONV_ERR_INVALID_ARGUMENT, "bad dtype");
   e3conv_status st = check_sizes(N, E, p->channels, p->num_out > p->num_x ? p->num_out : p->num_x);
   if (st != E3CONV_OK) return st;
+  if (num_real_nodes < 0 || num_real_nodes > N)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "num_real_nodes must be in [0, num_nodes]");
   if (N == 0) return ok();
   if (!out_dot || !row_ptr || (E > 0 && (!x || !y || !s || !dx || !dy || !ds || !src)))
     return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
@@ -348,7 +351,7 @@ e3conv_status e3conv_jvp(e3conv_plan_t p, e3conv_dtype dt, const void* x, const 
   const e3c::JvpLauncher L = dt == E3CONV_F32 ? p->kk->jvp_f32 : p->kk->jvp_bf16;
   if (!L) return fail(E3CONV_ERR_UNSUPPORTED, "no compiled forward-mode kernel for this dtype");
   e3c::JvpParams prm{x, y, s, dx, dy, ds, src, row_ptr, order, out, out_dot,
-                     (int)N, (int)E, 1.0f / p->avg, (int)N};
+                     (int)N, (int)E, 1.0f / p->avg, (int)num_real_nodes};
   const hipError_t err = L(prm, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "jvp launch");
   return ok();
@@ -366,16 +369,21 @@ e3conv_status e3conv_backward(e3conv_plan_t p, e3conv_dtype dt, const void* x, c
                               const int32_t* order, int64_t N, int64_t E, const float* g,
                               float* gx, float* gy,
                               float* gs, void* workspace, size_t workspace_bytes, void* stream) {
-  return e3conv_backward_masked(p, dt, x, y, s, src, row_ptr, order, N, E, N, g, gx, gy, gs,
-                                workspace, workspace_bytes, stream);
+  if (!gx && !gy && !gs) {
+    if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+    return ok();
+  }
+  if (!gx || (E > 0 && (!gy || !gs)))
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "grad_x, grad_y and grad_s are all required");
+  return e3conv_backward_ex(p, dt, x, y, s, src, row_ptr, order, N, E, N, g, gx, gy, gs, 0u,
+                            workspace, workspace_bytes, stream);
 }
 
-e3conv_status e3conv_backward_masked(e3conv_plan_t p, e3conv_dtype dt, const void* x, const void* y,
-                                     const void* s, const int32_t* src, const int32_t* row_ptr,
-                                     const int32_t* order, int64_t N, int64_t E,
-                                     int64_t num_real_nodes, const float* g, float* gx, float* gy,
-                                     float* gs, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
+e3conv_status e3conv_backward_ex(e3conv_plan_t p, e3conv_dtype dt, const void* x, const void* y,
+                                 const void* s, const int32_t* src, const int32_t* row_ptr,
+                                 const int32_t* order, int64_t N, int64_t E, int64_t num_real_nodes,
+                                 const float* g, float* gx, float* gy, float* gs, unsigned flags,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
   if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
@@ -384,17 +392,25 @@ e3conv_status e3conv_backward_masked(e3conv_plan_t p, e3conv_dtype dt, const voi
   if (st != E3CONV_OK) return st;
   if (num_real_nodes < 0 || num_real_nodes > N)
     return fail(E3CONV_ERR_INVALID_ARGUMENT, "num_real_nodes must be in [0, num_nodes]");
+  if (flags & ~(unsigned)(E3CONV_ACCUMULATE_GRAD_X | E3CONV_ACCUMULATE_GRAD_Y | E3CONV_ACCUMULATE_GRAD_S))
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "unknown flag bits");
   if (!gx && !gy && !gs) return ok();
   if (N == 0) return ok();
-  if (!gx || !g || !row_ptr || (E > 0 && (!x || !y || !s || !src || !gy || !gs)))
+  if (!g || !row_ptr || (E > 0 && (!x || !y || !s || !src)))
     return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
   if (!p->kk || p->kk->n_bwd_f32 == 0)
     return fail(E3CONV_ERR_UNSUPPORTED, "no compiled reverse kernel for this layout");
-  const int v = p->bwd_variant < p->kk->n_bwd_f32 ? p->bwd_variant : 0;
   e3c::BwdParams prm{static_cast<const float*>(x), static_cast<const float*>(y),
                      static_cast<const float*>(s), src, row_ptr, order, g, gx, gy, gs, (int)N, (int)E,
-                     1.0f / p->avg, (int)num_real_nodes};
-  const hipError_t err = p->kk->bwd_f32[v](prm, static_cast<hipStream_t>(stream));
+                     1.0f / p->avg, (int)num_real_nodes, (int)flags};
+  e3c::BwdLauncher L;
+  if (flags == 0 && gx && gy && gs) {
+    L = p->kk->bwd_f32[p->bwd_variant < p->kk->n_bwd_f32 ? p->bwd_variant : 0];
+  } else {
+    L = p->kk->bwd_f32_general;
+    if (!L) return fail(E3CONV_ERR_UNSUPPORTED, "no general reverse kernel for this layout");
+  }
+  const hipError_t err = L(prm, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "backward launch");
   return ok();
 }

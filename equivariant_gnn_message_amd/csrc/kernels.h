@@ -38,7 +38,12 @@ struct BwdParams {
   int num_edges;
   float inv_avg;
   int num_real;         // edges into receivers b >= num_real get zero grad_y / grad_s
+  int flags;            // kAccumulate*: add into the output instead of overwriting it
 };
+
+// BwdParams::flags.  Only the general reverse launchers honour them and
+// nullptr outputs (an output that is not computed).
+constexpr int kAccumulateX = 1, kAccumulateY = 2, kAccumulateS = 4;
 
 struct JvpParams {
   const void* x;        // primal operands, as in FwdParams
@@ -73,6 +78,7 @@ struct OrderingKernels {
   int n_fwd_bf16;
   const BwdLauncher* bwd_f32;
   int n_bwd_f32;
+  BwdLauncher bwd_f32_general;  // optional outputs and accumulation
   JvpLauncher jvp_f32;
   JvpLauncher jvp_bf16;
 };

@@ -20,6 +20,9 @@ E3CONV_F32 = 0
 E3CONV_BF16 = 1
 E3CONV_RECEIVER = 0
 E3CONV_SENDER = 1
+E3CONV_ACCUMULATE_GRAD_X = 1
+E3CONV_ACCUMULATE_GRAD_Y = 2
+E3CONV_ACCUMULATE_GRAD_S = 4
 
 STATUS_NAMES = {
     0: "E3CONV_OK", 1: "E3CONV_ERR_INVALID_ARGUMENT", 2: "E3CONV_ERR_PARSE",
@@ -32,7 +35,7 @@ EXPORTED = [
     "e3conv_plan", "e3conv_plan_ordered", "e3conv_plan_ordering", "e3conv_plan_destroy",
     "e3conv_plan_shape", "e3conv_plan_paths",
     "e3conv_plan_coefficients", "e3conv_plan_supported", "e3conv_forward", "e3conv_forward_masked",
-    "e3conv_jvp", "e3conv_backward_workspace_size", "e3conv_backward", "e3conv_backward_masked",
+    "e3conv_jvp", "e3conv_backward_workspace_size", "e3conv_backward", "e3conv_backward_ex",
     "e3conv_csr_from_receivers",
     "e3conv_validate_graph", "e3conv_receiver_order", "e3conv_stream_reference",
     "e3conv_plan_set_variant",
@@ -79,13 +82,14 @@ def load_library(path=LIB_PATH):
         "e3conv_forward": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, P, P], ctypes.c_int),
         "e3conv_forward_masked": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P, P],
                                   ctypes.c_int),
-        "e3conv_jvp": ([P, ctypes.c_int, P, P, P, P, P, P, P, P, P, I64, I64, P, P, P], ctypes.c_int),
+        "e3conv_jvp": ([P, ctypes.c_int, P, P, P, P, P, P, P, P, P, I64, I64, I64, P, P, P],
+                       ctypes.c_int),
         "e3conv_backward_workspace_size": ([P, I64, I64, ctypes.POINTER(ctypes.c_size_t)],
                                            ctypes.c_int),
         "e3conv_backward": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, P, P, P, P, P,
                              ctypes.c_size_t, P], ctypes.c_int),
-        "e3conv_backward_masked": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P, P, P, P, P,
-                                    ctypes.c_size_t, P], ctypes.c_int),
+        "e3conv_backward_ex": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P, P, P, P,
+                                ctypes.c_uint, P, ctypes.c_size_t, P], ctypes.c_int),
         "e3conv_receiver_order": ([P, P, I64, I64, ctypes.c_int, P], ctypes.c_int),
         "e3conv_stream_reference": ([P, P, ctypes.c_size_t, P], ctypes.c_int),
         "e3conv_csr_from_receivers": ([P, I64, I64, P, P], ctypes.c_int),
@@ -248,7 +252,7 @@ def e3conv_forward_masked(handle, x, y, s, src, row_ptr, num_nodes, num_edges, n
 
 
 def e3conv_jvp(handle, x, y, s, dx, dy, ds, src, row_ptr, num_nodes, num_edges, out, out_dot,
-               order=None, stream=None):
+               order=None, stream=None, num_real_nodes=None):
     import torch
     dt = _dtype_code(x)
     for t, n in ((x, "x"), (y, "y"), (s, "s"), (dx, "dx"), (dy, "dy"), (ds, "ds")):
@@ -259,7 +263,9 @@ def e3conv_jvp(handle, x, y, s, dx, dy, ds, src, row_ptr, num_nodes, num_edges, 
         _need(out, "out", torch.float32)
     _check(load_library().e3conv_jvp(handle, dt, _ptr(x), _ptr(y), _ptr(s), _ptr(dx), _ptr(dy),
                                      _ptr(ds), _ptr(src), _ptr(row_ptr), _ptr(order), int(num_nodes),
-                                     int(num_edges), _ptr(out), _ptr(out_dot), _stream(stream)))
+                                     int(num_edges),
+                                     int(num_nodes if num_real_nodes is None else num_real_nodes),
+                                     _ptr(out), _ptr(out_dot), _stream(stream)))
     return out, out_dot
 
 
@@ -272,22 +278,34 @@ def e3conv_backward_workspace_size(handle, num_nodes, num_edges):
 
 def e3conv_backward(handle, x, y, s, src, row_ptr, num_nodes, num_edges, grad_out, grad_x,
                     grad_y, grad_s, workspace=None, order=None, stream=None):
-    return e3conv_backward_masked(handle, x, y, s, src, row_ptr, num_nodes, num_edges, num_nodes,
-                                  grad_out, grad_x, grad_y, grad_s, workspace, order, stream)
-
-
-def e3conv_backward_masked(handle, x, y, s, src, row_ptr, num_nodes, num_edges, num_real_nodes,
-                           grad_out, grad_x, grad_y, grad_s, workspace=None, order=None, stream=None):
     import torch
     for t, n in ((x, "x"), (y, "y"), (s, "s"), (grad_out, "grad_out"), (grad_x, "grad_x"),
                  (grad_y, "grad_y"), (grad_s, "grad_s")):
         _need(t, n, torch.float32)
     _check_graph_args(src, row_ptr, order)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(load_library().e3conv_backward_masked(
+    _check(load_library().e3conv_backward(handle, E3CONV_F32, _ptr(x), _ptr(y), _ptr(s), _ptr(src),
+                                          _ptr(row_ptr), _ptr(order), int(num_nodes), int(num_edges),
+                                          _ptr(grad_out), _ptr(grad_x), _ptr(grad_y), _ptr(grad_s),
+                                          _ptr(workspace), wbytes, _stream(stream)))
+
+
+def e3conv_backward_ex(handle, x, y, s, src, row_ptr, num_nodes, num_edges, num_real_nodes,
+                       grad_out, grad_x, grad_y, grad_s, flags=0, workspace=None, order=None,
+                       stream=None):
+    """General reverse pass: grad_x / grad_y / grad_s may be None (not computed)."""
+    import torch
+    for t, n in ((x, "x"), (y, "y"), (s, "s"), (grad_out, "grad_out")):
+        _need(t, n, torch.float32)
+    for t, n in ((grad_x, "grad_x"), (grad_y, "grad_y"), (grad_s, "grad_s")):
+        if t is not None:
+            _need(t, n, torch.float32)
+    _check_graph_args(src, row_ptr, order)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().e3conv_backward_ex(
         handle, E3CONV_F32, _ptr(x), _ptr(y), _ptr(s), _ptr(src), _ptr(row_ptr), _ptr(order),
         int(num_nodes), int(num_edges), int(num_real_nodes), _ptr(grad_out), _ptr(grad_x),
-        _ptr(grad_y), _ptr(grad_s), _ptr(workspace), wbytes, _stream(stream)))
+        _ptr(grad_y), _ptr(grad_s), int(flags), _ptr(workspace), wbytes, _stream(stream)))
 
 
 def e3conv_csr_from_receivers(receivers, num_nodes, row_ptr=None, stream=None):
@@ -400,7 +418,7 @@ class Plan:
         return e3conv_forward_masked(self.handle, x, y, s, src, row_ptr, N, E, nr, out, order, stream)
 
     def jvp(self, x, y, s, dx, dy, ds, src, row_ptr, out=None, out_dot=None, order=None,
-            stream=None, want_out=True):
+            stream=None, want_out=True, num_real_nodes=None):
         """(out, out_dot): the convolution and its derivative along (dx, dy, ds)."""
         import torch
         N, E = self._check_shapes(x, y, s, src, row_ptr)
@@ -415,10 +433,16 @@ class Plan:
         if want_out and out is None:
             out = torch.empty(shape, dtype=torch.float32, device=x.device)
         return e3conv_jvp(self.handle, x, y, s, dx, dy, ds, src, row_ptr, N, E,
-                          out if want_out else None, out_dot, order, stream)
+                          out if want_out else None, out_dot, order, stream, num_real_nodes)
 
     def backward(self, x, y, s, src, row_ptr, grad_out, stream=None, grads=None, order=None,
-                 num_real_nodes=None):
+                 num_real_nodes=None, accumulate=(False, False, False)):
+        """(grad_x, grad_y, grad_s) of <grad_out, out>.
+
+        grads: output arrays; an entry may be None in a given tuple to skip that
+        gradient (returned as None).  accumulate[i]: add into grads[i] instead
+        of overwriting it.
+        """
         import torch
         N, E = self._check_shapes(x, y, s, src, row_ptr)
         if tuple(grad_out.shape) != (N, self.num_out, self.channels):
@@ -428,33 +452,74 @@ class Plan:
                      torch.empty_like(s, dtype=torch.float32))
         gx, gy, gs = grads
         for gt, ref, name in ((gx, x, "grad_x"), (gy, y, "grad_y"), (gs, s, "grad_s")):
-            if tuple(gt.shape) != tuple(ref.shape):
+            if gt is not None and tuple(gt.shape) != tuple(ref.shape):
                 raise ValueError(f"{name} must have shape {tuple(ref.shape)}, got {tuple(gt.shape)}")
         if order is not None and order.numel() != N:
             raise ValueError("order must have N entries")
         nr = N if num_real_nodes is None else int(num_real_nodes)
-        e3conv_backward_masked(self.handle, x, y, s, src, row_ptr, N, E, nr, grad_out.contiguous(),
-                               gx, gy, gs, None, order, stream)
+        flags = sum(bit for bit, on in zip((E3CONV_ACCUMULATE_GRAD_X, E3CONV_ACCUMULATE_GRAD_Y,
+                                            E3CONV_ACCUMULATE_GRAD_S), accumulate) if on)
+        e3conv_backward_ex(self.handle, x, y, s, src, row_ptr, N, E, nr, grad_out.contiguous(),
+                           gx, gy, gs, flags, None, order, stream)
         return gx, gy, gs
 
 
 def _autograd_function():
     import torch
 
-    class E3ConvFunction(torch.autograd.Function):
-        """out = conv(x, y, s) on a fixed graph; gradients for x, y and s (fp32)."""
+    class _ConvBackward(torch.autograd.Function):
+        """(gx, gy, gs) = reverse pass at (x, y, s) for cotangent g; itself differentiable.
+
+        L2 = <Gx, gx> + <Gy, gy> + <Gs, gs> is <g, D conv(x, y, s)[Gx, Gy, Gs]>, so
+          dL2/dg = jvp of conv along (Gx, Gy, Gs),
+          dL2/dx = reverse(x, Gy, s).gx + reverse(x, y, Gs).gx,
+          dL2/dy = reverse(Gx, y, s).gy + reverse(x, y, Gs).gy,
+          dL2/ds = reverse(Gx, y, s).gs + reverse(x, Gy, s).gs,
+        each sum accumulated in place by the library's reverse kernel.
+        """
 
         @staticmethod
-        def forward(ctx, plan, x, y, s, src, row_ptr):
+        def forward(ctx, plan, graph, x, y, s, g):
+            src, row_ptr, order, num_real = graph
+            ctx.plan, ctx.graph = plan, graph
+            ctx.save_for_backward(x, y, s, g)
+            return plan.backward(x, y, s, src, row_ptr, g, order=order, num_real_nodes=num_real)
+
+        @staticmethod
+        def backward(ctx, Gx, Gy, Gs):
+            x, y, s, g = ctx.saved_tensors
+            plan = ctx.plan
+            src, row_ptr, order, num_real = ctx.graph
+            Gx, Gy, Gs = (t.contiguous() for t in (Gx, Gy, Gs))
+            dx, dy, ds = torch.empty_like(x), torch.empty_like(y), torch.empty_like(s)
+            common = dict(order=order, num_real_nodes=num_real)
+            plan.backward(Gx, y, s, src, row_ptr, g, grads=(None, dy, ds), **common)
+            plan.backward(x, Gy, s, src, row_ptr, g, grads=(dx, None, ds),
+                          accumulate=(False, False, True), **common)
+            plan.backward(x, y, Gs, src, row_ptr, g, grads=(dx, dy, None),
+                          accumulate=(True, True, False), **common)
+            _, dg = plan.jvp(x, y, s, Gx, Gy, Gs, src, row_ptr, order=order, want_out=False,
+                             num_real_nodes=num_real)
+            return None, None, dx, dy, ds, dg
+
+    class E3ConvFunction(torch.autograd.Function):
+        """out = conv(x, y, s) on a fixed graph; first and second derivatives (fp32).
+
+        apply(plan, x, y, s, src, row_ptr, order=None, num_real_nodes=None).
+        """
+
+        @staticmethod
+        def forward(ctx, plan, x, y, s, src, row_ptr, order=None, num_real_nodes=None):
             ctx.plan = plan
-            ctx.save_for_backward(x, y, s, src, row_ptr)
-            return plan.forward(x, y, s, src, row_ptr)
+            ctx.graph = (src, row_ptr, order, num_real_nodes)
+            ctx.save_for_backward(x, y, s)
+            return plan.forward(x, y, s, src, row_ptr, order=order, num_real_nodes=num_real_nodes)
 
         @staticmethod
         def backward(ctx, grad_out):
-            x, y, s, src, row_ptr = ctx.saved_tensors
-            gx, gy, gs = ctx.plan.backward(x, y, s, src, row_ptr, grad_out)
-            return None, gx, gy, gs, None, None
+            x, y, s = ctx.saved_tensors
+            gx, gy, gs = _ConvBackward.apply(ctx.plan, ctx.graph, x, y, s, grad_out.contiguous())
+            return None, gx, gy, gs, None, None, None, None
 
     return E3ConvFunction
 

@@ -175,12 +175,13 @@ e3conv_status e3conv_forward_masked(e3conv_plan_t plan, e3conv_dtype in_dtype, c
  * computed in one pass that also yields out = conv(x, y, s).  dx, dy, ds have
  * the shapes and in_dtype of x, y, s; out (may be NULL when not wanted) and
  * out_dot are fp32 (num_nodes, num_out, C), fully overwritten.  Graph
- * arguments, ordering and rules as e3conv_forward. */
+ * arguments, ordering, node-mask count and rules as e3conv_forward_masked
+ * (num_real_nodes = num_nodes for no padding). */
 e3conv_status e3conv_jvp(e3conv_plan_t plan, e3conv_dtype in_dtype, const void* x, const void* y,
                          const void* s, const void* dx, const void* dy, const void* ds,
                          const int32_t* src, const int32_t* row_ptr, const int32_t* order,
-                         int64_t num_nodes, int64_t num_edges, float* out, float* out_dot,
-                         void* hip_stream);
+                         int64_t num_nodes, int64_t num_edges, int64_t num_real_nodes, float* out,
+                         float* out_dot, void* hip_stream);
 
 /* Bytes of device workspace e3conv_backward needs (currently 0). */
 e3conv_status e3conv_backward_workspace_size(e3conv_plan_t plan, int64_t num_nodes,
@@ -203,16 +204,30 @@ e3conv_status e3conv_backward(e3conv_plan_t plan, e3conv_dtype in_dtype, const v
                               float* grad_s, void* workspace, size_t workspace_bytes,
                               void* hip_stream);
 
-/* Reverse pass of e3conv_forward_masked: as e3conv_backward, except that the
- * edges of padding receivers (b >= num_real_nodes) get zero grad_y and grad_s
- * rows and contribute nothing to grad_x. */
-e3conv_status e3conv_backward_masked(e3conv_plan_t plan, e3conv_dtype in_dtype, const void* x,
-                                     const void* y, const void* s, const int32_t* src,
-                                     const int32_t* row_ptr, const int32_t* order,
-                                     int64_t num_nodes, int64_t num_edges, int64_t num_real_nodes,
-                                     const float* grad_out, float* grad_x, float* grad_y,
-                                     float* grad_s, void* workspace, size_t workspace_bytes,
-                                     void* hip_stream);
+/* Flags of e3conv_backward_ex: add the gradient into the caller's array
+ * instead of overwriting it. */
+#define E3CONV_ACCUMULATE_GRAD_X 1u
+#define E3CONV_ACCUMULATE_GRAD_Y 2u
+#define E3CONV_ACCUMULATE_GRAD_S 4u
+
+/* General reverse pass: e3conv_backward with node-mask padding (edges of
+ * receivers b >= num_real_nodes contribute nothing: zero grad_y and grad_s
+ * rows, nothing added to grad_x; the derivative of e3conv_forward_masked),
+ * optional outputs (any of grad_x, grad_y, grad_s may be NULL: not
+ * computed; all NULL is a no-op) and accumulation (flags: a set
+ * E3CONV_ACCUMULATE_GRAD_* bit adds into that array, which must then hold
+ * valid data; otherwise it is overwritten).  Unknown flag bits are
+ * E3CONV_ERR_INVALID_ARGUMENT.  These are the building blocks of second
+ * derivatives (reverse over reverse), where the gradient of <G, grad> with
+ * respect to each operand sums reverse passes with one operand replaced by a
+ * cotangent.  With flags = 0 and all three outputs it runs the same kernels as
+ * e3conv_backward. */
+e3conv_status e3conv_backward_ex(e3conv_plan_t plan, e3conv_dtype in_dtype, const void* x,
+                                 const void* y, const void* s, const int32_t* src,
+                                 const int32_t* row_ptr, const int32_t* order, int64_t num_nodes,
+                                 int64_t num_edges, int64_t num_real_nodes, const float* grad_out,
+                                 float* grad_x, float* grad_y, float* grad_s, unsigned flags,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Receiver CSR on the device: row_ptr[b] = first edge whose receiver is >= b,
  * for b = 0..num_nodes, from the receiver of each edge (device int32[num_edges],

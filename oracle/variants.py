@@ -15,9 +15,9 @@ Built from ``oracle.conv`` without new arithmetic of its own:
   padding nodes.  Read plainly: the messages of edges into padding receivers
   are dropped and the rows of padding nodes are zero; the reverse pass is the
   derivative of that function.
-* forward-mode derivative (e3nn_mlx page, "JVP and generated-kernel
-  boundary"): the convolution is trilinear in (x, y, s), so by the product
-  rule its derivative along (dx, dy, ds) is
+* forward-mode derivative and second derivatives (e3nn_mlx page, "JVP and
+  generated-kernel boundary"): the convolution is trilinear in (x, y, s), so
+  by the product rule its derivative along (dx, dy, ds) is
   conv(dx, y, s) + conv(x, dy, s) + conv(x, y, ds).
 """
 
@@ -79,3 +79,20 @@ def jvp(lay, x, y, s, dx, dy, ds, senders, receivers, num_nodes):
     out = f(x, y, s)
     out_dot = f(dx, y, s) + f(x, dy, s) + f(x, y, ds)
     return out, out_dot
+
+
+def double_backward(lay, x, y, s, g, Gx, Gy, Gs, senders, receivers, num_nodes):
+    """Second derivatives (reverse over reverse; e3nn_mlx page, JVP section).
+
+    With (gx, gy, gs) the gradients of <g, conv(x, y, s)>, returns the
+    gradients of L2 = <Gx, gx> + <Gy, gy> + <Gs, gs> with respect to
+    (x, y, s, g).  L2 = <g, D conv(x, y, s)[Gx, Gy, Gs]>, so by the product
+    rule dL2/dg is the JVP along (Gx, Gy, Gs) and each operand's gradient sums
+    the reverse passes in which another operand is replaced by its cotangent.
+    """
+    bw = lambda a, b, c: conv.backward(lay, a, b, c, g, senders, receivers, num_nodes)
+    _, dy_a, ds_a = bw(Gx, y, s)
+    dx_b, _, ds_b = bw(x, Gy, s)
+    dx_c, dy_c, _ = bw(x, y, Gs)
+    _, dg = jvp(lay, x, y, s, Gx, Gy, Gs, senders, receivers, num_nodes)
+    return dx_b + dx_c, dy_a + dy_c, ds_a + ds_b, dg

@@ -198,3 +198,57 @@ def test_jvp_parity(idx, n, ordering):
             rel_err(only_dot.cpu().numpy(), ref_dot)]
     say(f"  max|err|/RMS out {errs[0]:.3e} out_dot {errs[1]:.3e} (tangent only {errs[2]:.3e})")
     assert max(errs) <= tolerance(inp)
+
+
+def test_backward_ex_optional_outputs_and_accumulation():
+    import torch
+    inp = synth.make_inputs(4, num_nodes=301, with_cotangent=True)
+    lay = lay_of(inp)
+    say(f"[reverse, general] N={inp.num_nodes} E={inp.num_edges}")
+    rx, ry, rs = conv.backward(lay, inp.x, inp.y, inp.s, inp.g, inp.senders, inp.receivers,
+                               inp.num_nodes)
+    w = inp.workload
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    x, y, s, g = dev(inp.x), dev(inp.y), dev(inp.s), dev(inp.g)
+    src = dev(inp.senders.astype(np.int32))
+    row_ptr = E.e3conv_csr_from_receivers(dev(inp.receivers.astype(np.int32)), inp.num_nodes)
+    gy, gs = torch.empty_like(y), torch.empty_like(s)
+    plan.backward(x, y, s, src, row_ptr, g, grads=(None, gy, gs))
+    gx = torch.empty_like(x)
+    plan.backward(x, y, s, src, row_ptr, g, grads=(gx, None, None))
+    rng = np.random.default_rng(4)
+    pre = [rng.standard_normal(a.shape).astype(np.float32) for a in (rx, ry, rs)]
+    acc = tuple(dev(a) for a in pre)
+    plan.backward(x, y, s, src, row_ptr, g, grads=acc, accumulate=(True, True, True))
+    torch.cuda.synchronize()
+    errs = [rel_err(gx.cpu().numpy(), rx), rel_err(gy.cpu().numpy(), ry), rel_err(gs.cpu().numpy(), rs)]
+    errs += [rel_err(a.cpu().numpy() - p, r) for a, p, r in zip(acc, pre, (rx, ry, rs))]
+    say("  max|err|/RMS " + " ".join(f"{e:.3e}" for e in errs))
+    assert max(errs) <= 1e-5
+
+
+@pytest.mark.parametrize("idx,n", [(0, None), (4, 201)], ids=["w0", "w4-n201"])
+def test_second_derivatives(idx, n):
+    """Reverse over reverse through E3ConvFunction against the oracle."""
+    import torch
+    inp = synth.make_inputs(idx, num_nodes=n, with_cotangent=True) if n else \
+        synth.make_inputs(idx, with_cotangent=True)
+    lay = lay_of(inp)
+    N = inp.num_nodes
+    rng = np.random.default_rng(idx + 70)
+    G = [rng.standard_normal(a.shape).astype(np.float32) for a in (inp.x, inp.y, inp.s)]
+    say(f"[second derivatives] workload {idx} N={N} E={inp.num_edges}")
+    ref = variants.double_backward(lay, inp.x, inp.y, inp.s, inp.g, *G, inp.senders,
+                                   inp.receivers, N)
+    w = inp.workload
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    x, y, s, g = (dev(a).requires_grad_(True) for a in (inp.x, inp.y, inp.s, inp.g))
+    src = dev(inp.senders.astype(np.int32))
+    row_ptr = E.e3conv_csr_from_receivers(dev(inp.receivers.astype(np.int32)), N)
+    out = E.E3ConvFunction.apply(plan, x, y, s, src, row_ptr)
+    first = torch.autograd.grad(out, (x, y, s), g, create_graph=True)
+    second = torch.autograd.grad(first, (x, y, s, g), tuple(dev(a) for a in G))
+    torch.cuda.synchronize()
+    errs = [rel_err(a.detach().cpu().numpy(), b) for a, b in zip(second, ref)]
+    say("  max|err|/RMS dx {:.3e} dy {:.3e} ds {:.3e} dg {:.3e}".format(*errs))
+    assert max(errs) <= 1e-5

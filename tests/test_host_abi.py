@@ -164,6 +164,20 @@ def test_forward_backward_argument_errors(lib):
     assert lib.e3conv_backward(h, 1, f, f, f, f, f, None, 4, 4, f, f, f, f, n, 0, None) == 3   # bf16 reverse
     assert lib.e3conv_backward(h, 0, f, f, f, f, f, None, 4, 4, f, n, f, f, n, 0, None) == 1   # partial outputs
     assert lib.e3conv_backward(h, 0, f, f, f, f, f, None, 4, 4, f, n, n, n, n, 0, None) == 0   # nothing to do
+    # general reverse pass: unknown flag bits, mask count out of range, bf16, nothing to do
+    assert lib.e3conv_backward_ex(h, 0, f, f, f, f, f, None, 4, 4, 4, f, f, f, f, 8, n, 0, None) == 1
+    assert lib.e3conv_backward_ex(h, 0, f, f, f, f, f, None, 4, 4, 5, f, f, f, f, 0, n, 0, None) == 1
+    assert lib.e3conv_backward_ex(h, 0, f, f, f, f, f, None, 4, 4, -1, f, f, f, f, 0, n, 0, None) == 1
+    assert lib.e3conv_backward_ex(h, 1, f, f, f, f, f, None, 4, 4, 4, f, f, f, f, 0, n, 0, None) == 3
+    assert lib.e3conv_backward_ex(h, 0, f, f, f, f, f, None, 4, 4, 4, f, n, n, n, 7, n, 0, None) == 0
+    assert lib.e3conv_backward_ex(h, 0, f, f, f, f, n, None, 4, 4, 4, f, n, f, n, 0, n, 0, None) == 1
+    # masked forward and forward-mode: count out of range, null tangent, bad dtype
+    assert lib.e3conv_forward_masked(h, 0, f, f, f, f, f, None, 4, 4, 5, f, None) == 1
+    assert lib.e3conv_forward_masked(h, 0, f, f, f, f, f, None, 4, 4, -1, f, None) == 1
+    assert lib.e3conv_jvp(h, 0, f, f, f, f, n, f, f, f, None, 4, 4, 4, f, f, None) == 1
+    assert lib.e3conv_jvp(h, 0, f, f, f, f, f, f, f, f, None, 4, 4, 4, f, n, None) == 1
+    assert lib.e3conv_jvp(h, 2, f, f, f, f, f, f, f, f, None, 4, 4, 4, f, f, None) == 1
+    assert lib.e3conv_jvp(h, 0, f, f, f, f, f, f, f, f, None, 4, 4, 9, f, f, None) == 1
     sz = ctypes.c_size_t(123)
     assert lib.e3conv_backward_workspace_size(h, 10, 10, ctypes.byref(sz)) == 0 and sz.value == 0
     assert lib.e3conv_csr_from_receivers(f, -1, 4, f, None) == 1
@@ -229,3 +243,21 @@ def test_receiver_order_clusters_are_connected():
     for v in first[1:]:
         nbrs = inp.senders[row_ptr[v]:row_ptr[v + 1]]
         assert np.any(pos[nbrs] < pos[v])    # the radius graph is symmetric
+
+
+def test_ordered_plans(lib):
+    w = synth.WORKLOADS[2]
+    h = ctypes.c_void_p()
+    args = (w.irreps_in.encode(), w.lmax, w.irreps_out.encode(), w.avg_num_neighbors)
+    assert lib.e3conv_plan_ordered(*args, 2, ctypes.byref(h)) == 1          # unknown ordering
+    assert lib.e3conv_plan_ordered(*args, -1, ctypes.byref(h)) == 1
+    for ordering in (E.E3CONV_RECEIVER, E.E3CONV_SENDER):
+        p = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors, ordering=ordering)
+        assert p.ordering == ordering
+        assert p.supported() == (True, True, True)
+        nf, nb = p.num_variants(E.E3CONV_F32)
+        assert nf >= 1 and nb >= 1
+    plain = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    assert plain.ordering == E.E3CONV_RECEIVER
+    v = ctypes.c_int(5)
+    assert lib.e3conv_plan_ordering(None, ctypes.byref(v)) == 1

@@ -10,6 +10,9 @@
 * JVP (e3nn_mlx page, JVP section): for a trilinear map f and a tangent d,
   f(p + d) - f(p - d) = 2 J_p d + 2 f(d) exactly, which ties the tangent to
   three plain forward evaluations.
+* second derivatives (same section, reverse over reverse): the same identity
+  for the homogeneous cubic <G, grad(x, y, s, g)> ties them to the plain
+  reverse pass.
 """
 
 import numpy as np
@@ -153,3 +156,37 @@ def test_jvp_polarization_identity(idx):
     # a tangent along one operand only is that operand's linear map
     _, only_s = variants.jvp(lay, x, y, s, 0 * dx, 0 * dy, ds, src, dst, n)
     assert rel_max_err(only_s, f(x, y, ds)) < 1e-12
+
+
+@pytest.mark.parametrize("idx", [0, 2])
+def test_double_backward_central_difference_identity(idx):
+    """L2(p) = <G, grad(p)> is homogeneous cubic in p = (x, y, s, g), so
+    [L2(p + d) - L2(p - d)] / 2 = <dL2/dp, d> + L2(d) exactly."""
+    lay = layout_of(idx)
+    rng = np.random.default_rng(idx + 60)
+    n, E = 10, 35
+    src, dst = rng.integers(0, n, E), rng.integers(0, n, E)
+    shapes = [(n, lay.num_x, lay.channels), (E, lay.num_y), (E, lay.num_paths, lay.channels),
+              (n, lay.num_out, lay.channels)]
+    p = [rng.standard_normal(sh) for sh in shapes]
+    d = [rng.standard_normal(sh) for sh in shapes]
+    G = [rng.standard_normal(sh) for sh in shapes[:3]]
+
+    def L2(x, y, s, g):
+        grads = conv.backward(lay, x, y, s, g, src, dst, n)
+        return sum(np.vdot(a, b) for a, b in zip(G, grads))
+
+    plus = L2(*[a + b for a, b in zip(p, d)])
+    minus = L2(*[a - b for a, b in zip(p, d)])
+    deriv = (plus - minus) / 2 - L2(*d)
+    dx, dy, ds, dg = variants.double_backward(lay, *p, *G, src, dst, n)
+    pred = sum(np.vdot(a, b) for a, b in zip((dx, dy, ds, dg), d))
+    assert abs(pred - deriv) <= 1e-10 * (abs(deriv) + 1.0)
+    # each component separately (direction along one operand only)
+    for k in range(4):
+        dk = [np.zeros_like(a) for a in d]
+        dk[k] = d[k]
+        plus = L2(*[a + b for a, b in zip(p, dk)])
+        minus = L2(*[a - b for a, b in zip(p, dk)])
+        comp = (dx, dy, ds, dg)[k]
+        assert abs(np.vdot(comp, d[k]) - (plus - minus) / 2) <= 1e-10 * (abs(plus) + abs(minus) + 1.0)
