@@ -46,6 +46,10 @@ def parse():
                     help="time every compiled kernel variant (one JSON line each) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--mode", default="conv", choices=("conv", "sender", "jvp", "second"),
+                    help="conv: the hot path (default); sender: SENDER graph ordering; "
+                         "jvp: fused forward-mode pass; second: second derivatives of the "
+                         "training step (one line each)")
     return ap.parse_args()
 
 
@@ -196,6 +200,10 @@ def main():
     from equivariant_gnn_message_amd import e3conv as E
     from equivariant_gnn_message_amd import synth
 
+    if args.mode != "conv":
+        bench_mode(args)
+        return
+
     w = synth.WORKLOADS[args.workload]
     t0 = time.perf_counter()
     inp = synth.make_inputs(args.workload)
@@ -328,6 +336,161 @@ def main():
         res["cpu_baseline"] = None
     res["input_gen_s"] = t_gen
     print(json.dumps(res), flush=True)
+
+
+def _timed(fn, steps, warmup):
+    """Mean HIP-event time (ms) of fn() on torch's current stream (the launch stream)."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def bench_mode(args):
+    """One JSON line for a variant of the path: SENDER ordering, forward mode, second order."""
+    import numpy as np
+    import torch
+
+    from equivariant_gnn_message_amd import e3conv as E
+    from equivariant_gnn_message_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    inp = synth.make_inputs(args.workload)
+    N, Ec = inp.num_nodes, inp.num_edges
+    b_in = 2 if w.dtype == "bf16" else 4
+    C, nx, ny, no, P = w.channels, w.num_x, (w.lmax + 1) ** 2, w.num_out, w.num_paths
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    src_np, dst_np = inp.senders, inp.receivers
+    ordering = E.E3CONV_RECEIVER
+    y_np, s_np = inp.y, inp.s
+    if args.mode == "sender":
+        perm = synth.sender_sorted(src_np, dst_np)
+        src_np, dst_np, y_np, s_np = src_np[perm], dst_np[perm], y_np[perm], s_np[perm]
+        ordering = E.E3CONV_SENDER
+    gather_np, seg_np = (dst_np, src_np) if args.mode == "sender" else (src_np, dst_np)
+    x, y, s, g = dev(inp.x), dev(y_np), dev(s_np), dev(inp.g)
+    gather = dev(gather_np.astype(np.int32))
+    row_ptr = E.e3conv_csr_from_receivers(dev(seg_np.astype(np.int32)), N)
+    order = dev(E.e3conv_receiver_order(row_ptr.cpu().numpy(), gather_np.astype(np.int32), N, Ec,
+                                        args.cluster))
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors, ordering=ordering)
+    fwd_bytes, bwd_bytes = alg_bytes(w, N, Ec, b_in)
+    node_x, node_o = N * nx * C, N * no * C
+    res = {"metric": None, "value": None, "unit": "edges/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+           "config": {"workload": f"{w.name}, N={N} E={Ec}, {w.irreps_in} (x) SH lmax {w.lmax} -> "
+                                  f"{w.irreps_out}", "mode": args.mode}}
+    kernels = {}
+    if args.mode == "sender":
+        out = torch.empty((N, no, C), dtype=torch.float32, device="cuda")
+        kernels["forward"] = (_timed(lambda: plan.forward(x, y, s, gather, row_ptr, out=out, order=order),
+                                     args.steps, args.warmup), fwd_bytes)
+        if w.backward:
+            grads = (torch.empty_like(x), torch.empty_like(y), torch.empty_like(s))
+            kernels["reverse"] = (_timed(lambda: plan.backward(x, y, s, gather, row_ptr, g, grads=grads,
+                                                               order=order), args.steps, args.warmup),
+                                  bwd_bytes)
+        res["metric"] = "edges/sec, SENDER graph ordering (edges grouped by sender), 1 MI355X"
+    elif args.mode == "jvp":
+        dx, dy, ds = (dev(a) for a in synth.make_tangents(inp))
+        out = torch.empty((N, no, C), dtype=torch.float32, device="cuda")
+        out_dot = torch.empty_like(out)
+        jvp_bytes = (2 * node_x * b_in + Ec * (2 * ny * b_in + 2 * P * C * b_in + 4) + 4 * (N + 1)
+                     + 2 * node_o * 4)
+        kernels["jvp"] = (_timed(lambda: plan.jvp(x, y, s, dx, dy, ds, gather, row_ptr, out=out,
+                                                  out_dot=out_dot, order=order),
+                                 args.steps, args.warmup), jvp_bytes)
+        res["metric"] = "edges/sec, fused forward-mode pass (out and its tangent), 1 MI355X"
+    else:
+        if not w.backward:
+            raise SystemExit("--mode second needs a workload with a reverse pass (4)")
+        Gx, Gy, Gs = (dev(a) for a in synth.make_tangents(inp))
+        dx, dy, ds = torch.empty_like(x), torch.empty_like(y), torch.empty_like(s)
+        dg = torch.empty_like(g)
+        e_in = Ec * (ny + P * C) * 4 + Ec * 4 + 4 * (N + 1)
+
+        def second():
+            plan.backward(Gx, y, s, gather, row_ptr, g, grads=(None, dy, ds), order=order)
+            plan.backward(x, Gy, s, gather, row_ptr, g, grads=(dx, None, ds), order=order,
+                          accumulate=(False, False, True))
+            plan.backward(x, y, Gs, gather, row_ptr, g, grads=(dx, dy, None), order=order,
+                          accumulate=(True, True, False))
+            plan.jvp(x, y, s, Gx, Gy, Gs, gather, row_ptr, out_dot=dg, order=order, want_out=False)
+
+        # per call: operands read once, outputs written once, accumulated outputs read once more
+        second_bytes = ((node_x + e_in + node_o + Ec * (ny + P * C) * 4)
+                        + (2 * node_x + e_in + node_o + 2 * Ec * P * C * 4)
+                        + (2 * node_x + e_in + node_o + 2 * Ec * ny * 4)
+                        + (2 * node_x + e_in + Ec * (ny + P * C) * 4 + node_o))
+        kernels["second_order"] = (_timed(second, args.steps, args.warmup), second_bytes)
+        res["metric"] = "edges/sec, second derivatives of the training step (gradient of <G, grad>), 1 MI355X"
+    total_ms = sum(ms for ms, _ in kernels.values())
+    res["value"] = Ec / (total_ms * 1e-3)
+    res["ms_per_step"] = total_ms
+    for k, (ms, by) in kernels.items():
+        res[f"{k}_ms"] = ms
+        res[f"{k}_hbm_GBps"] = by / (ms * 1e-3) / 1e9
+        res[f"{k}_hbm_frac"] = by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS
+    k, (ms, by) = max(kernels.items(), key=lambda kv: kv[1][0])
+    res["roofline"] = {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS,
+                       "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "traffic": None,
+                       "kernel": k, "algorithmic_bytes": by}
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_mode(args.mode, inp, args.cpu_sample_edges)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_mode(mode, inp, sample_edges):
+    """The oracle's variant on the edges of the first receivers (single thread)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import conv, variants
+    from equivariant_gnn_message_amd import synth
+
+    w = inp.workload
+    lay = conv.make_layout(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    # these passes cost several plain forwards each: a smaller sample keeps ~10-30 s
+    e1 = min(sample_edges // (8 if w.dtype == "bf16" else 4), inp.num_edges)
+    x = inp.as_f32("x")
+    y, s = inp.as_f32("y")[:e1], inp.as_f32("s")[:e1]
+    src, dst, N = inp.senders[:e1], inp.receivers[:e1], inp.num_nodes
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        if mode == "sender":
+            variants.forward_sender(lay, x, y, s, src, dst, N)
+            if w.backward:
+                variants.backward_sender(lay, x, y, s, inp.g, src, dst, N)
+            what = "SENDER forward" + (" + reverse" if w.backward else "")
+        elif mode == "jvp":
+            dx, dy, ds = (synth.bf16_to_f32(a).reshape(a.shape) if a.dtype == np.uint16 else a
+                          for a in synth.make_tangents(inp))
+            variants.jvp(lay, x, y, s, dx, dy[:e1], ds[:e1], src, dst, N)
+            what = "forward-mode pass"
+        else:
+            Gx, Gy, Gs = synth.make_tangents(inp)
+            variants.double_backward(lay, x, y, s, inp.g, Gx, Gy[:e1], Gs[:e1], src, dst, N)
+            what = "second derivatives"
+        dt = time.perf_counter() - t0
+    return {"value": e1 / dt, "unit": "edges/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {e1} edges of the same graph, {what}, fp64 numpy, {dt:.1f} s"}
 
 
 if __name__ == "__main__":

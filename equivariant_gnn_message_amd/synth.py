@@ -80,6 +80,7 @@ WORKLOADS = {
 
 # tensor ids
 T_GRAPH, T_X, T_DIR, T_S, T_MLP, T_G = 0, 1, 2, 3, 4, 5
+T_DX, T_DY, T_DS = 6, 7, 8   # tangents / second-order cotangents
 
 
 def rng(workload, tensor_id, chunk=0):
@@ -362,3 +363,10 @@ def edge_vectors(pos, senders, receivers):
     """Receiver minus sender position of each edge."""
     pos = np.asarray(pos, dtype=np.float64)
     return pos[np.asarray(receivers)] - pos[np.asarray(senders)]
+
+
+def make_tangents(inp):
+    """Seeded N(0,1) arrays shaped like x, y, s, in the workload's storage type."""
+    w = inp.workload
+    draw = normal_bf16 if w.dtype == "bf16" else normal_f32
+    return tuple(draw(w.idx, tid, a.shape) for tid, a in ((T_DX, inp.x), (T_DY, inp.y), (T_DS, inp.s)))
