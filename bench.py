@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, AMD published
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix, AMD published
 METRIC = "edges/sec + achieved HBM GB/s (% of peak) for fused TP conv fwd/bwd, 1 MI355X"
 
 
@@ -46,7 +47,7 @@ def parse():
                     help="time every compiled kernel variant (one JSON line each) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (counter calibration) and exit")
-    ap.add_argument("--mode", default="conv", choices=("conv", "sender", "jvp", "second"),
+    ap.add_argument("--mode", default="conv", choices=("conv", "sender", "jvp", "second", "linear"),
                     help="conv: the hot path (default); sender: SENDER graph ordering; "
                          "jvp: fused forward-mode pass; second: second derivatives of the "
                          "training step (one line each)")
@@ -364,6 +365,9 @@ def bench_mode(args):
     from equivariant_gnn_message_amd import e3conv as E
     from equivariant_gnn_message_amd import synth
 
+    if args.mode == "linear":
+        bench_linear(args)
+        return
     w = synth.WORKLOADS[args.workload]
     inp = synth.make_inputs(args.workload)
     N, Ec = inp.num_nodes, inp.num_edges
@@ -454,6 +458,60 @@ def bench_mode(args):
                        "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "traffic": None,
                        "kernel": k, "algorithmic_bytes": by}
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_mode(args.mode, inp, args.cpu_sample_edges)
+    print(json.dumps(res), flush=True)
+
+
+def bench_linear(args):
+    """The output linear on the convolution output of a workload (C_out = C)."""
+    import numpy as np
+    import torch
+
+    from equivariant_gnn_message_amd import e3conv as E
+    from equivariant_gnn_message_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    inp = synth.make_inputs(args.workload)
+    N, C, NO = inp.num_nodes, w.channels, w.num_out
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    nb = plan.num_out_blocks()
+    rng = np.random.default_rng(5)
+    x = torch.from_numpy(rng.standard_normal((N, NO, C)).astype(np.float32)).cuda()
+    W = torch.from_numpy(rng.standard_normal((nb, C, C)).astype(np.float32)).cuda()
+    g = torch.from_numpy(rng.standard_normal((N, NO, C)).astype(np.float32)).cuda()
+    out, gi, gw = torch.empty_like(x), torch.empty_like(x), torch.empty_like(W)
+    fwd_ms = _timed(lambda: plan.linear(x, W, C, out=out), args.steps, args.warmup)
+    bwd_ms = _timed(lambda: E.e3conv_linear_backward(plan.handle, C, 1.0, W, x, N, g, gi, gw),
+                    args.steps, args.warmup)
+    flops = 2.0 * N * NO * C * C
+    tf_f, tf_b = flops / (fwd_ms * 1e-3) / 1e12, 2 * flops / (bwd_ms * 1e-3) / 1e12
+    byt = 4.0 * (2 * N * NO * C + nb * C * C)
+    res = {"metric": "node rows/sec, output linear (channel mixing per irrep block), fp32 MFMA, 1 MI355X",
+           "value": N / ((fwd_ms + bwd_ms) * 1e-3), "unit": "nodes/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": fwd_ms + bwd_ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"output linear on {w.name} output: N={N}, {w.irreps_out} -> same irreps",
+                      "mode": "linear"},
+           "forward_ms": fwd_ms, "forward_TFLOPs": tf_f, "forward_hbm_GBps": byt / (fwd_ms * 1e-3) / 1e9,
+           "reverse_ms": bwd_ms, "reverse_TFLOPs": tf_b,
+           "roofline": {"bound": "mfma", "achieved": tf_f, "peak": PEAK_FP32_MFMA_TFLOPS,
+                        "unit": "TFLOP/s", "frac": tf_f / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                        "kernel": "linear_gemm (forward)", "algorithmic_flops": flops}}
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        from oracle import conv, linear
+        lay = conv.make_layout(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+        n1 = min(N, 4000)
+        xs, gs = x[:n1].cpu().numpy(), g[:n1].cpu().numpy()
+        Wn = W.cpu().numpy()
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            linear.linear(lay, Wn, 1.0, xs)
+            linear.linear_backward(lay, Wn, 1.0, xs, gs)
+            dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": n1 / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {n1} node rows, forward + reverse, fp64 numpy, {dt:.1f} s"}
+    else:
+        res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
 
 

@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libe3conv.so")
 
 SOURCES = ["host_core.cpp", "e3conv.cpp", "kernels.hip", "layout_tiny.hip", "layout_gate.hip",
-           "layout_mace.hip", "layout_big.hip"]
+           "layout_mace.hip", "layout_big.hip", "linear.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]

@@ -415,6 +415,96 @@ e3conv_status e3conv_backward_ex(e3conv_plan_t p, e3conv_dtype dt, const void* x
   return ok();
 }
 
+// ------------------------------------------------------------- linear ---
+
+namespace {
+
+e3conv_status linear_setup(e3conv_plan_t p, int c_out, float scale, int64_t N, e3c::LinearGemm* g) {
+  if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (c_out <= 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "channels_out must be positive");
+  if (!std::isfinite(scale)) return fail(E3CONV_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (N < 0 || N >= ((int64_t)1 << 31) - 1) return fail(E3CONV_ERR_INVALID_ARGUMENT, "bad num_nodes");
+  if (p->num_out > e3c::kMaxLinearComponents)
+    return fail(E3CONV_ERR_UNSUPPORTED, "too many output components for the linear");
+  const int64_t width = p->channels > c_out ? p->channels : c_out;
+  if (N * p->num_out * width >= (int64_t)1 << 31)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "node tensor exceeds 2^31 elements");
+  std::memset(g, 0, sizeof(*g));
+  int o = 0;
+  for (size_t k = 0; k < p->out.size(); ++k)
+    for (int m = 0; m < 2 * p->out[k].l + 1; ++m) g->comp_block[o++] = (int)k;
+  g->num_comp = p->num_out;
+  g->alpha = scale / std::sqrt((float)p->channels);
+  return E3CONV_OK;
+}
+
+}  // namespace
+
+e3conv_status e3conv_linear(e3conv_plan_t p, int c_out, float scale, const float* w, const float* in,
+                            int64_t N, float* out, void* stream) {
+  e3c::LinearGemm g;
+  const e3conv_status st = linear_setup(p, c_out, scale, N, &g);
+  if (st != E3CONV_OK) return st;
+  if (N == 0) return ok();
+  if (!w || !in || !out) return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  const long C = p->channels, NO = p->num_out;
+  g.A = in;   g.a_i = NO * C;      g.a_k = 1;  g.a_comp = C;
+  g.B = w;    g.b_k = c_out;       g.b_j = 1;  g.b_comp = 0;     g.b_block = C * c_out;
+  g.C = out;  g.c_i = NO * c_out;  g.c_j = 1;  g.c_comp = c_out; g.c_block = 0;
+  g.M = (int)N; g.N = c_out; g.K = (int)C; g.k_chunk = (int)C;
+  const hipError_t err = e3c::launch_linear_gemm(g, 1, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "linear launch");
+  return ok();
+}
+
+e3conv_status e3conv_linear_backward(e3conv_plan_t p, int c_out, float scale, const float* w,
+                                     const float* in, int64_t N, const float* grad_out,
+                                     float* grad_in, float* grad_w, void* stream) {
+  e3c::LinearGemm g;
+  e3conv_status st = linear_setup(p, c_out, scale, N, &g);
+  if (st != E3CONV_OK) return st;
+  if (!grad_in && !grad_w) return ok();
+  if (!grad_out || (grad_in && !w) || (grad_w && !in))
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  const long C = p->channels, NO = p->num_out;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (grad_in && N > 0) {
+    e3c::LinearGemm a = g;
+    a.A = grad_out; a.a_i = NO * c_out; a.a_k = 1;  a.a_comp = c_out;
+    a.B = w;        a.b_k = 1;          a.b_j = c_out; a.b_comp = 0; a.b_block = C * c_out;
+    a.C = grad_in;  a.c_i = NO * C;     a.c_j = 1;  a.c_comp = C;  a.c_block = 0;
+    a.M = (int)N; a.N = (int)C; a.K = c_out; a.k_chunk = c_out;
+    const hipError_t err = e3c::launch_linear_gemm(a, 1, s);
+    if (err != hipSuccess) return hip_fail(err, "linear backward launch");
+  }
+  if (grad_w) {
+    hipError_t err = e3c::launch_fill_zero(grad_w, (size_t)p->out.size() * C * c_out, s);
+    if (err != hipSuccess) return hip_fail(err, "fill launch");
+    if (N > 0) {
+      e3c::LinearGemm b = g;
+      b.A = in;       b.a_i = 1;       b.a_k = NO * C;     b.a_comp = C;
+      b.B = grad_out; b.b_k = NO * c_out; b.b_j = 1;    b.b_comp = c_out; b.b_block = 0;
+      b.C = grad_w;   b.c_i = c_out;   b.c_j = 1;        b.c_comp = 0;  b.c_block = C * c_out;
+      b.M = (int)C; b.N = c_out; b.K = (int)N;
+      // split the node reduction so the grid has a few thousand work-groups
+      const long tiles = ((C + 63) / 64) * ((c_out + 63) / 64) * NO;
+      long splits = (4096 + tiles - 1) / tiles;
+      const long max_splits = (N + 255) / 256;
+      if (splits > max_splits) splits = max_splits;
+      if (splits < 1) splits = 1;
+      if (splits * NO > 65535) splits = 65535 / NO;
+      long chunk = (N + splits - 1) / splits;
+      chunk = (chunk + 31) / 32 * 32;
+      splits = (N + chunk - 1) / chunk;
+      b.k_chunk = (int)chunk;
+      b.atomic = 1;
+      err = e3c::launch_linear_gemm(b, (int)splits, s);
+      if (err != hipSuccess) return hip_fail(err, "linear weight-gradient launch");
+    }
+  }
+  return ok();
+}
+
 e3conv_status e3conv_csr_from_receivers(const int32_t* dst, int64_t E, int64_t N, int32_t* row_ptr,
                                         void* stream) {
   if (N < 0 || E < 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "negative size");

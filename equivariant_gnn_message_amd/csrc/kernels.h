@@ -103,6 +103,29 @@ const KernelSet* kernels_gate();
 const KernelSet* kernels_mace();
 const KernelSet* kernels_big();
 
+// One strided GEMM per output component o (blockIdx.z), optionally split
+// along K: C_o(i, j) (+)= alpha * sum_k A_o(i, k) B_o(k, j), with
+// A_o(i, k) = A[o*a_comp + i*a_i + k*a_k], B_o(k, j) = B[o*b_comp + blk(o)*b_block +
+// k*b_k + j*b_j], C_o(i, j) = C[o*c_comp + blk(o)*c_block + i*c_i + j*c_j].
+constexpr int kMaxLinearComponents = 128;
+struct LinearGemm {
+  const float* A;
+  long a_i, a_k, a_comp;
+  const float* B;
+  long b_k, b_j, b_comp, b_block;
+  float* C;
+  long c_i, c_j, c_comp, c_block;
+  int M, N, K;
+  int k_chunk;          // K range of one split (a multiple of 32 when split)
+  int num_comp;
+  int atomic;           // 1: atomic add (K split), 0: store
+  float alpha;
+  int comp_block[kMaxLinearComponents];
+};
+
+hipError_t launch_linear_gemm(const LinearGemm& g, int k_splits, hipStream_t stream);
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
+
 // Streaming reference kernels (copy when dst != nullptr, else read only).
 hipError_t launch_stream(const void* src, void* dst, size_t bytes, hipStream_t stream);
 

@@ -36,7 +36,7 @@ EXPORTED = [
     "e3conv_plan_shape", "e3conv_plan_paths",
     "e3conv_plan_coefficients", "e3conv_plan_supported", "e3conv_forward", "e3conv_forward_masked",
     "e3conv_jvp", "e3conv_backward_workspace_size", "e3conv_backward", "e3conv_backward_ex",
-    "e3conv_csr_from_receivers",
+    "e3conv_linear", "e3conv_linear_backward", "e3conv_csr_from_receivers",
     "e3conv_validate_graph", "e3conv_receiver_order", "e3conv_stream_reference",
     "e3conv_plan_set_variant",
     "e3conv_plan_num_variants",
@@ -91,6 +91,9 @@ def load_library(path=LIB_PATH):
         "e3conv_backward_ex": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P, P, P, P,
                                 ctypes.c_uint, P, ctypes.c_size_t, P], ctypes.c_int),
         "e3conv_receiver_order": ([P, P, I64, I64, ctypes.c_int, P], ctypes.c_int),
+        "e3conv_linear": ([P, ctypes.c_int, ctypes.c_float, P, P, I64, P, P], ctypes.c_int),
+        "e3conv_linear_backward": ([P, ctypes.c_int, ctypes.c_float, P, P, I64, P, P, P, P],
+                                   ctypes.c_int),
         "e3conv_stream_reference": ([P, P, ctypes.c_size_t, P], ctypes.c_int),
         "e3conv_csr_from_receivers": ([P, I64, I64, P, P], ctypes.c_int),
         "e3conv_validate_graph": ([P, P, I64, I64, ctypes.c_int], ctypes.c_int),
@@ -308,6 +311,30 @@ def e3conv_backward_ex(handle, x, y, s, src, row_ptr, num_nodes, num_edges, num_
         _ptr(grad_y), _ptr(grad_s), int(flags), _ptr(workspace), wbytes, _stream(stream)))
 
 
+def e3conv_linear(handle, channels_out, scale, weights, inp, num_nodes, out, stream=None):
+    import torch
+    for t, n in ((weights, "weights"), (inp, "in"), (out, "out")):
+        _need(t, n, torch.float32)
+    _check(load_library().e3conv_linear(handle, int(channels_out), float(scale), _ptr(weights),
+                                        _ptr(inp), int(num_nodes), _ptr(out), _stream(stream)))
+    return out
+
+
+def e3conv_linear_backward(handle, channels_out, scale, weights, inp, num_nodes, grad_out,
+                           grad_in=None, grad_weights=None, stream=None):
+    import torch
+    for t, n in ((weights, "weights"), (inp, "in"), (grad_out, "grad_out")):
+        _need(t, n, torch.float32)
+    for t, n in ((grad_in, "grad_in"), (grad_weights, "grad_weights")):
+        if t is not None:
+            _need(t, n, torch.float32)
+    _check(load_library().e3conv_linear_backward(handle, int(channels_out), float(scale),
+                                                 _ptr(weights), _ptr(inp), int(num_nodes),
+                                                 _ptr(grad_out), _ptr(grad_in), _ptr(grad_weights),
+                                                 _stream(stream)))
+    return grad_in, grad_weights
+
+
 def e3conv_csr_from_receivers(receivers, num_nodes, row_ptr=None, stream=None):
     import torch
     _need(receivers, "receivers", torch.int32)
@@ -393,6 +420,32 @@ class Plan:
 
     def set_variant(self, forward=0, backward=0):
         e3conv_plan_set_variant(self.handle, forward, backward)
+
+    def num_out_blocks(self):
+        return len({(p["l3"], p["p3"]) for p in self.paths()})
+
+    def linear(self, inp, weights, channels_out, scale=1.0, out=None, stream=None):
+        """Output linear (channel mixing per output irrep block); in (N, num_out, C)."""
+        import torch
+        N = inp.shape[0]
+        if tuple(inp.shape) != (N, self.num_out, self.channels):
+            raise ValueError(f"in must be (N, {self.num_out}, {self.channels}), got {tuple(inp.shape)}")
+        if tuple(weights.shape) != (self.num_out_blocks(), self.channels, int(channels_out)):
+            raise ValueError("weights must be (num_out_blocks, C, channels_out)")
+        if out is None:
+            out = torch.empty((N, self.num_out, int(channels_out)), dtype=torch.float32, device=inp.device)
+        return e3conv_linear(self.handle, channels_out, scale, weights, inp, N, out, stream)
+
+    def linear_backward(self, inp, weights, channels_out, grad_out, scale=1.0, want_in=True,
+                        want_weights=True, stream=None):
+        import torch
+        N = inp.shape[0]
+        if tuple(grad_out.shape) != (N, self.num_out, int(channels_out)):
+            raise ValueError("grad_out must be (N, num_out, channels_out)")
+        gi = torch.empty_like(inp) if want_in else None
+        gw = torch.empty_like(weights) if want_weights else None
+        return e3conv_linear_backward(self.handle, channels_out, scale, weights, inp, N,
+                                      grad_out.contiguous(), gi, gw, stream)
 
     def _check_shapes(self, x, y, s, src, row_ptr):
         N, E = x.shape[0], s.shape[0]

@@ -229,6 +229,35 @@ e3conv_status e3conv_backward_ex(e3conv_plan_t plan, e3conv_dtype in_dtype, cons
                                  float* grad_x, float* grad_y, float* grad_s, unsigned flags,
                                  void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Output linear: channel mixing within each output irrep block, the step
+ * after the convolution (cuEquivariance page, Flax NNX layers, IrrepsLinear:
+ * matching irreps mix their channels with scale / sqrt(mul_in)
+ * normalization).  For every output block k of the plan, with C = the plan's
+ * channels and C_out = channels_out,
+ *     out[b, i, v] = scale / sqrt(C) * sum_u weights[k, u, v] * in[b, i, u]
+ * for each component i of block k.
+ *   weights  device float[num_out_blocks * C * C_out] (blocks in the plan's
+ *            output order, then u, then v);
+ *   in       device float (num_nodes, num_out, C), e.g. e3conv_forward's out;
+ *   out      device float (num_nodes, num_out, C_out), fully overwritten.
+ * fp32 products and sums on the matrix cores; asynchronous on hip_stream.
+ * channels_out > 0, scale finite, num_out <= 128 components, else
+ * E3CONV_ERR_INVALID_ARGUMENT / E3CONV_ERR_UNSUPPORTED. */
+e3conv_status e3conv_linear(e3conv_plan_t plan, int channels_out, float scale,
+                            const float* weights, const float* in, int64_t num_nodes, float* out,
+                            void* hip_stream);
+
+/* Reverse pass of e3conv_linear for L = <grad_out, out>:
+ *   grad_in[b, i, u]   = scale / sqrt(C) * sum_v weights[k, u, v] grad_out[b, i, v]
+ *   grad_weights[k, u, v] = scale / sqrt(C) * sum_{b, i in block k} in[b, i, u] grad_out[b, i, v]
+ * Either output may be NULL (not computed).  grad_in is overwritten;
+ * grad_weights is zeroed then accumulated with fp32 atomics across node
+ * chunks (rounding order varies from run to run). */
+e3conv_status e3conv_linear_backward(e3conv_plan_t plan, int channels_out, float scale,
+                                     const float* weights, const float* in, int64_t num_nodes,
+                                     const float* grad_out, float* grad_in, float* grad_weights,
+                                     void* hip_stream);
+
 /* Receiver CSR on the device: row_ptr[b] = first edge whose receiver is >= b,
  * for b = 0..num_nodes, from the receiver of each edge (device int32[num_edges],
  * non-decreasing).  One thread per node, binary search; asynchronous.  For a

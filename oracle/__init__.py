@@ -22,11 +22,12 @@ irreps  -- irreps string parser (``"8x0e+8x1o"``, ``"64x(0e+1o+2e)"``).
 so3     -- Racah complex CG, complex->real basis change, real CG tensors,
            real Wigner D matrices from the exponential map of generators.
 conv    -- path enumeration, brute-force and vectorised forward, backward.
-variants -- SENDER graph ordering, node_mask padding and the forward-mode
-           derivative, built from ``conv``.
+variants -- SENDER graph ordering, node_mask padding, forward-mode and second
+           derivatives, built from ``conv``.
+linear  -- the output linear (channel mixing per irrep block) and its gradients.
 
 Pins (what ties this oracle to something other than itself) live in
 ``tests/test_oracle_*.py``; every function here is pinned there.
 """
 
-from . import irreps, so3, conv, variants  # noqa: F401
+from . import irreps, so3, conv, variants, linear  # noqa: F401

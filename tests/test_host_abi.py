@@ -261,3 +261,19 @@ def test_ordered_plans(lib):
     assert plain.ordering == E.E3CONV_RECEIVER
     v = ctypes.c_int(5)
     assert lib.e3conv_plan_ordering(None, ctypes.byref(v)) == 1
+
+
+def test_linear_argument_errors(lib):
+    w = synth.WORKLOADS[2]
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out)
+    assert plan.num_out_blocks() == 4
+    f = ctypes.c_void_p(0x1000)
+    h = plan.handle
+    assert lib.e3conv_linear(None, 8, 1.0, f, f, 4, f, None) == 1
+    assert lib.e3conv_linear(h, 0, 1.0, f, f, 4, f, None) == 1               # channels_out
+    assert lib.e3conv_linear(h, 8, float("inf"), f, f, 4, f, None) == 1      # scale
+    assert lib.e3conv_linear(h, 8, 1.0, None, f, 4, f, None) == 1            # weights
+    assert lib.e3conv_linear(h, 8, 1.0, f, f, -1, f, None) == 1              # num_nodes
+    assert lib.e3conv_linear(h, 8, 1.0, f, f, 0, f, None) == 0               # empty: no-op
+    assert lib.e3conv_linear_backward(h, 8, 1.0, f, f, 4, f, None, None, None) == 0   # nothing asked
+    assert lib.e3conv_linear_backward(h, 8, 1.0, f, f, 4, None, f, None, None) == 1   # grad_out
