@@ -8,10 +8,11 @@
 // and its reverse is two more GEMMs:
 //     grad_in[:, o, :] = alpha * grad_out[:, o, :] @ W_k^T,
 //     grad_W_k        += alpha * in[:, o, :]^T @ grad_out[:, o, :]  (summed over o in block k).
-// One tiled kernel serves all three through element strides: 64 x 64 output
-// tiles per work-group of four waves, 32-deep K chunks staged in LDS, each
-// wave a 32 x 32 sub-tile of 2 x 2 v_mfma_f32_16x16x4_f32 accumulators
-// (fp32 products and sums, as the scalar reference computes them).  The
+// One tiled kernel serves all three through element strides: 64 x 128 output
+// tiles per work-group of four waves (128 columns cover C_out <= 128 in one
+// tile, so each input row is read from memory once), 32-deep K chunks staged
+// in LDS, each wave a 64 x 32 slab of 4 x 2 v_mfma_f32_16x16x4_f32
+// accumulators (fp32 products and sums, as the scalar reference computes them).  The
 // reduction over nodes for grad_W is split across work-groups and combined
 // with fp32 atomics.
 #include <hip/hip_runtime.h>
@@ -23,7 +24,8 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TM = 64, TN = 64, TK = 32;
+constexpr int TM = 64, TN = 128, TK = 32;
+constexpr int MT = TM / 16;   // 16-row MFMA tiles per wave
 
 __global__ void __launch_bounds__(256) linear_gemm(LinearGemm g) {
   __shared__ float As[TM][TK + 1];
@@ -42,44 +44,81 @@ __global__ void __launch_bounds__(256) linear_gemm(LinearGemm g) {
 
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
-  const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+  const int wc = w * 32;
   const int lr = lane & 15, lk = lane >> 4;
 
-  f32x4 acc[2][2];
+  f32x4 acc[MT][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < MT; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Staging map: thread t always loads the same (row, column) slots of the
+  // A and B tiles, so their element offsets (32-bit: the tensors hold fewer
+  // than 2^31 elements) are computed once; each K chunk only adds k0 * stride.
+  // Consecutive threads walk the operand's contiguous axis.
+  constexpr int RA = TM * TK / 256, RB = TK * TN / 256;
+  const bool a_rows = g.a_k == 1;      // A contiguous along k: thread keeps k, walks rows
+  const bool b_cols = g.b_j == 1;      // B contiguous along j: thread keeps j, walks k
+  int a_off[RA], a_i[RA], a_k[RA];
+  bool a_ok[RA];
+#pragma unroll
+  for (int r = 0; r < RA; ++r) {
+    const int idx = t + 256 * r;
+    a_i[r] = a_rows ? idx / TK : idx % TM;
+    a_k[r] = a_rows ? idx % TK : idx / TM;
+    a_ok[r] = i0 + a_i[r] < g.M;
+    a_off[r] = a_ok[r] ? (int)((long)(i0 + a_i[r]) * g.a_i + (long)a_k[r] * g.a_k) : 0;
+  }
+  int b_off[RB], b_k[RB], b_j[RB];
+  bool b_ok[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int idx = t + 256 * r;
+    b_k[r] = b_cols ? idx / TN : idx % TK;
+    b_j[r] = b_cols ? idx % TN : idx / TK;
+    b_ok[r] = j0 + b_j[r] < g.N;
+    b_off[r] = b_ok[r] ? (int)((long)b_k[r] * g.b_k + (long)(j0 + b_j[r]) * g.b_j) : 0;
+  }
+
+  // Out-of-range slots load a valid element (offset 0 of the chunk: row or
+  // column k0 exists) and are then replaced by zero, so the loads need no
+  // branches.  The next chunk's elements are loaded into registers while the
+  // current chunk is multiplied.
+  float ra[RA], rb[RB];
+  auto fetch = [&](int k0) {
+    const float* Ak = A + (long)k0 * g.a_k;
+    const float* Bk = B + (long)k0 * g.b_k;
+#pragma unroll
+    for (int r = 0; r < RA; ++r) {
+      const bool ok = a_ok[r] && k0 + a_k[r] < kend;
+      const float v = Ak[ok ? a_off[r] : 0];
+      ra[r] = ok ? v : 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const bool ok = b_ok[r] && k0 + b_k[r] < kend;
+      const float v = Bk[ok ? b_off[r] : 0];
+      rb[r] = ok ? v : 0.0f;
+    }
+  };
+  if (kbeg < kend) fetch(kbeg);
   for (int k0 = kbeg; k0 < kend; k0 += TK) {
-    // Stage A (TM x TK) and B (TK x TN); consecutive threads walk the
-    // operand's contiguous axis.
 #pragma unroll
-    for (int r = 0; r < TM * TK / 256; ++r) {
-      const int idx = t + 256 * r;
-      int i, k;
-      if (g.a_k == 1) { i = idx / TK; k = idx % TK; } else { k = idx / TM; i = idx % TM; }
-      const int gi = i0 + i, gk = k0 + k;
-      As[i][k] = (gi < g.M && gk < kend) ? A[(long)gi * g.a_i + (long)gk * g.a_k] : 0.0f;
-    }
+    for (int r = 0; r < RA; ++r) As[a_i[r]][a_k[r]] = ra[r];
 #pragma unroll
-    for (int r = 0; r < TK * TN / 256; ++r) {
-      const int idx = t + 256 * r;
-      int k, j;
-      if (g.b_j == 1) { k = idx / TN; j = idx % TN; } else { j = idx / TK; k = idx % TK; }
-      const int gk = k0 + k, gj = j0 + j;
-      Bs[k][j] = (gk < kend && gj < g.N) ? B[(long)gk * g.b_k + (long)gj * g.b_j] : 0.0f;
-    }
+    for (int r = 0; r < RB; ++r) Bs[b_k[r]][b_j[r]] = rb[r];
     __syncthreads();
+    if (k0 + TK < kend) fetch(k0 + TK);
 #pragma unroll
     for (int kk = 0; kk < TK; kk += 4) {
-      float av[2], bv[2];
+      float av[MT], bv[2];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) av[a] = As[wr + a * 16 + lr][kk + lk];
+      for (int a = 0; a < MT; ++a) av[a] = As[a * 16 + lr][kk + lk];
 #pragma unroll
       for (int b = 0; b < 2; ++b) bv[b] = Bs[kk + lk][wc + b * 16 + lr];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < MT; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[b], acc[a][b], 0, 0, 0);
@@ -89,12 +128,12 @@ __global__ void __launch_bounds__(256) linear_gemm(LinearGemm g) {
 
   // D[4*(lane/16) + r][lane % 16] of each 16 x 16 accumulator
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < MT; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int gi = i0 + wr + a * 16 + 4 * lk + r;
+        const int gi = i0 + a * 16 + 4 * lk + r;
         const int gj = j0 + wc + b * 16 + lr;
         if (gi < g.M && gj < g.N) {
           float* dst = C + (long)gi * g.c_i + (long)gj * g.c_j;
