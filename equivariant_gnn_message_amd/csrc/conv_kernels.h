@@ -955,6 +955,18 @@ __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float
   const bool want_y = !GEN || prm.gy;
   const bool want_x = !GEN || prm.gx;
   float* gsrow = want_s ? prm.gs + (size_t)e * NP * C + li : nullptr;
+  // Accumulating into grad_s: fetch the edge's rows up front, in one batch,
+  // rather than one dependent load per path before its store.
+  float gs_prev[GEN ? NP : 1][CPL];
+  const bool acc_s = GEN && want_s && (prm.flags & kAccumulateS);
+  if constexpr (GEN) {
+    if (acc_s) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) gs_prev[p][c] = __builtin_nontemporal_load(gsrow + p * C + c * LPG);
+    }
+  }
 
   // Per path, with w = K^T g (g already divided by N):
   //   grad_s = sum_m1 x[o1+m1] w[m1]            (= <g, K x>)
@@ -1002,8 +1014,7 @@ __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float
       if (want_s) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-          float* dst = gsrow + p * C + c * LPG;
-          __builtin_nontemporal_store((prm.flags & kAccumulateS) ? ds[c] + *dst : ds[c], dst);
+          __builtin_nontemporal_store(acc_s ? ds[c] + gs_prev[p][c] : ds[c], gsrow + p * C + c * LPG);
         }
       }
     } else {
