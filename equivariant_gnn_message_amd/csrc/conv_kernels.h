@@ -17,11 +17,18 @@
 //   by cross-lane shuffles at the end of the segment.
 // * Per edge: y (channel-less, shared by the group) builds the per-path
 //   matrices K^p[m3][m1] = sum_m2 C^p[m1,m2,m3] y[o2+m2] in registers from the
-//   compile-time nonzero pattern (coefficient values arrive as kernel
-//   arguments, i.e. scalar registers); then per channel
-//   acc[o3+m3] += s[p] * sum_m1 K^p[m3][m1] x[a][o1+m1].
+//   compile-time nonzero pattern (the CG values are compile-time constants,
+//   emitted as instruction literals); then per channel either
+//   acc[o3+m3] += sum_m1 K^p[m3][m1] (s[p] x[a][o1+m1])   (2l1+1 <= 2l3+1) or
+//   acc[o3+m3] += s[p] * sum_m1 K^p[m3][m1] x[a][o1+m1]   (otherwise),
+//   whichever needs fewer products.
+// * The pipelined kernels keep the next edge's rows in flight while the
+//   current edge is contracted (two register buffers).
 // * s and y are streamed with non-temporal loads so the gathered x rows stay
 //   cache resident; out is written with non-temporal stores.
+// * Work-group b runs logical block (b mod 8) * (grid / 8) + b / 8, so each of
+//   the 8 XCDs (each with its own L2) runs a contiguous range of the receiver
+//   processing order.
 #pragma once
 
 #include <hip/hip_runtime.h>
