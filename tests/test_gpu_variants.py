@@ -252,3 +252,53 @@ def test_second_derivatives(idx, n):
     errs = [rel_err(a.detach().cpu().numpy(), b) for a, b in zip(second, ref)]
     say("  max|err|/RMS dx {:.3e} dy {:.3e} ds {:.3e} dg {:.3e}".format(*errs))
     assert max(errs) <= 1e-5
+
+
+def _rows_and_edges(seg, N, k=48, seed=0):
+    """Sampled segment nodes (random plus the heaviest) and the edges of each."""
+    ptr = np.searchsorted(seg, np.arange(N + 1))
+    deg = np.diff(ptr)
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.choice(N, k, replace=False), [int(np.argmax(deg)), 0, N - 1]]))
+    edges = np.concatenate([np.arange(ptr[b], ptr[b + 1]) for b in rows])
+    return rows, edges, ptr
+
+
+def test_sender_full_size_sampled():
+    """SENDER ordering at the full training-workload size, sampled rows against the oracle."""
+    import torch
+    inp, x, y, s, src, dst, g = sender_sorted_inputs(4, None)
+    N, E_ = inp.num_nodes, len(src)
+    say(f"[sender full] N={N} E={E_}")
+    w = inp.workload
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors, ordering=E.E3CONV_SENDER)
+    row_ptr = E.e3conv_csr_from_receivers(dev(src.astype(np.int32)), N)
+    order = dev(E.e3conv_receiver_order(row_ptr.cpu().numpy(), dst.astype(np.int32), N, E_, 512))
+    out = plan.forward(dev(x), dev(y), dev(s), dev(dst.astype(np.int32)), row_ptr, order=order)
+    torch.cuda.synchronize()
+    rows, edges, _ = _rows_and_edges(src, N)
+    ref = variants.forward_sender(lay_of(inp), x, y[edges], s[edges], src[edges], dst[edges], N)[rows]
+    err = rel_err(out.cpu().numpy()[rows], ref)
+    say(f"  {len(rows)} rows, max|err|/RMS {err:.3e}")
+    assert err <= 1e-5
+
+
+def test_jvp_full_size_sampled():
+    """Forward mode at the full MACE-scale size, sampled receivers against the oracle."""
+    import torch
+    inp = synth.make_inputs(2)
+    N = inp.num_nodes
+    say(f"[jvp full] N={N} E={inp.num_edges}")
+    dx, dy, ds = synth.make_tangents(inp)
+    w = inp.workload
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    row_ptr = E.e3conv_csr_from_receivers(dev(inp.receivers.astype(np.int32)), N)
+    out, out_dot = plan.jvp(dev(inp.x), dev(inp.y), dev(inp.s), dev(dx), dev(dy), dev(ds),
+                            dev(inp.senders.astype(np.int32)), row_ptr)
+    torch.cuda.synchronize()
+    rows, edges, _ = _rows_and_edges(inp.receivers, N, seed=1)
+    r, rd = variants.jvp(lay_of(inp), inp.x, inp.y[edges], inp.s[edges], dx, dy[edges], ds[edges],
+                         inp.senders[edges], inp.receivers[edges], N)
+    errs = [rel_err(out.cpu().numpy()[rows], r[rows]), rel_err(out_dot.cpu().numpy()[rows], rd[rows])]
+    say(f"  {len(rows)} rows, max|err|/RMS out {errs[0]:.3e} out_dot {errs[1]:.3e}")
+    assert max(errs) <= 1e-5
