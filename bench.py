@@ -187,8 +187,8 @@ def cpu_baseline(inp, sample_edges, with_backward):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(the multi-GPU sharding is described in DESIGN.md, not implemented)", file=sys.stderr)
+        print(f"bench.py: e3conv runs on one GPU per process; --gpus {args.gpus} is not supported "
+              f"(multi-GPU sharding is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     if args.calibrate_copy:

@@ -2,15 +2,16 @@
 // (device templates and launchers; each layout file instantiates them).
 //
 //   out[b] = (1/N) sum_{e=(a->b)} (x[a] (x) y[e]) (.) s[e]
-// (e3j Convolution page: class formula; the plain implementation's four steps
-// -- gather by senders, tensor product with the edge features, mixing with
-// the edge scalars, scatter-add onto receivers -- are fused into one pass.)
+// (e3j Convolution page: class formula.  The unfused implementation the page
+// describes runs over all edges four times -- sender rows, product with the
+// harmonics, weighting by the scalars, accumulation at the receivers; here
+// the four happen in one pass per receiver.)
 //
 // Design (wave64):
 // * Receiver-sorted CSR: a wave owns one or more receivers, so the scatter-add
 //   becomes a register-resident segmented sum with a single coalesced store
-//   per output row and no atomics (RECEIVER ordering of the e3j page, which
-//   aggregates each receiver's incoming edges directly).
+//   per output row and no atomics (the e3j page's RECEIVER ordering: every
+//   receiver's messages are summed where they arrive).
 // * Trailing channels: lanes map to channels.  A "group" of LPG = C/CPL lanes
 //   covers all C channels of one edge, CPL channels per lane; a wave holds
 //   64/LPG groups, GPR of which split the edges of one receiver and are summed
@@ -715,8 +716,8 @@ __device__ __forceinline__ void zero_edge_grads(const BwdParams& prm, int e0, in
 //
 // Reverse pass of L = <g, out>, receiver ordered: the cotangent row g[b] is
 // loaded once per receiver; per incoming edge the narrow sender row x[a] is
-// gathered (the e3j page prefers RECEIVER ordering because the backward's
-// per-edge gather then stays on the node features).  With t^p = K^p x[a] and
+// gathered (the reason the e3j page gives for preferring RECEIVER ordering:
+// the reverse pass then reads x rows per edge, narrower than cotangent rows).  With t^p = K^p x[a] and
 // h^p = s^p * g[b] / N (per channel):
 //   grad_s[e,p] = sum_m3 g[b][o3+m3] t^p[m3] / N
 //   grad_y[e,o2+m2] = sum_p sum_c sum_{m1,m3} C^p[m1,m2,m3] x[a][o1+m1] h^p[m3]

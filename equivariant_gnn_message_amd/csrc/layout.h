@@ -1,14 +1,15 @@
 // Compile-time description of one irrep layout of the convolution
 //   m_b = (1/N) sum_{a->b} (x_a (x) y_ab) (.) s_ab
-// (e3j Convolution page, class formula and plain implementation).
+// (e3j Convolution page: class formula, and the unfused implementation
+// described beneath it).
 //
 // A layout is (C, x blocks, SH lmax L, output blocks).  Blocks are encoded in a
 // 32-bit "block code": 2 bits per l = 0..15, 0 = absent, 1 = even, 2 = odd;
 // blocks are stored in ascending l.  Paths are every (x block, l2 = 0..L,
 // output block) triple, in that nesting order, with |l1-l2| <= l3 <= l1+l2 and
 // p3 = p1 (-1)^l2 (the edge features are spherical harmonics of parity (-1)^l2).
-// The path index is the scalar axis of s (the "third source space" that the
-// page infers from the two inputs).
+// The path index is the scalar axis of s (the page derives the space of the
+// mixing scalars from the spaces of the two inputs).
 //
 // The nonzero pattern of each real Clebsch-Gordan tensor C[m1,m2,m3] (real
 // basis, m = -l..l) follows the selection rule

@@ -1,7 +1,7 @@
 // Output linear (channel mixing within each irrep block) on fp32 MFMA.
 //
-// cuEquivariance page, Flax NNX layers, IrrepsLinear: matching irreps mix
-// their channels, out[..., v, i] = scale / sqrt(mul_in) * sum_u w[u, v] in[..., u, i].
+// cuEquivariance page, Flax NNX layers, IrrepsLinear: within each irrep block
+// the channels are mixed, out[..., v, i] = scale / sqrt(mul_in) * sum_u w[u, v] in[..., u, i].
 // With trailing channels the convolution output is (N, num_out, C): for each
 // output component o (of block k) this is a plain GEMM over the node axis,
 //     out[:, o, :] = alpha * in[:, o, :] @ W_k,   W_k (C, C_out),

@@ -1,8 +1,8 @@
 /*
  * e3conv -- equivariant message-passing convolution on AMD MI355X (gfx950).
  *
- * The operation (e3j "Convolution" API page, class formula and the four-step
- * plain implementation beneath it):
+ * The operation (e3j Convolution API page: the class formula, and the
+ * unfused JAX implementation described beneath it):
  *
  *     out[b] = (1/N) * sum over edges e = (a -> b) of  (x[a] (x) y[e]) (.) s[e]
  *
@@ -11,12 +11,12 @@
  * - y  edge features (spherical harmonics 0..sh_lmax), shape (num_edges, num_y),
  *      no channel axis, broadcast over channels;
  * - s  edge scalars, shape (num_edges, num_paths, C): one value per
- *      (path, channel), the "third source space" the page infers from x and y;
+ *      (path, channel); the page derives this space from those of x and y;
  * - (x) the channelwise Clebsch-Gordan tensor product, one path per allowed
  *      (x block, l2, output block) triple; (.) the per-(path, channel) mixing;
  * - the sum runs over the incoming edges of receiver b (RECEIVER ordering of
  *      that page: edges sorted by receiver, so aggregation is a segmented sum);
- * - N = avg_num_neighbors ("messages are divided by this factor").
+ * - N = avg_num_neighbors: every message is scaled by 1/N.
  *
  * Conventions (readings of the pages; the pages print no formula for them):
  * - components: blocks in the order given, m = -l..l inside a block, real
@@ -69,8 +69,9 @@ typedef enum { E3CONV_F32 = 0, E3CONV_BF16 = 1 } e3conv_dtype;
  * the incoming edges of b directly.  SENDER: edges grouped by sender; out[b]
  * is assembled from the outgoing edges e = (b -> a) of b as
  * (1/N) sum_e (x[a] (x) P y[e]) (.) s[e], where P negates the odd-l blocks of
- * y.  Under the page's assumptions for SENDER ordering (every edge (a, b) has
- * its reverse, y[b->a] = (-1)^l y[a->b] per l block, s[b->a] = s[a->b]) this
+ * y.  Under the page's assumptions for SENDER ordering (the graph holds b->a
+ * whenever it holds a->b, y[b->a] = (-1)^l y[a->b] per l block, and
+ * s[b->a] = s[a->b]) this
  * equals the RECEIVER result; the library computes the formula above
  * whether or not they hold, and its reverse pass is the exact derivative of
  * that formula. */
@@ -231,8 +232,8 @@ e3conv_status e3conv_backward_ex(e3conv_plan_t plan, e3conv_dtype in_dtype, cons
 
 /* Output linear: channel mixing within each output irrep block, the step
  * after the convolution (cuEquivariance page, Flax NNX layers, IrrepsLinear:
- * matching irreps mix their channels with scale / sqrt(mul_in)
- * normalization).  For every output block k of the plan, with C = the plan's
+ * each block is mixed across its channels by a weight matrix and scaled by
+ * scale / sqrt of the input multiplicity).  For every output block k of the plan, with C = the plan's
  * channels and C_out = channels_out,
  *     out[b, i, v] = scale / sqrt(C) * sum_u weights[k, u, v] * in[b, i, u]
  * for each component i of block k.

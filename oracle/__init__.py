@@ -6,9 +6,10 @@ convolution
     m_b = (1/N) * sum_{a -> b} (x_a (x) y_ab) (.) s_ab
 
 as defined on the e3j ``Convolution`` API page (class description, the
-formula and the four-step plain implementation: gather by senders, tensor
-product with edge features, mixing with edge scalars, scatter-add onto
-receivers, optional division by ``avg_num_neighbors``).
+formula, and the unfused JAX implementation the page describes: each edge
+takes its sender's row of x, forms the product with its harmonics y,
+weights it by its scalars s, and is summed into its receiver's row, with
+the sum scaled by 1/avg_num_neighbors).
 
 It exists only to check the HIP implementation.  Only ``tests/``,
 ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may

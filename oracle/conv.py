@@ -4,28 +4,30 @@ Definition (e3j ``Convolution`` page, class formula):
 
     m_b = (1/N) sum_{a -> b} (x_a (x) y_ab) (.) s_ab
 
-computed the way the same page's "plain implementation" lists it:
-  1. gather node features by senders,
-  2. tensor product of the gathered features with the edge features,
-  3. mix the tensor-product outputs with the edge scalars,
-  4. scatter-add the messages onto receivers,
-then divide by ``avg_num_neighbors`` ("messages are divided by this factor").
+computed in the order of the unfused JAX implementation that the same
+page describes, step by step over all edges:
+  1. each edge takes its sender's row of x,
+  2. that row meets the edge's harmonics y in the channelwise CG product,
+  3. every (path, channel) of the product is weighted by the edge scalar s,
+  4. each edge's message is added into its receiver's row,
+and the sums are scaled by 1/N, N = ``avg_num_neighbors``.
 
 Shapes follow the same page's ``__call__``: node_features (num_nodes, num_x, C),
 edge_features (num_edges, num_y) broadcast over channels, edge_scalars
 (num_edges, num_scalars, C), senders / receivers index vectors in
 [0, num_nodes).  The oracle accepts edges in any order.
 
-Readings where the page is silent (each listed in the design doc):
+Readings where the page is silent:
 * the tensor product is channelwise ("weighted"): channel c of x meets the
   channel-less y, every allowed (x block, l2, out block) triple is one path,
-  and the mixing scalars carry one value per (path, channel) -- the "third
-  source space inferred from the former two";
+  and the mixing scalars carry one value per (path, channel): the page derives
+  this third operand's space from the spaces of x and y;
 * a path exists iff |l1-l2| <= l3 <= l1+l2 and p3 = p1 * (-1)^l2 (y are
   spherical harmonics, parity (-1)^l2); paths are enumerated x block, then
   l2 = 0..L, then output block; this order is the scalar axis;
 * paths into the same output block add up;
-* an output block no path reaches is an error (the "target" filters blocks);
+* an output block no path reaches is an error (the target argument filters
+  output blocks, it does not create them);
 * CG tensors are the real, orthonormal ones of ``oracle.so3.real_cg``.
 """
 

@@ -1,8 +1,8 @@
 """Oracle for the output linear (test infrastructure, fp64).
 
-cuEquivariance page, Flax NNX layers, ``IrrepsLinear``: matching irreps mix
-their channels, output[ir] = scale / sqrt(mul_in) * einsum("uv,...ui->...vi",
-w[ir], features[ir]), with features[ir] of shape (..., mul, ir.dim).  Applied
+cuEquivariance page, Flax NNX layers, ``IrrepsLinear``: within each irrep
+block, output[..., v, i] = scale / sqrt(mul_in) * sum_u w[u, v] input[..., u, i],
+u and v running over the input and output channels, i over the components.  Applied
 to the convolution output (N, num_out, C) -- trailing channels -- each output
 block of the layout is one ``ir`` with mul_in = C.
 """
@@ -27,9 +27,8 @@ def linear(lay, w, scale, x):
     out = np.zeros((N, lay.num_out, w.shape[2]))
     factor = scale / np.sqrt(C)
     for k, (o, d) in enumerate(blocks(lay)):
-        feat = x[:, o:o + d, :].transpose(0, 2, 1)                 # (..., mul, ir.dim)
-        res = factor * np.einsum("uv,...ui->...vi", w[k], feat)
-        out[:, o:o + d, :] = res.transpose(0, 2, 1)
+        # trailing channels: x[n, component, u]; out[n, component, v]
+        out[:, o:o + d, :] = factor * np.einsum("niu,uv->niv", x[:, o:o + d, :], w[k])
     return out
 
 

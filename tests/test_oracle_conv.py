@@ -1,8 +1,8 @@
 """Pins for the oracle convolution (forward and backward), CPU only.
 
 The properties come from the pages: the definition and plain algorithm on the
-e3j Convolution page; O(3) equivariance over rotations and inversion, message
-invariance to edge ordering and safe zero-edge execution, repeated indices and
+e3j Convolution page; O(3) equivariance over rotations and inversion, results
+independent of the edge order, graphs without edges, repeated indices and
 empty inputs for the scatter, isolated nodes, input gradients (e3nn_mlx
 gate-points page, verification evidence); explicit edgewise summation and
 finite differences (cuEquivariance skill page, examples).  Hand-worked values
