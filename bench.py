@@ -132,12 +132,38 @@ def kernel_source_files():
                   ("conv_kernels.h", "kernels.h", "layout.h"))
 
 
+def strip_comments(src):
+    """C/C++ source without comments and with whitespace runs collapsed (code only)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
-    """sha256[:16] of the device sources (every .hip file and the kernel headers)."""
+    """sha256[:16] of the code of the device sources (every .hip file and the kernel
+    headers), comments and layout whitespace excluded: an edit of the comments
+    leaves the counter records of unchanged kernels valid."""
     h = hashlib.sha256()
     for f in kernel_source_files():
-        with open(os.path.join(ROOT, "equivariant_gnn_message_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "equivariant_gnn_message_amd", "csrc", f)) as fh:
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
