@@ -302,12 +302,31 @@ def radial_mlp_scalars(r, width, rmax, idx=1, num_basis=5, hidden=100):
     rbf = np.exp(-(((r[:, None] - mu[None, :]) / sigma) ** 2))
     cut = 0.5 * (1.0 + np.cos(np.pi * r / rmax))
     feat = rbf * cut[:, None]
-    wr = rng(idx, T_MLP)
-    W1 = wr.standard_normal((num_basis, hidden)) / math.sqrt(num_basis)
-    W2 = wr.standard_normal((hidden, width)) / math.sqrt(hidden)
+    W1, W2 = radial_mlp_weights(width, idx, num_basis, hidden)
     h = feat @ W1
     h = h / (1.0 + np.exp(-h))
     return (h @ W2).astype(np.float32)
+
+
+def radial_mlp_weights(width, idx=1, num_basis=5, hidden=100):
+    """The two weight matrices of the radial MLP, N(0, 1) / sqrt(fan_in), float64."""
+    wr = rng(idx, T_MLP)
+    W1 = wr.standard_normal((num_basis, hidden)) / math.sqrt(num_basis)
+    W2 = wr.standard_normal((hidden, width)) / math.sqrt(hidden)
+    return W1, W2
+
+
+def radial_inputs(inp):
+    """Edge lengths and float32 MLP weights of a gate-points workload's edges.
+
+    The lengths are |pos[receiver] - pos[sender]|; the weights are the draws
+    that generate the workload's s, so the MLP of these inputs reproduces s.
+    """
+    w = inp.workload
+    pos = inp.extra["pos"]
+    r = np.linalg.norm(pos[inp.receivers] - pos[inp.senders], axis=1).astype(np.float32)
+    W1, W2 = radial_mlp_weights(w.num_paths * w.channels, w.idx)
+    return r, W1.astype(np.float32), W2.astype(np.float32)
 
 
 def subgraph16(inp):

@@ -26,9 +26,11 @@ conv    -- path enumeration, brute-force and vectorised forward, backward.
 variants -- SENDER graph ordering, node_mask padding, forward-mode and second
            derivatives, built from ``conv``.
 linear  -- the output linear (channel mixing per irrep block) and its gradients.
+radial  -- edge scalars from edge lengths (radial basis, cutoff, two-layer
+           network) and the convolution they feed.
 
 Pins (what ties this oracle to something other than itself) live in
 ``tests/test_oracle_*.py``; every function here is pinned there.
 """
 
-from . import irreps, so3, conv, variants, linear  # noqa: F401
+from . import irreps, so3, conv, variants, linear, radial  # noqa: F401

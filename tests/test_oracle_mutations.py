@@ -108,3 +108,48 @@ def test_missing_average_is_caught(monkeypatch):
     monkeypatch.setattr(conv, "forward", no_avg)
     assert not golden_ok()
     assert not trilinear_ok()
+
+
+# ------------------------------------------------------- radial scalars -----
+
+def radial_pins_ok():
+    """The closed-form pins of tests/test_oracle_radial.py, as one predicate."""
+    from . import test_oracle_radial as T
+    try:
+        T.test_cutoff_closed_forms()
+        T.test_gaussians_at_their_centers_and_one_sigma_away(5, 2.0, 0.5)
+        T.test_silu_identities()
+        T.test_network_linear_in_last_layer_and_zero_without_first()
+        T.test_scalars_match_the_workload_recipe()
+    except AssertionError:
+        return False
+    return True
+
+
+def test_unpatched_radial_oracle_passes_its_pins():
+    assert radial_pins_ok()
+
+
+@pytest.mark.parametrize("name", ["centers", "no_cutoff", "sigma_squared", "sigmoid", "half_period"])
+def test_radial_mistakes_are_caught(monkeypatch, name):
+    import math as _m
+    from oracle import radial
+    orig_basis, orig_cut, orig_silu = radial.basis, radial.cutoff, radial.silu
+    if name == "centers":            # centers at k r_max / num_basis
+        def basis(r, nb, r_max, sigma):
+            r = np.asarray(r, np.float64)
+            c = np.array([k * r_max / nb for k in range(nb)])
+            return np.exp(-(((r[:, None] - c[None, :]) / sigma) ** 2)) * orig_cut(r, r_max)[:, None]
+        monkeypatch.setattr(radial, "basis", basis)
+    elif name == "no_cutoff":
+        monkeypatch.setattr(radial, "basis", lambda r, nb, r_max, sigma:
+                            orig_basis(r, nb, r_max, sigma) / orig_cut(r, r_max)[:, None])
+    elif name == "sigma_squared":     # exp(-(r - mu)^2 / sigma)
+        def basis(r, nb, r_max, sigma):
+            return orig_basis(r, nb, r_max, _m.sqrt(sigma))
+        monkeypatch.setattr(radial, "basis", basis)
+    elif name == "sigmoid":
+        monkeypatch.setattr(radial, "silu", lambda z: 1.0 / (1.0 + np.exp(-np.asarray(z, np.float64))))
+    elif name == "half_period":       # cos(pi r / (2 r_max))
+        monkeypatch.setattr(radial, "cutoff", lambda r, r_max: orig_cut(r, 2.0 * r_max))
+    assert not radial_pins_ok()
