@@ -333,6 +333,34 @@ e3conv_status e3conv_forward_masked(e3conv_plan_t p, e3conv_dtype dt, const void
   return ok();
 }
 
+e3conv_status e3conv_forward_radial(e3conv_plan_t p, const float* x, const float* y, const float* r,
+                                    const float* w1, const float* w2, int32_t num_basis,
+                                    int32_t hidden, float r_max, float sigma, const int32_t* src,
+                                    const int32_t* row_ptr, const int32_t* order, int64_t N, int64_t E,
+                                    int64_t num_real_nodes, float* out, void* stream) {
+  if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+  e3conv_status st = check_sizes(N, E, p->channels, p->num_out > p->num_x ? p->num_out : p->num_x);
+  if (st != E3CONV_OK) return st;
+  if (num_real_nodes < 0 || num_real_nodes > N)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "num_real_nodes must be in [0, num_nodes]");
+  if (num_basis < 2 || num_basis > 8)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "num_basis must be in [2, 8]");
+  if (hidden < 4 || hidden > 128 || hidden % 4 != 0)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "hidden must be a multiple of 4 in [4, 128]");
+  if (!(r_max > 0.0f) || !(sigma > 0.0f))
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "r_max and sigma must be positive");
+  if (!p->kk || !p->kk->radial_f32)
+    return fail(E3CONV_ERR_UNSUPPORTED, "no radial-scalar kernel for this layout and ordering");
+  if (N == 0) return ok();
+  if (!out || !row_ptr || !w1 || !w2 || (E > 0 && (!x || !y || !r || !src)))
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  e3c::RadialParams prm{x, y, r, w1, w2, src, row_ptr, order, out, (int)N, (int)E, 1.0f / p->avg,
+                        (int)num_real_nodes, num_basis, hidden, r_max, sigma};
+  const hipError_t err = p->kk->radial_f32(prm, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "radial forward launch");
+  return ok();
+}
+
 e3conv_status e3conv_jvp(e3conv_plan_t p, e3conv_dtype dt, const void* x, const void* y,
                          const void* s, const void* dx, const void* dy, const void* ds,
                          const int32_t* src, const int32_t* row_ptr, const int32_t* order,

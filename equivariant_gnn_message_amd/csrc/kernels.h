@@ -63,7 +63,31 @@ struct JvpParams {
   int num_real;
 };
 
+// Convolution with the edge scalars computed per edge from its length:
+// s[e] = silu(f(r[e]) W1) W2, f the Gaussian radial basis times the cosine
+// cutoff (centers k r_max / (num_basis - 1), width sigma).
+struct RadialParams {
+  const float* x;       // (N, NX, C)
+  const float* y;       // (E, NY)
+  const float* r;       // (E) edge lengths
+  const float* w1;      // (num_basis, hidden) row-major
+  const float* w2;      // (hidden, NP * C) row-major; column p * C + c is s[., p, c]
+  const int* src;
+  const int* row_ptr;
+  const int* order;     // (N) or nullptr
+  float* out;           // (N, NO, C)
+  int num_nodes;
+  int num_edges;
+  float inv_avg;
+  int num_real;
+  int num_basis;        // <= 8
+  int hidden;           // multiple of 4, <= 128
+  float r_max;
+  float sigma;
+};
+
 using FwdLauncher = hipError_t (*)(const FwdParams&, hipStream_t);
+using RadialLauncher = hipError_t (*)(const RadialParams&, hipStream_t);
 using BwdLauncher = hipError_t (*)(const BwdParams&, hipStream_t);
 using JvpLauncher = hipError_t (*)(const JvpParams&, hipStream_t);
 
@@ -81,6 +105,7 @@ struct OrderingKernels {
   BwdLauncher bwd_f32_general;  // optional outputs and accumulation
   JvpLauncher jvp_f32;
   JvpLauncher jvp_bf16;
+  RadialLauncher radial_f32;    // nullptr: no radial-scalar kernel for this layout
 };
 
 struct KernelSet {

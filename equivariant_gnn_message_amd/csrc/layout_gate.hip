@@ -1,5 +1,6 @@
 // Kernels of the layout 32x0e+32x1o, lmax 3 -> 32x(0e+1o+2e).
 #include "conv_kernels.h"
+#include "conv_radial.h"
 
 namespace e3c {
 namespace {
@@ -29,7 +30,7 @@ const KernelSet* kernels_gate() {
   static const KernelSet k = {
     L::C, L::XCODE, L::L, L::OCODE, &kTables, kCG.v,
     {kF32, E3C_N(kF32), kBF16, E3C_N(kBF16), kBwd, E3C_N(kBwd), launch_bwd_pipe<L, 2, 4, true>,
-     launch_jvp<L, float, 2, 4>, launch_jvp<L, bf16_bits, 2, 4>},
+     launch_jvp<L, float, 2, 4>, launch_jvp<L, bf16_bits, 2, 4>, launch_fwd_radial<L>},
     {kSenderF32, 1, kSenderBF16, 1, kSenderBwd, 1, launch_bwd_pipe<LS, 2, 4, true>,
      launch_jvp<LS, float, 2, 4>, launch_jvp<LS, bf16_bits, 2, 4>},
   };

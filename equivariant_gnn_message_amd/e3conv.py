@@ -35,7 +35,7 @@ EXPORTED = [
     "e3conv_plan", "e3conv_plan_ordered", "e3conv_plan_ordering", "e3conv_plan_destroy",
     "e3conv_plan_shape", "e3conv_plan_paths",
     "e3conv_plan_coefficients", "e3conv_plan_supported", "e3conv_forward", "e3conv_forward_masked",
-    "e3conv_jvp", "e3conv_backward_workspace_size", "e3conv_backward", "e3conv_backward_ex",
+    "e3conv_forward_radial", "e3conv_jvp", "e3conv_backward_workspace_size", "e3conv_backward", "e3conv_backward_ex",
     "e3conv_linear", "e3conv_linear_backward", "e3conv_csr_from_receivers",
     "e3conv_validate_graph", "e3conv_receiver_order", "e3conv_stream_reference",
     "e3conv_plan_set_variant",
@@ -82,6 +82,8 @@ def load_library(path=LIB_PATH):
         "e3conv_forward": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, P, P], ctypes.c_int),
         "e3conv_forward_masked": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P, P],
                                   ctypes.c_int),
+        "e3conv_forward_radial": ([P, P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                   ctypes.c_float, P, P, P, I64, I64, I64, P, P], ctypes.c_int),
         "e3conv_jvp": ([P, ctypes.c_int, P, P, P, P, P, P, P, P, P, I64, I64, I64, P, P, P],
                        ctypes.c_int),
         "e3conv_backward_workspace_size": ([P, I64, I64, ctypes.POINTER(ctypes.c_size_t)],
@@ -251,6 +253,23 @@ def e3conv_forward_masked(handle, x, y, s, src, row_ptr, num_nodes, num_edges, n
                                                 _ptr(row_ptr), _ptr(order), int(num_nodes),
                                                 int(num_edges), int(num_real_nodes), _ptr(out),
                                                 _stream(stream)))
+    return out
+
+
+def e3conv_forward_radial(handle, x, y, r, w1, w2, r_max, sigma, src, row_ptr, num_nodes, num_edges,
+                          num_real_nodes, out, order=None, stream=None):
+    import torch
+    for t, n in ((x, "x"), (y, "y"), (r, "r"), (w1, "w1"), (w2, "w2"), (out, "out")):
+        _need(t, n, torch.float32)
+    _check_graph_args(src, row_ptr, order)
+    if w1.dim() != 2 or w2.dim() != 2 or w1.shape[1] != w2.shape[0]:
+        raise ValueError(f"w1 (num_basis, hidden) and w2 (hidden, P*C) do not chain: "
+                         f"{tuple(w1.shape)}, {tuple(w2.shape)}")
+    _check(load_library().e3conv_forward_radial(handle, _ptr(x), _ptr(y), _ptr(r), _ptr(w1), _ptr(w2),
+                                                int(w1.shape[0]), int(w1.shape[1]), float(r_max),
+                                                float(sigma), _ptr(src), _ptr(row_ptr), _ptr(order),
+                                                int(num_nodes), int(num_edges), int(num_real_nodes),
+                                                _ptr(out), _stream(stream)))
     return out
 
 
@@ -469,6 +488,32 @@ class Plan:
             out = torch.empty((N, self.num_out, self.channels), dtype=torch.float32, device=x.device)
         nr = N if num_real_nodes is None else int(num_real_nodes)
         return e3conv_forward_masked(self.handle, x, y, s, src, row_ptr, N, E, nr, out, order, stream)
+
+    def forward_radial(self, x, y, r, w1, w2, src, row_ptr, r_max, sigma=0.5, out=None, order=None,
+                       stream=None, num_real_nodes=None):
+        """out (N, num_out, C) fp32 with s[e] = silu(f(r[e]) w1) w2 formed in the kernel.
+
+        r (E,) edge lengths; w1 (num_basis, hidden); w2 (hidden, num_paths * C); f the
+        Gaussian basis (centers k r_max / (num_basis - 1), width sigma) times the
+        cosine cutoff.
+        """
+        import torch
+        N, E = x.shape[0], r.shape[0]
+        if tuple(x.shape) != (N, self.num_x, self.channels):
+            raise ValueError(f"x must be (N, {self.num_x}, {self.channels}), got {tuple(x.shape)}")
+        if tuple(y.shape) != (E, self.num_y) or tuple(r.shape) != (E,):
+            raise ValueError(f"y must be (E, {self.num_y}) and r (E,), got {tuple(y.shape)}, {tuple(r.shape)}")
+        if w2.dim() != 2 or w2.shape[1] != self.num_paths * self.channels:
+            raise ValueError(f"w2 must be (hidden, {self.num_paths * self.channels}), got {tuple(w2.shape)}")
+        if src.numel() != E or row_ptr.numel() != N + 1:
+            raise ValueError("src must have E entries and row_ptr N+1")
+        if order is not None and order.numel() != N:
+            raise ValueError("order must have N entries")
+        if out is None:
+            out = torch.empty((N, self.num_out, self.channels), dtype=torch.float32, device=x.device)
+        nr = N if num_real_nodes is None else int(num_real_nodes)
+        return e3conv_forward_radial(self.handle, x, y, r, w1, w2, r_max, sigma, src, row_ptr, N, E, nr,
+                                     out, order, stream)
 
     def jvp(self, x, y, s, dx, dy, ds, src, row_ptr, out=None, out_dot=None, order=None,
             stream=None, want_out=True, num_real_nodes=None):

@@ -169,6 +169,33 @@ e3conv_status e3conv_forward_masked(e3conv_plan_t plan, e3conv_dtype in_dtype, c
                                     int64_t num_nodes, int64_t num_edges, int64_t num_real_nodes,
                                     float* out, void* hip_stream);
 
+/* Convolution with the edge scalars computed from the edge lengths in the
+ * kernel (e3nn_mlx gate-points page: radial embedding of each edge length and
+ * the fully connected network that maps it to the convolution's per-path,
+ * per-channel weights; the network's two weight layers without biases):
+ *     f_k(r) = exp(-((r - mu_k) / sigma)^2) * (1 + cos(pi r / r_max)) / 2,
+ *              mu_k = k r_max / (num_basis - 1),
+ *     s[e]   = silu(f(r[e]) w1) w2, reshaped (num_paths, C), silu(z) = z / (1 + e^-z),
+ * then out as e3conv_forward.  The scalars are formed per receiver in
+ * registers and never written to memory.
+ * - x (num_nodes, num_x, C), y (num_edges, num_y), r (num_edges): fp32 device,
+ *   edges sorted by receiver as in e3conv_forward; out fp32 (num_nodes,
+ *   num_out, C), fully overwritten.
+ * - w1 (num_basis, hidden), w2 (hidden, num_paths * C): fp32 device, row
+ *   major; column p * C + c of w2 produces s[., p, c].
+ * - 2 <= num_basis <= 8; hidden a multiple of 4 in [4, 128]; r_max, sigma > 0,
+ *   else E3CONV_ERR_INVALID_ARGUMENT.  Edges with r >= r_max are not
+ *   excluded; the cutoff makes their weight vanish at r = r_max.
+ * - Compiled for layouts of 32 channels and at most 8 paths (the gate-points
+ *   layout) in RECEIVER ordering; other plans give E3CONV_ERR_UNSUPPORTED.
+ * - order and num_real_nodes as e3conv_forward_masked. */
+e3conv_status e3conv_forward_radial(e3conv_plan_t plan, const float* x, const float* y, const float* r,
+                                    const float* w1, const float* w2, int32_t num_basis,
+                                    int32_t hidden, float r_max, float sigma, const int32_t* src,
+                                    const int32_t* row_ptr, const int32_t* order, int64_t num_nodes,
+                                    int64_t num_edges, int64_t num_real_nodes, float* out,
+                                    void* hip_stream);
+
 /* Forward-mode derivative (Jacobian-vector product; e3nn_mlx page, "JVP and
  * generated-kernel boundary").  The convolution is trilinear, so along the
  * tangent (dx, dy, ds)

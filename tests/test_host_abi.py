@@ -277,3 +277,28 @@ def test_linear_argument_errors(lib):
     assert lib.e3conv_linear(h, 8, 1.0, f, f, 0, f, None) == 0               # empty: no-op
     assert lib.e3conv_linear_backward(h, 8, 1.0, f, f, 4, f, None, None, None) == 0   # nothing asked
     assert lib.e3conv_linear_backward(h, 8, 1.0, f, f, 4, None, f, None, None) == 1   # grad_out
+
+
+def test_radial_argument_errors(lib):
+    """e3conv_forward_radial rejects bad network shapes, radii and layouts before any launch."""
+    w = synth.WORKLOADS[1]
+    gate = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    w2 = synth.WORKLOADS[2]
+    mace = E.Plan(w2.irreps_in, w2.lmax, w2.irreps_out, w2.avg_num_neighbors)
+    sender = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors, ordering=E.E3CONV_SENDER)
+    f = ctypes.c_void_p(0x1000)
+    call = lambda h, nb=5, hid=100, rmax=2.0, sig=0.5, N=4, Ecount=8, nr=4, x=f, w1=f: \
+        lib.e3conv_forward_radial(h, x, f, f, w1, f, nb, hid, rmax, sig, f, f, None, N, Ecount, nr, f, None)
+    assert call(None) == 1
+    assert call(gate.handle, nb=1) == 1
+    assert call(gate.handle, nb=9) == 1
+    assert call(gate.handle, hid=102) == 1
+    assert call(gate.handle, hid=132) == 1
+    assert call(gate.handle, rmax=0.0) == 1
+    assert call(gate.handle, sig=float("nan")) == 1
+    assert call(gate.handle, nr=5) == 1
+    assert call(gate.handle, x=None) == 1
+    assert call(gate.handle, w1=None) == 1
+    assert call(mace.handle) == 3        # E3CONV_ERR_UNSUPPORTED: 128 channels
+    assert call(sender.handle) == 3      # RECEIVER ordering only
+    assert call(gate.handle, N=0, Ecount=0, nr=0) == 0
