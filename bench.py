@@ -47,10 +47,12 @@ def parse():
                     help="time every compiled kernel variant (one JSON line each) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (counter calibration) and exit")
-    ap.add_argument("--mode", default="conv", choices=("conv", "sender", "jvp", "second", "linear"),
+    ap.add_argument("--mode", default="conv",
+                    choices=("conv", "sender", "jvp", "second", "linear", "radial"),
                     help="conv: the hot path (default); sender: SENDER graph ordering; "
                          "jvp: fused forward-mode pass; second: second derivatives of the "
-                         "training step (one line each)")
+                         "training step; linear: output linear; radial: edge scalars from "
+                         "edge lengths in the kernel (gate-points workload) (one line each)")
     return ap.parse_args()
 
 
@@ -430,6 +432,9 @@ def bench_mode(args):
     if args.mode == "linear":
         bench_linear(args)
         return
+    if args.mode == "radial":
+        bench_radial(args)
+        return
     w = synth.WORKLOADS[args.workload]
     inp = synth.make_inputs(args.workload)
     N, Ec = inp.num_nodes, inp.num_edges
@@ -572,6 +577,81 @@ def bench_linear(args):
             dt = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": n1 / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
                                "sample": f"first {n1} node rows, forward + reverse, fp64 numpy, {dt:.1f} s"}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+def bench_radial(args):
+    """Forward with the edge scalars formed in the kernel from the edge lengths (gate-points)."""
+    import numpy as np
+    import torch
+
+    from equivariant_gnn_message_amd import e3conv as E
+    from equivariant_gnn_message_amd import synth
+
+    w = synth.WORKLOADS[1]
+    inp = synth.make_inputs(1)
+    N, Ec, C, P = inp.num_nodes, inp.num_edges, w.channels, w.num_paths
+    r, w1, w2 = synth.radial_inputs(inp)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    x, y, rr, W1, W2 = dev(inp.x), dev(inp.y), dev(r), dev(w1), dev(w2)
+    src = dev(inp.senders.astype(np.int32))
+    row_ptr = E.e3conv_csr_from_receivers(dev(inp.receivers.astype(np.int32)), N)
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    out = torch.empty((N, w.num_out, C), dtype=torch.float32, device="cuda")
+    fused_ms = _timed(lambda: plan.forward_radial(x, y, rr, W1, W2, src, row_ptr, w.radius, 0.5, out=out),
+                      args.steps, args.warmup)
+    # the same convolution reading precomputed scalars (E, P, C) from memory
+    s = dev(inp.s)
+    plain_ms = _timed(lambda: plan.forward(x, y, s, src, row_ptr, out=out), args.steps, args.warmup)
+    # the unfused composition for comparison: the network as torch (hipBLAS) GEMMs writing s, then
+    # the plain forward reading it
+    nb_, hid_ = w1.shape
+    centers = torch.arange(nb_, device="cuda", dtype=torch.float32) * (w.radius / (nb_ - 1))
+
+    def unfused():
+        f = torch.exp(-((rr[:, None] - centers[None, :]) / 0.5) ** 2) * \
+            (0.5 * (1.0 + torch.cos(math.pi * rr / w.radius)))[:, None]
+        h = f @ W1
+        s_ = (h * torch.sigmoid(h)) @ W2
+        return plan.forward(x, y, s_.view(Ec, P, C), src, row_ptr, out=out)
+    unfused_ms = _timed(unfused, args.steps, args.warmup)
+    nb, hid = w1.shape
+    flops = 2.0 * Ec * (nb * hid + hid * P * C)
+    tf = flops / (fused_ms * 1e-3) / 1e12
+    # compulsory bytes: per edge y, r and the sender index; per node x, out and row_ptr
+    byt = 4.0 * (Ec * ((w.lmax + 1) ** 2 + 2) + N * (w.num_x + w.num_out) * C + N + 1)
+    res = {"metric": "edges/sec, convolution with edge scalars computed in the kernel from edge "
+                     "lengths (radial basis + 2-layer network), fp32, 1 MI355X",
+           "value": Ec / (fused_ms * 1e-3), "unit": "edges/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": fused_ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": (f"{w.name}: radial graph N={N} E={Ec}, {w.irreps_in} (x) SH lmax {w.lmax} "
+                                   f"-> {w.irreps_out}, s = silu(rbf({nb}) x cutoff @ W1[{nb}x{hid}]) "
+                                   f"@ W2[{hid}x{P * C}] per edge"),
+                      "mode": "radial"},
+           "fused_ms": fused_ms, "fused_TFLOPs_network": tf,
+           "fused_hbm_GBps": byt / (fused_ms * 1e-3) / 1e9,
+           "plain_forward_ms_with_precomputed_s": plain_ms,
+           "unfused_ms_torch_network_then_forward": unfused_ms,
+           "scalar_bytes_not_moved": 2.0 * Ec * P * C * 4,
+           "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tf / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                        "kernel": "conv_fwd_radial (network layers; the tensor product runs on the VALU)",
+                        "algorithmic_flops": flops}}
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        from oracle import conv, radial
+        lay = conv.make_layout(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+        e1 = min(args.cpu_sample_edges, Ec)
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            radial.forward_radial(lay, inp.x, inp.y[:e1], r[:e1], w1, w2, w.radius, 0.5,
+                                  inp.senders[:e1], inp.receivers[:e1], N)
+            dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": e1 / dt, "unit": "edges/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {e1} edges (receiver order), fp64 numpy, {dt:.1f} s"}
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -40,7 +40,7 @@ struct RadialShape {
   static constexpr int C = LY::C, NP = LY::NP;
   static constexpr int NT = NP * C / 16;   // accumulator tiles of 16 columns
   static_assert(C == 32, "radial kernel: 32 channels (two per lane)");
-  static_assert(NT <= 16, "radial kernel: at most 8 paths");
+  static_assert(NT <= 16 && NT % 4 == 0, "radial kernel: at most 8 paths, an even number");
 };
 
 // Wave index in processing order for 8-wave work-groups (XCD-contiguous
@@ -108,18 +108,65 @@ __device__ __forceinline__ void radial_edge(const float (&yv)[LY::NY], const flo
   });
 }
 
+// The rows one lane needs for one edge: y and its two channels of x[src].
+template <class LY>
+struct RadialRows {
+  f32x4 y[LY::NY / 4];
+  float x[LY::NX][2];
+};
+
+template <class LY>
+__device__ __forceinline__ void radial_load(RadialRows<LY>& R, const RadialParams& prm, int e, int a, int n) {
+  constexpr int C = LY::C, NX = LY::NX, NY = LY::NY;
+  static_assert(NY % 4 == 0, "y rows load as float4");
+  const f32x4* yr = reinterpret_cast<const f32x4*>(prm.y + (size_t)e * NY);
+#pragma unroll
+  for (int i = 0; i < NY / 4; ++i) R.y[i] = yr[i];
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    R.x[i][0] = prm.x[((size_t)a * NX + i) * C + n];
+    R.x[i][1] = prm.x[((size_t)a * NX + i) * C + n + 16];
+  }
+}
+
 template <class LY>
 __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParams prm) {
   using SH = RadialShape<LY>;
-  constexpr int C = LY::C, NX = LY::NX, NY = LY::NY, NO = LY::NO, NP = LY::NP, NT = SH::NT;
-  // W2 as [k][n][t] (k < hidden, n < 16, t < NT), W1 as [k][b] (b < 8)
+  constexpr int C = LY::C, NY = LY::NY, NO = LY::NO, NP = LY::NP, NT = SH::NT;
+  // W2 as [k][t/4][n][t%4] (k < hidden, n < 16, t < NT): the 16 lanes of a
+  // quarter-wave read 16 consecutive 16-byte chunks (no bank conflicts);
+  // W1 as [k][b] (b < 8)
   __shared__ __attribute__((aligned(16))) float w2s[kRadialMaxHidden * 16 * NT];
   __shared__ __attribute__((aligned(16))) float w1s[kRadialMaxHidden * kRadialMaxBasis];
 
   const int H = prm.hidden, NB = prm.num_basis;
-  for (int i = threadIdx.x; i < H * NP * C; i += 64 * kRadialWaves) {
-    const int k = i / (NP * C), col = i % (NP * C);
-    w2s[(k * 16 + (col & 15)) * NT + (col >> 4)] = prm.w2[i];
+  // Coalesced float4 reads of W2, eight in flight per thread, scattered into
+  // the LDS layout (NP * C is a multiple of 64, so a float4 stays in one row
+  // and one tile).
+  {
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(prm.w2);
+    const int total4 = H * NP * C / 4;
+    for (int base = threadIdx.x; base < total4; base += 8 * 64 * kRadialWaves) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i4 = base + u * 64 * kRadialWaves;
+        v[u] = i4 < total4 ? g4[i4] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i4 = base + u * 64 * kRadialWaves;
+        if (i4 < total4) {
+          const int k = (4 * i4) / (NP * C), col = (4 * i4) % (NP * C);
+          const int tt = col >> 4, n0 = col & 15;
+          float* dst = w2s + ((k * (NT / 4) + (tt >> 2)) * 16 + n0) * 4 + (tt & 3);
+          dst[0] = v[u].x;
+          dst[4] = v[u].y;
+          dst[8] = v[u].z;
+          dst[12] = v[u].w;
+        }
+      }
+    }
   }
   for (int i = threadIdx.x; i < H * kRadialMaxBasis; i += 64 * kRadialWaves) {
     const int k = i / kRadialMaxBasis, bb = i % kRadialMaxBasis;
@@ -134,25 +181,77 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
   const float center_step = prm.r_max / (float)(NB - 1);
   const float half_turns = 0.5f / prm.r_max;   // cos(pi r / r_max) = cos(2 pi (r / (2 r_max)))
 
+  // Each wave owns a contiguous range of the processing order.  In index
+  // order the ranges are cut at equal shares of the edges (receiver b goes to
+  // the wave whose share holds row_ptr[b]), so waves get similar work; with a
+  // permutation they are cut at equal numbers of receivers.
   const int waves = (int)gridDim.x * kRadialWaves;
-  const int per_wave = (prm.num_nodes + waves - 1) / waves;
   const int wave = logical_wave8();
-  const int b_first = wave * per_wave;
-  const int b_last = b_first + per_wave < prm.num_nodes ? b_first + per_wave : prm.num_nodes;
+  int b_first, b_last;
+  if (prm.order) {
+    const int per_wave = (prm.num_nodes + waves - 1) / waves;
+    b_first = wave * per_wave < prm.num_nodes ? wave * per_wave : prm.num_nodes;
+    b_last = b_first + per_wave < prm.num_nodes ? b_first + per_wave : prm.num_nodes;
+  } else {
+    auto first_at = [&](long v) {   // first b in [0, N] with row_ptr[b] >= v
+      int lo = 0, hi = prm.num_nodes;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((long)prm.row_ptr[mid] < v) lo = mid + 1; else hi = mid;
+      }
+      return lo;
+    };
+    const long E = prm.row_ptr[prm.num_nodes];
+    b_first = first_at(E * wave / waves);
+    b_last = wave == waves - 1 ? prm.num_nodes : first_at(E * (wave + 1) / waves);
+  }
+
+  // The edge length and the four sender indices a lane needs for a tile are
+  // fetched one tile ahead (across receiver boundaries), so that neither the
+  // network nor the gathers of a tile wait for them.
+  auto recv = [&](int bl, int& b, int& beg, int& end) {
+    b = prm.order ? prm.order[bl] : bl;
+    beg = prm.row_ptr[b];
+    end = b < prm.num_real ? prm.row_ptr[b + 1] : beg;
+  };
+  auto tile_ids = [&](int e0, int end, float& rv, int (&sv)[4]) {
+    rv = prm.r[e0 + n < end ? e0 + n : end - 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = e0 + 4 * q + i < end ? prm.src[e0 + 4 * q + i] : 0;
+  };
+  int b = 0, beg = 0, end = 0;
+  float r_cur = 0.0f;
+  int s_cur[4] = {0, 0, 0, 0};
+  if (b_first < b_last) {
+    recv(b_first, b, beg, end);
+    if (beg < end) tile_ids(beg, end, r_cur, s_cur);
+  }
 
   for (int bl = b_first; bl < b_last; ++bl) {
-    const int b = prm.order ? prm.order[bl] : bl;
-    const int beg = prm.row_ptr[b];
-    const int end = b < prm.num_real ? prm.row_ptr[b + 1] : beg;
+    const bool more = bl + 1 < b_last;
+    int bn = 0, begn = 0, endn = 0;
+    if (more) recv(bl + 1, bn, begn, endn);
 
     float acc[NO][2];
 #pragma unroll
     for (int o = 0; o < NO; ++o) acc[o][0] = acc[o][1] = 0.0f;
 
     for (int e0 = beg; e0 < end; e0 += 16) {
+      float r_next = 0.0f;
+      int s_next[4] = {0, 0, 0, 0};
+      if (e0 + 16 < end) {
+        tile_ids(e0 + 16, end, r_next, s_next);
+      } else if (more && begn < endn) {
+        tile_ids(begn, endn, r_next, s_next);
+      }
+      // rows of this lane's first two edges, in flight during the network
+      const int eq = e0 + 4 * q;
+      RadialRows<LY> ra, rb;
+      if (eq < end) radial_load<LY>(ra, prm, eq, s_cur[0], n);
+      if (eq + 1 < end) radial_load<LY>(rb, prm, eq + 1, s_cur[1], n);
+
       // --- hidden units of edge e0 + n (A operand: units 4j + q)
-      const int ea = e0 + n < end ? e0 + n : end - 1;
-      const float rr = prm.r[ea];
+      const float rr = r_cur;
       const float cut = 0.5f * (1.0f + __cosf(6.283185307179586f * (rr * half_turns)));
       float f[kRadialMaxBasis];
 #pragma unroll
@@ -161,11 +260,8 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
         f[bb] = bb < NB ? __expf(-d * d) * cut : 0.0f;
       }
 
-      f32x4 D[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) D[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      for (int j = 0; j < steps; ++j) {
-        const int k = 4 * j + q;
+      // silu(f . W1[:, k]) for this lane's edge
+      auto hidden = [&](int k) {
         const f32x4* w1k = reinterpret_cast<const f32x4*>(w1s + k * kRadialMaxBasis);
         const f32x4 wa = w1k[0], wb = w1k[1];
         float z = f[0] * wa.x;
@@ -176,42 +272,79 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
         z = __builtin_fmaf(f[5], wb.y, z);
         z = __builtin_fmaf(f[6], wb.z, z);
         z = __builtin_fmaf(f[7], wb.w, z);
-        const float hk = z / (1.0f + __expf(-z));
-        const f32x4* bk = reinterpret_cast<const f32x4*>(w2s + (k * 16 + n) * NT);
+        return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+      };
+      // this lane's B values of hidden unit row k for all NT tiles
+      auto bload = [&](int k, f32x4 (&bv)[NT / 4]) {
+        const f32x4* bk = reinterpret_cast<const f32x4*>(w2s + k * 16 * NT) + n;
+#pragma unroll
+        for (int t4 = 0; t4 < NT / 4; ++t4) bv[t4] = bk[16 * t4];
+      };
+      f32x4 D[NT];
+      auto step = [&](float h, const f32x4 (&bv)[NT / 4], bool first) {
 #pragma unroll
         for (int t4 = 0; t4 < NT / 4; ++t4) {
-          const f32x4 bv = bk[t4];
-          D[4 * t4 + 0] = __builtin_amdgcn_mfma_f32_16x16x4f32(hk, bv.x, D[4 * t4 + 0], 0, 0, 0);
-          D[4 * t4 + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(hk, bv.y, D[4 * t4 + 1], 0, 0, 0);
-          D[4 * t4 + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(hk, bv.z, D[4 * t4 + 2], 0, 0, 0);
-          D[4 * t4 + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(hk, bv.w, D[4 * t4 + 3], 0, 0, 0);
+          const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+          D[4 * t4 + 0] = __builtin_amdgcn_mfma_f32_16x16x4f32(h, bv[t4].x, first ? zero : D[4 * t4 + 0], 0, 0, 0);
+          D[4 * t4 + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(h, bv[t4].y, first ? zero : D[4 * t4 + 1], 0, 0, 0);
+          D[4 * t4 + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(h, bv[t4].z, first ? zero : D[4 * t4 + 2], 0, 0, 0);
+          D[4 * t4 + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(h, bv[t4].w, first ? zero : D[4 * t4 + 3], 0, 0, 0);
+        }
+      };
+      // Two operand buffers, each filled two steps before its MFMAs: a step's
+      // hidden unit and B rows never wait for the instructions just before it.
+      f32x4 b0[NT / 4], b1[NT / 4];
+      bload(q, b0);
+      float h0 = hidden(q), h1 = 0.0f;
+      if (steps > 1) {
+        bload(4 + q, b1);
+        h1 = hidden(4 + q);
+      }
+      step(h0, b0, true);
+      for (int j = 0; j < steps; j += 2) {
+        if (j > 0) step(h0, b0, false);
+        if (j + 2 < steps) {
+          h0 = hidden(4 * (j + 2) + q);
+          bload(4 * (j + 2) + q, b0);
+        }
+        if (j + 1 < steps) {
+          step(h1, b1, false);
+          if (j + 3 < steps) {
+            h1 = hidden(4 * (j + 3) + q);
+            bload(4 * (j + 3) + q, b1);
+          }
         }
       }
 
-      // --- tensor product and mixing of edges e0 + 4q + r, channels n, n + 16
+      // --- tensor product and mixing of edges e0 + 4q + r, channels n, n + 16;
+      // the rows of edge r + 2 load while edge r is processed
+      auto edge = [&](const RadialRows<LY>& R, int r) {
+        float sv[NP][2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = e0 + 4 * q + r;
-        if (e < end) {
-          float sv[NP][2];
-#pragma unroll
-          for (int p = 0; p < NP; ++p) {
-            sv[p][0] = D[2 * p][r];
-            sv[p][1] = D[2 * p + 1][r];
-          }
-          float yv[NY];
-#pragma unroll
-          for (int i = 0; i < NY; ++i) yv[i] = prm.y[(size_t)e * NY + i];
-          const int a = prm.src[e];
-          float xv[NX][2];
-#pragma unroll
-          for (int i = 0; i < NX; ++i) {
-            xv[i][0] = prm.x[((size_t)a * NX + i) * C + n];
-            xv[i][1] = prm.x[((size_t)a * NX + i) * C + n + 16];
-          }
-          radial_edge<LY>(yv, xv, sv, acc);
+        for (int p = 0; p < NP; ++p) {
+          sv[p][0] = D[2 * p][r];
+          sv[p][1] = D[2 * p + 1][r];
         }
+        float yv[NY];
+#pragma unroll
+        for (int i = 0; i < NY / 4; ++i) {
+          yv[4 * i] = R.y[i].x; yv[4 * i + 1] = R.y[i].y; yv[4 * i + 2] = R.y[i].z; yv[4 * i + 3] = R.y[i].w;
+        }
+        radial_edge<LY>(yv, R.x, sv, acc);
+      };
+      if (eq < end) {
+        edge(ra, 0);
+        if (eq + 2 < end) radial_load<LY>(ra, prm, eq + 2, s_cur[2], n);
       }
+      if (eq + 1 < end) {
+        edge(rb, 1);
+        if (eq + 3 < end) radial_load<LY>(rb, prm, eq + 3, s_cur[3], n);
+      }
+      if (eq + 2 < end) edge(ra, 2);
+      if (eq + 3 < end) edge(rb, 3);
+      r_cur = r_next;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_cur[i] = s_next[i];
     }
 
     // the four lane groups hold partial sums of different edges
@@ -228,6 +361,13 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
       if ((o & 3) != q) continue;
       __builtin_nontemporal_store(acc[o][0] * prm.inv_avg, orow + o * C + n);
       __builtin_nontemporal_store(acc[o][1] * prm.inv_avg, orow + o * C + n + 16);
+    }
+    if (more) {
+      // after a receiver without edges the next one's first tile was not fetched
+      if (beg == end && begn < endn) tile_ids(begn, endn, r_cur, s_cur);
+      b = bn;
+      beg = begn;
+      end = endn;
     }
   }
 }
