@@ -129,9 +129,10 @@ def alg_bytes(w, N, E, b_in):
 
 
 def kernel_source_files():
+    """Every device source: the .hip files and every header except the host builder's."""
     csrc = os.path.join(ROOT, "equivariant_gnn_message_amd", "csrc")
-    return sorted(f for f in os.listdir(csrc) if f.endswith(".hip") or f in
-                  ("conv_kernels.h", "kernels.h", "layout.h"))
+    return sorted(f for f in os.listdir(csrc)
+                  if f.endswith(".hip") or (f.endswith(".h") and f != "host_core.h"))
 
 
 def strip_comments(src):
