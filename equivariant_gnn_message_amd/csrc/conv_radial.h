@@ -11,25 +11,29 @@
 // be written by the network and read back by the convolution is formed per
 // receiver in registers.
 //
-// Per receiver, in tiles of 16 of its edges (one wave):
+// Per tile of 16 edges of one receiver (one wave):
 // * lane (m, q) = (lane % 16, lane / 16) evaluates the basis for edge m of the
-//   tile and the hidden units k = 4 j + q (j = 0 .. hidden/4 - 1), which is
-//   exactly the A operand of v_mfma_f32_16x16x4_f32 for contraction step j;
-// * s (16 edges x NP*C) = h W2 is accumulated over hidden/4 steps in NP*C/16
-//   accumulator tiles; W2 is staged once per work-group in LDS, permuted so
-//   that a lane's B values of one step for all N tiles are contiguous;
+//   tile and the hidden units u = 32 j + 4 i + q (i < 8) of contraction step j,
+//   which is the A operand of v_mfma_f32_16x16x32_f16 (A[m][8 q + i]);
+// * s (16 edges x NP*C) = h W2 is accumulated over hidden/32 steps in NP*C/16
+//   accumulator tiles, from two-part fp16 operands (fp32-level accuracy, see
+//   the kernel); W2 is staged once per work-group in LDS;
 // * the accumulator layout hands lane (g, n) = (lane / 16, lane % 16) the
 //   scalars of edges 4g .. 4g+3 of the tile for channels n and n + 16 of every
 //   path (column p*C + c lies in tile 2p + c/16), so each lane runs the tensor
 //   product and mixing of its 4 edges for those two channels;
-// * the partial sums of the 4 lane groups are combined per receiver with
-//   cross-lane shuffles and each output row is written once.
+// * the partial sums of the 4 lane groups are combined with cross-lane
+//   shuffles; a receiver's tiles are summed in registers by the wave that
+//   holds them, or through LDS when neighbouring waves share the receiver,
+//   and each output row is written once.
 #pragma once
 
 #include "conv_kernels.h"
 
 namespace e3c {
 namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRadialWaves = 8;          // waves per work-group (one W2 copy in LDS)
 constexpr int kRadialMaxHidden = 128;
@@ -43,13 +47,25 @@ struct RadialShape {
   static_assert(NT <= 16 && NT % 4 == 0, "radial kernel: at most 8 paths, an even number");
 };
 
-// Wave index in processing order for 8-wave work-groups (XCD-contiguous
-// ranges, as logical_wave() for 4-wave groups).
-__device__ __forceinline__ int logical_wave8() {
-  const int per_xcd = (int)(gridDim.x >> 3);
-  const int bid = (int)blockIdx.x;
-  const int lb = (bid & 7) * per_xcd + (bid >> 3);
-  return __builtin_amdgcn_readfirstlane(lb * kRadialWaves + (int)(threadIdx.x >> 6));
+// First b in [0, n] with row_ptr[b] + 8 b >= v (requires v <= row_ptr[n] + 8 n),
+// searched by the whole wave: each round reads 64 samples of the range and
+// keeps the interval between the last sample below v and the first at or above
+// it, so a range of n shrinks to one entry in about log64(n) + 1 dependent loads.
+__device__ __forceinline__ int radial_lower_bound(const int* row_ptr, int n, long v, int lane) {
+  int lo = 0, hi = n;   // the answer lies in [lo, hi]; hi always satisfies the condition
+  while (hi - lo >= 64) {
+    const int step = (hi - lo + 63) >> 6;
+    const int idx = lo + (lane + 1) * step < hi ? lo + (lane + 1) * step : hi;   // lane 63 samples hi
+    const unsigned long long m = __ballot((long)row_ptr[idx] + 8L * idx >= v);
+    const int k = (int)__builtin_ctzll(m);
+    const int nhi = __builtin_amdgcn_readlane(idx, k);
+    const int nlo = k == 0 ? lo : __builtin_amdgcn_readlane(idx, k - 1) + 1;
+    lo = nlo;
+    hi = nhi;
+  }
+  const int idx = lo + lane;
+  const unsigned long long m = __ballot(idx <= hi && (long)row_ptr[idx] + 8L * idx >= v);
+  return lo + (int)__builtin_ctzll(m);
 }
 
 // The tensor product and mixing of one edge for a lane's two channels, with
@@ -133,87 +149,231 @@ template <class LY>
 __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParams prm) {
   using SH = RadialShape<LY>;
   constexpr int C = LY::C, NY = LY::NY, NO = LY::NO, NP = LY::NP, NT = SH::NT;
-  // W2 as [k][t/4][n][t%4] (k < hidden, n < 16, t < NT): the 16 lanes of a
-  // quarter-wave read 16 consecutive 16-byte chunks (no bank conflicts);
-  // W1 as [k][b] (b < 8)
-  __shared__ __attribute__((aligned(16))) float w2s[kRadialMaxHidden * 16 * NT];
+  // The second layer (hidden -> NP * C) runs on the fp16 matrix instruction
+  // with each operand split into two fp16 parts, v = hi + lo with
+  // |v - hi - lo| <= 2^-22 |v|, and three products per term (hi hi + hi lo +
+  // lo hi; the dropped lo lo is below 2^-22 of the term), accumulated in fp32:
+  // fp32-level accuracy at a small fraction of the fp32 matrix instruction's
+  // cycles.  Powers of two keep both operands inside the fp16 range: hidden
+  // unit u is scaled by 2^-g_u, with sum_b |W1[b, u]| (a bound of |silu(z_u)|,
+  // since 0 <= f_b <= 1) in [2^(13 + g_u), 2^(14 + g_u)); W2 row u by 2^g_u;
+  // column c by 2^-e_c so that its largest entry lies in [2^13, 2^14); the
+  // accumulated column is multiplied by 2^e_c.
+  //
+  // Hidden unit u = 32 j + 4 i + q is element i of lane group q's A operand in
+  // contraction step j, so the real units of the last step fill the lowest i;
+  // W2 is staged as [j][t][hi, lo][q][n][i] (fp16): the B operand of tile t is
+  // 16 contiguous bytes per lane.  W1 as [u][b] (b < 8).
+  __shared__ __attribute__((aligned(16))) f16x8 w2s[kRadialMaxHidden / 32 * NT * 2 * 64];
   __shared__ __attribute__((aligned(16))) float w1s[kRadialMaxHidden * kRadialMaxBasis];
+  __shared__ float hsc[kRadialMaxHidden];    // 2^-g_u
+  __shared__ int hexp[kRadialMaxHidden];     // g_u
+  __shared__ unsigned colmax[16 * NT];       // bits of max_u |W2[u, c]| 2^g_u (non-negative floats order as integers)
+  __shared__ float colsc[16 * NT];           // 2^e_c
+  // partial output rows of receivers shared between waves ([wave][slot][NO * C]),
+  // which slots are used (bit 0: slot 0, bit 1: slot 1, bit 2: the receiver in
+  // slot 0 also continues after the wave), the receiver in slot 1
+  __shared__ float part[kRadialWaves * 2 * NO * C];
+  __shared__ int part_flags[kRadialWaves];
+  __shared__ int part_recv[kRadialWaves];
 
+  constexpr int NPC = NP * C;
   const int H = prm.hidden, NB = prm.num_basis;
-  // Coalesced float4 reads of W2, eight in flight per thread, scattered into
-  // the LDS layout (NP * C is a multiple of 64, so a float4 stays in one row
-  // and one tile).
+  const int S = (H + 31) >> 5;   // contraction steps of 32 hidden units
+  const int tid = (int)threadIdx.x;
+  // All weight loads are issued before any is used (clamped addresses and
+  // selects instead of branches, which would wait for each load in turn).
+  if (tid < S * 32) {
+    float wv[kRadialMaxBasis];
+    const int uc = tid < H ? tid : H - 1;
+#pragma unroll
+    for (int bb = 0; bb < kRadialMaxBasis; ++bb) wv[bb] = prm.w1[(bb < NB ? bb : NB - 1) * H + uc];
+    float beta = 0.0f;
+#pragma unroll
+    for (int bb = 0; bb < kRadialMaxBasis; ++bb) {
+      wv[bb] = bb < NB && tid < H ? wv[bb] : 0.0f;
+      beta += fabsf(wv[bb]);
+    }
+    const int g = beta > 0.0f ? __builtin_amdgcn_frexp_expf(beta) - 14 : 0;
+    hexp[tid] = g;
+    hsc[tid] = __builtin_amdgcn_ldexpf(1.0f, -g);
+#pragma unroll
+    for (int bb = 0; bb < kRadialMaxBasis; ++bb) w1s[tid * kRadialMaxBasis + bb] = wv[bb];
+  }
+  if (tid < NPC) colmax[tid] = 0u;
+  __syncthreads();
   {
-    const f32x4* g4 = reinterpret_cast<const f32x4*>(prm.w2);
-    const int total4 = H * NP * C / 4;
-    for (int base = threadIdx.x; base < total4; base += 8 * 64 * kRadialWaves) {
-      f32x4 v[8];
+    // thread: column c, steps 2 hf and 2 hf + 1 (64 rows); the loads are
+    // coalesced across the lanes (consecutive columns)
+    const int c = tid & 255, hf = tid >> 8;
+    const int cc = c < NPC ? c : NPC - 1;
+    float w[64];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i4 = base + u * 64 * kRadialWaves;
-        v[u] = i4 < total4 ? g4[i4] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      }
+    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i4 = base + u * 64 * kRadialWaves;
-        if (i4 < total4) {
-          const int k = (4 * i4) / (NP * C), col = (4 * i4) % (NP * C);
-          const int tt = col >> 4, n0 = col & 15;
-          float* dst = w2s + ((k * (NT / 4) + (tt >> 2)) * 16 + n0) * 4 + (tt & 3);
-          dst[0] = v[u].x;
-          dst[4] = v[u].y;
-          dst[8] = v[u].z;
-          dst[12] = v[u].w;
+      for (int q2 = 0; q2 < 4; ++q2)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int u = 32 * (2 * hf + jj) + 4 * i + q2;
+          w[(jj * 4 + q2) * 8 + i] = prm.w2[(size_t)(u < H ? u : H - 1) * NPC + cc];
+        }
+    float m = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int u = 32 * (2 * hf + jj) + 4 * i + q2;
+          float& v = w[(jj * 4 + q2) * 8 + i];
+          v = c < NPC && u < H ? __builtin_amdgcn_ldexpf(v, hexp[u]) : 0.0f;
+          m = fmaxf(m, fabsf(v));
+        }
+    if (c < NPC) atomicMax(&colmax[c], __float_as_uint(m));
+    __syncthreads();
+    const float cm = c < NPC ? __uint_as_float(colmax[c]) : 0.0f;
+    const int e = cm > 0.0f ? __builtin_amdgcn_frexp_expf(cm) - 14 : 0;
+    if (hf == 0 && c < NPC) colsc[c] = __builtin_amdgcn_ldexpf(1.0f, e);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const int j = 2 * hf + jj;
+        if (j < S && c < NPC) {
+          f16x8 hi, lo;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float v = __builtin_amdgcn_ldexpf(w[(jj * 4 + q2) * 8 + i], -e);
+            hi[i] = (_Float16)v;
+            lo[i] = (_Float16)(v - (float)hi[i]);
+          }
+          w2s[((j * NT + (c >> 4)) * 2 + 0) * 64 + q2 * 16 + (c & 15)] = hi;
+          w2s[((j * NT + (c >> 4)) * 2 + 1) * 64 + q2 * 16 + (c & 15)] = lo;
         }
       }
-    }
-  }
-  for (int i = threadIdx.x; i < H * kRadialMaxBasis; i += 64 * kRadialWaves) {
-    const int k = i / kRadialMaxBasis, bb = i % kRadialMaxBasis;
-    w1s[i] = bb < NB ? prm.w1[bb * H + k] : 0.0f;
   }
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
-  const int q = lane >> 4, n = lane & 15;   // A-operand role (edge n, hidden units 4j + q); output role (group q, column n)
-  const int steps = H / 4;
+  const int q = lane >> 4, n = lane & 15;   // A-operand role (edge n, lane group q); output role (group q, column n)
   const float inv_sigma = 1.0f / prm.sigma;
   const float center_step = prm.r_max / (float)(NB - 1);
   const float half_turns = 0.5f / prm.r_max;   // cos(pi r / r_max) = cos(2 pi (r / (2 r_max)))
 
-  // Each wave owns a contiguous range of the processing order.  In index
-  // order the ranges are cut at equal shares of the edges (receiver b goes to
-  // the wave whose share holds row_ptr[b]), so waves get similar work; with a
-  // permutation they are cut at equal numbers of receivers.
-  const int waves = (int)gridDim.x * kRadialWaves;
-  const int wave = logical_wave8();
-  int b_first, b_last;
+  // Work distribution.  Work-group ranges of receivers are cut at equal
+  // shares of row_ptr[b] + 8 b (edges plus the expected padding of a
+  // receiver's last tile) in index order, at equal receiver counts when a
+  // processing order is given.  Within a work-group the tiles (16 edges of one
+  // receiver) are split evenly over the 8 waves, so a receiver can be shared
+  // by neighbouring waves: each wave writes the receivers it holds entirely,
+  // keeps the partial rows of its first and last receiver in LDS when they
+  // continue in another wave, and after a barrier the wave holding the first
+  // part of such a receiver adds the others' parts and writes the row.
+  const int N = prm.num_nodes;
+  const int nblk = (int)gridDim.x;
+  const int blk = (int)(blockIdx.x & 7) * (nblk >> 3) + (int)(blockIdx.x >> 3);   // XCD-contiguous
+  const int wid = (int)(threadIdx.x >> 6);
+  int B0, B1;
   if (prm.order) {
-    const int per_wave = (prm.num_nodes + waves - 1) / waves;
-    b_first = wave * per_wave < prm.num_nodes ? wave * per_wave : prm.num_nodes;
-    b_last = b_first + per_wave < prm.num_nodes ? b_first + per_wave : prm.num_nodes;
+    const int per = (N + nblk - 1) / nblk;
+    B0 = blk * per < N ? blk * per : N;
+    B1 = B0 + per < N ? B0 + per : N;
   } else {
-    auto first_at = [&](long v) {   // first b in [0, N] with row_ptr[b] >= v
-      int lo = 0, hi = prm.num_nodes;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if ((long)prm.row_ptr[mid] < v) lo = mid + 1; else hi = mid;
-      }
-      return lo;
-    };
-    const long E = prm.row_ptr[prm.num_nodes];
-    b_first = first_at(E * wave / waves);
-    b_last = wave == waves - 1 ? prm.num_nodes : first_at(E * (wave + 1) / waves);
+    const long total = (long)prm.row_ptr[N] + 8L * N;
+    B0 = radial_lower_bound(prm.row_ptr, N, total * blk / nblk, lane);
+    B1 = blk == nblk - 1 ? N : radial_lower_bound(prm.row_ptr, N, total * (blk + 1) / nblk, lane);
   }
+
+  // receiver at processing position i: node id and edge range (empty for padding receivers)
+  auto recv = [&](int i, int& b, int& beg, int& end) {
+    b = prm.order ? prm.order[i] : i;
+    beg = prm.row_ptr[b];
+    end = b < prm.num_real ? prm.row_ptr[b + 1] : beg;
+  };
+  // tiles of the receivers at positions c0 + lane (< B1), their inclusive prefix
+  // within the chunk, and the chunk's total
+  auto chunk = [&](int c0, int& nt, int& incl) {
+    nt = 0;
+    if (c0 + lane < B1) {
+      int bb, bg, en;
+      recv(c0 + lane, bb, bg, en);
+      nt = (en - bg + 15) >> 4;
+    }
+    int v = nt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(v, d, 64);
+      if (lane >= d) v += t;
+    }
+    incl = v;
+    return __builtin_amdgcn_readlane(v, 63);
+  };
+  int nt0, incl0;
+  int T = chunk(B0, nt0, incl0);
+  for (int c0 = B0 + 64; c0 < B1; c0 += 64) {
+    int a, c;
+    T += chunk(c0, a, c);
+  }
+  // first position i with (tiles up to and including i) >= v, for 1 <= v <= T:
+  // the receiver holding tile v - 1; also its inclusive prefix and tile count
+  auto locate = [&](int v, int& at, int& a_incl, int& a_nt) {
+    unsigned long long m = __ballot(B0 + lane < B1 && incl0 >= v);
+    if (m) {
+      const int k = (int)__builtin_ctzll(m);
+      at = B0 + k;
+      a_incl = __builtin_amdgcn_readlane(incl0, k);
+      a_nt = __builtin_amdgcn_readlane(nt0, k);
+      return;
+    }
+    int R = __builtin_amdgcn_readlane(incl0, 63);
+    for (int c0 = B0 + 64; c0 < B1; c0 += 64) {
+      int nt, incl;
+      const int tot = chunk(c0, nt, incl);
+      m = __ballot(c0 + lane < B1 && R + incl >= v);
+      if (m) {
+        const int k = (int)__builtin_ctzll(m);
+        at = c0 + k;
+        a_incl = R + __builtin_amdgcn_readlane(incl, k);
+        a_nt = __builtin_amdgcn_readlane(nt, k);
+        return;
+      }
+      R += tot;
+    }
+    at = B1;
+    a_incl = R;
+    a_nt = 0;
+  };
+  // this wave's tiles [ts, te) of the work-group's T; positions [p_lo, p_hi) it
+  // visits (with the receivers without tiles that lie between its tiles and the
+  // previous wave's), P = tiles before p_lo
+  const int ts = (int)((long)T * wid / kRadialWaves), te = (int)((long)T * (wid + 1) / kRadialWaves);
+  int p_lo = B0, P = 0;
+  if (ts > 0) {
+    int at, ai, an;
+    locate(ts, at, ai, an);
+    if (ai == ts) {
+      p_lo = at + 1;
+      P = ts;
+    } else {
+      p_lo = at;
+      P = ai - an;
+    }
+  }
+  int p_hi;
+  if (wid == kRadialWaves - 1) {
+    p_hi = B1;
+  } else if (te == ts) {
+    p_hi = p_lo;
+  } else {
+    int at, ai, an;
+    locate(te, at, ai, an);
+    p_hi = at + 1;
+  }
+  if (lane == 0) part_flags[wid] = 0;
 
   // The edge length and the four sender indices a lane needs for a tile are
   // fetched one tile ahead (across receiver boundaries), so that neither the
   // network nor the gathers of a tile wait for them.
-  auto recv = [&](int bl, int& b, int& beg, int& end) {
-    b = prm.order ? prm.order[bl] : bl;
-    beg = prm.row_ptr[b];
-    end = b < prm.num_real ? prm.row_ptr[b + 1] : beg;
-  };
   auto tile_ids = [&](int e0, int end, float& rv, int (&sv)[4]) {
     rv = prm.r[e0 + n < end ? e0 + n : end - 1];
 #pragma unroll
@@ -222,24 +382,30 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
   int b = 0, beg = 0, end = 0;
   float r_cur = 0.0f;
   int s_cur[4] = {0, 0, 0, 0};
-  if (b_first < b_last) {
-    recv(b_first, b, beg, end);
-    if (beg < end) tile_ids(beg, end, r_cur, s_cur);
+  if (p_lo < p_hi) {
+    recv(p_lo, b, beg, end);
+    const int t0 = ts > P ? ts - P : 0;
+    if (beg + 16 * t0 < end) tile_ids(beg + 16 * t0, end, r_cur, s_cur);
   }
 
-  for (int bl = b_first; bl < b_last; ++bl) {
-    const bool more = bl + 1 < b_last;
+  for (int i = p_lo; i < p_hi; ++i) {
+    const bool more = i + 1 < p_hi;
     int bn = 0, begn = 0, endn = 0;
-    if (more) recv(bl + 1, bn, begn, endn);
+    if (more) recv(i + 1, bn, begn, endn);
+    const int nt = (end - beg + 15) >> 4;
+    const int tlo = ts > P ? ts - P : 0;
+    const int thi = te - P < nt ? te - P : nt;
+    P += nt;
 
     float acc[NO][2];
 #pragma unroll
     for (int o = 0; o < NO; ++o) acc[o][0] = acc[o][1] = 0.0f;
 
-    for (int e0 = beg; e0 < end; e0 += 16) {
+    const int e_stop = beg + 16 * thi;
+    for (int e0 = beg + 16 * tlo; e0 < e_stop; e0 += 16) {
       float r_next = 0.0f;
       int s_next[4] = {0, 0, 0, 0};
-      if (e0 + 16 < end) {
+      if (e0 + 16 < e_stop) {
         tile_ids(e0 + 16, end, r_next, s_next);
       } else if (more && begn < endn) {
         tile_ids(begn, endn, r_next, s_next);
@@ -250,7 +416,7 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
       if (eq < end) radial_load<LY>(ra, prm, eq, s_cur[0], n);
       if (eq + 1 < end) radial_load<LY>(rb, prm, eq + 1, s_cur[1], n);
 
-      // --- hidden units of edge e0 + n (A operand: units 4j + q)
+      // --- radial basis of edge e0 + n
       const float rr = r_cur;
       const float cut = 0.5f * (1.0f + __cosf(6.283185307179586f * (rr * half_turns)));
       float f[kRadialMaxBasis];
@@ -260,61 +426,51 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
         f[bb] = bb < NB ? __expf(-d * d) * cut : 0.0f;
       }
 
-      // silu(f . W1[:, k]) for this lane's edge
-      auto hidden = [&](int k) {
-        const f32x4* w1k = reinterpret_cast<const f32x4*>(w1s + k * kRadialMaxBasis);
-        const f32x4 wa = w1k[0], wb = w1k[1];
-        float z = f[0] * wa.x;
-        z = __builtin_fmaf(f[1], wa.y, z);
-        z = __builtin_fmaf(f[2], wa.z, z);
-        z = __builtin_fmaf(f[3], wa.w, z);
-        z = __builtin_fmaf(f[4], wb.x, z);
-        z = __builtin_fmaf(f[5], wb.y, z);
-        z = __builtin_fmaf(f[6], wb.z, z);
-        z = __builtin_fmaf(f[7], wb.w, z);
-        return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
-      };
-      // this lane's B values of hidden unit row k for all NT tiles
-      auto bload = [&](int k, f32x4 (&bv)[NT / 4]) {
-        const f32x4* bk = reinterpret_cast<const f32x4*>(w2s + k * 16 * NT) + n;
-#pragma unroll
-        for (int t4 = 0; t4 < NT / 4; ++t4) bv[t4] = bk[16 * t4];
-      };
       f32x4 D[NT];
-      auto step = [&](float h, const f32x4 (&bv)[NT / 4], bool first) {
 #pragma unroll
-        for (int t4 = 0; t4 < NT / 4; ++t4) {
-          const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-          D[4 * t4 + 0] = __builtin_amdgcn_mfma_f32_16x16x4f32(h, bv[t4].x, first ? zero : D[4 * t4 + 0], 0, 0, 0);
-          D[4 * t4 + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(h, bv[t4].y, first ? zero : D[4 * t4 + 1], 0, 0, 0);
-          D[4 * t4 + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(h, bv[t4].z, first ? zero : D[4 * t4 + 2], 0, 0, 0);
-          D[4 * t4 + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(h, bv[t4].w, first ? zero : D[4 * t4 + 3], 0, 0, 0);
-        }
-      };
-      // Two operand buffers, each filled two steps before its MFMAs: a step's
-      // hidden unit and B rows never wait for the instructions just before it.
-      f32x4 b0[NT / 4], b1[NT / 4];
-      bload(q, b0);
-      float h0 = hidden(q), h1 = 0.0f;
-      if (steps > 1) {
-        bload(4 + q, b1);
-        h1 = hidden(4 + q);
-      }
-      step(h0, b0, true);
-      for (int j = 0; j < steps; j += 2) {
-        if (j > 0) step(h0, b0, false);
-        if (j + 2 < steps) {
-          h0 = hidden(4 * (j + 2) + q);
-          bload(4 * (j + 2) + q, b0);
-        }
-        if (j + 1 < steps) {
-          step(h1, b1, false);
-          if (j + 3 < steps) {
-            h1 = hidden(4 * (j + 3) + q);
-            bload(4 * (j + 3) + q, b1);
+      for (int t = 0; t < NT; ++t) D[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < S; ++j) {
+        // A operands: hidden units u = 32 j + 4 i + q of this lane's edge, scaled
+        // and split; units beyond H (i >= imax, H a multiple of 4) are zero
+        const int imax = (H - 32 * j) >> 2;
+        f16x8 ah, al;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float h = 0.0f;
+          if (i < imax) {
+            const int u = 32 * j + 4 * i + q;
+            const f32x4* w1u = reinterpret_cast<const f32x4*>(w1s + u * kRadialMaxBasis);
+            const f32x4 wa = w1u[0], wb = w1u[1];
+            float z = f[0] * wa.x;
+            z = __builtin_fmaf(f[1], wa.y, z);
+            z = __builtin_fmaf(f[2], wa.z, z);
+            z = __builtin_fmaf(f[3], wa.w, z);
+            z = __builtin_fmaf(f[4], wb.x, z);
+            z = __builtin_fmaf(f[5], wb.y, z);
+            z = __builtin_fmaf(f[6], wb.z, z);
+            z = __builtin_fmaf(f[7], wb.w, z);
+            h = z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)) * hsc[u];
           }
+          ah[i] = (_Float16)h;
+          al[i] = (_Float16)(h - (float)ah[i]);
+        }
+        // three products per tile, two tiles interleaved
+        const f16x8* bj = w2s + j * NT * 2 * 64 + lane;
+#pragma unroll
+        for (int t = 0; t < NT; t += 2) {
+          const f16x8 bh0 = bj[(2 * t) * 64], bl0 = bj[(2 * t + 1) * 64];
+          const f16x8 bh1 = bj[(2 * t + 2) * 64], bl1 = bj[(2 * t + 3) * 64];
+          D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh0, D[t], 0, 0, 0);
+          D[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh1, D[t + 1], 0, 0, 0);
+          D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl0, D[t], 0, 0, 0);
+          D[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl1, D[t + 1], 0, 0, 0);
+          D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh0, D[t], 0, 0, 0);
+          D[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh1, D[t + 1], 0, 0, 0);
         }
       }
+      // columns back to their scale (tile t holds columns 16 t .. 16 t + 15)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) D[t] *= colsc[16 * t + n];
 
       // --- tensor product and mixing of edges e0 + 4q + r, channels n, n + 16;
       // the rows of edge r + 2 load while edge r is processed
@@ -355,19 +511,54 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
         acc[o][c] += __shfl_xor(acc[o][c], 16, 64);
         acc[o][c] += __shfl_xor(acc[o][c], 32, 64);
       }
-    float* orow = prm.out + (size_t)b * NO * C;
+    if (tlo == 0 && thi == nt) {
+      float* orow = prm.out + (size_t)b * NO * C;
 #pragma unroll
-    for (int o = 0; o < NO; ++o) {
-      if ((o & 3) != q) continue;
-      __builtin_nontemporal_store(acc[o][0] * prm.inv_avg, orow + o * C + n);
-      __builtin_nontemporal_store(acc[o][1] * prm.inv_avg, orow + o * C + n + 16);
+      for (int o = 0; o < NO; ++o) {
+        if ((o & 3) != q) continue;
+        __builtin_nontemporal_store(acc[o][0] * prm.inv_avg, orow + o * C + n);
+        __builtin_nontemporal_store(acc[o][1] * prm.inv_avg, orow + o * C + n + 16);
+      }
+    } else {
+      // shared with a neighbouring wave: slot 0 holds a receiver that began in
+      // an earlier wave, slot 1 one that continues in a later wave
+      const int slot = tlo > 0 ? 0 : 1;
+      float* prow = part + (wid * 2 + slot) * (NO * C);
+#pragma unroll
+      for (int o = 0; o < NO; ++o) {
+        if ((o & 3) != q) continue;
+        prow[o * C + n] = acc[o][0];
+        prow[o * C + n + 16] = acc[o][1];
+      }
+      if (lane == 0) {
+        part_flags[wid] |= slot == 0 ? (thi < nt ? 5 : 1) : 2;
+        if (slot == 1) part_recv[wid] = b;
+      }
     }
     if (more) {
-      // after a receiver without edges the next one's first tile was not fetched
-      if (beg == end && begn < endn) tile_ids(begn, endn, r_cur, s_cur);
+      // after a receiver without tiles here the next one's first tile was not fetched
+      if (tlo == thi && begn < endn) tile_ids(begn, endn, r_cur, s_cur);
       b = bn;
       beg = begn;
       end = endn;
+    }
+  }
+
+  // Receivers shared between waves: the wave holding the first part adds the
+  // parts of the following waves (waves without tiles hold none) up to the one
+  // in which the receiver ends.
+  __syncthreads();
+  if (part_flags[wid] & 2) {
+    const int bb = part_recv[wid];
+    for (int idx = lane; idx < NO * C; idx += 64) {
+      float sum = part[(wid * 2 + 1) * (NO * C) + idx];
+      for (int w2 = wid + 1; w2 < kRadialWaves; ++w2) {
+        const int f = part_flags[w2];
+        if (f == 0) continue;
+        sum += part[(w2 * 2) * (NO * C) + idx];
+        if (!(f & 4)) break;
+      }
+      __builtin_nontemporal_store(sum * prm.inv_avg, prm.out + (size_t)bb * NO * C + idx);
     }
   }
 }
@@ -378,7 +569,7 @@ hipError_t launch_fwd_radial(const RadialParams& p, hipStream_t st) {
   if (p.num_basis < 2 || p.num_basis > kRadialMaxBasis || p.hidden < 4 || p.hidden > kRadialMaxHidden ||
       p.hidden % 4 != 0)
     return hipErrorInvalidValue;
-  // one work-group per CU holds W2; each wave owns a contiguous range of receivers
+  // one work-group per CU holds W2 and a contiguous range of receivers
   const long want = (p.num_nodes + kRadialWaves - 1) / kRadialWaves;
   long blocks = want < 256 ? want : 256;
   blocks = (blocks + 7) / 8 * 8;

@@ -91,6 +91,50 @@ def test_radial_tile_boundaries():
     assert np.all(got[empty] == 0.0)
 
 
+@pytest.mark.parametrize("degrees", [
+    [5, 700, 0, 0, 3, 250, 17, 0, 1, 64, 2],   # receivers spread over several waves of a work-group
+    [0] * 40 + [3, 0, 0, 9] + [0] * 30,        # receivers without edges around a few tiles
+    [1, 2, 1, 0, 3, 1, 1, 2] * 30,             # many one-tile receivers
+], ids=["long", "sparse", "short"])
+def test_radial_receivers_shared_between_waves(degrees):
+    x, y, r, src, dst, N = handmade(degrees, seed=len(degrees))
+    _, w1, w2 = synth.radial_inputs(synth.make_inputs(1, num_graphs=1))
+    ref = radial.forward_radial(lay(), x, y, r, w1, w2, 2.0, 0.5, src, dst, N)
+    got = run(x, y, r, w1, w2, src, dst, N)
+    err = rel_err(got, ref)
+    say(f"[radial shared] {len(degrees)} receivers, {len(dst)} edges: max|err|/RMS = {err:.3e}")
+    assert err <= 1e-5
+    empty = [b for b in range(N) if b >= len(degrees) or degrees[b] == 0]
+    assert np.all(got[empty] == 0.0)
+
+
+@pytest.mark.parametrize("use_order", [False, True], ids=["index", "clustered"])
+def test_radial_heavy_tailed_degrees(use_order):
+    """Degrees 0 .. 600 over 3 000 receivers: work-groups and waves cut inside receivers."""
+    rng = np.random.default_rng(21)
+    deg = rng.geometric(1 / 12, 3000) - 1
+    deg[rng.choice(3000, 12, replace=False)] = rng.integers(100, 600, 12)
+    x, y, r, src, dst, N = handmade(list(deg), seed=22, n_extra=0)
+    _, w1, w2 = synth.radial_inputs(synth.make_inputs(1, num_graphs=1))
+    ref = radial.forward_radial(lay(), x, y, r, w1, w2, 2.0, 0.5, src, dst, N)
+    order = None
+    if use_order:
+        ptr = np.searchsorted(dst, np.arange(N + 1)).astype(np.int32)
+        order = E.e3conv_receiver_order(ptr, src.astype(np.int32), N, len(src), 64)
+    got = run(x, y, r, w1, w2, src, dst, N, order=order)
+    err = rel_err(got, ref)
+    # context: the plain forward reading the oracle's scalars rounded to fp32
+    import torch
+    s = radial.scalars(lay(), r, w1, w2, 2.0, 0.5).astype(np.float32)
+    row_ptr = E.e3conv_csr_from_receivers(dev(dst, np.int32), N)
+    plain = plan().forward(dev(x), dev(y), dev(s), dev(src, np.int32), row_ptr)
+    torch.cuda.synchronize()
+    say(f"[radial heavy] order={use_order} E={len(dst)}: max|err|/RMS = {err:.3e} "
+        f"(plain forward on fp32 scalars: {rel_err(plain.cpu().numpy(), ref):.3e})")
+    assert err <= 1e-5
+    assert np.all(got[deg == 0] == 0.0)
+
+
 @pytest.mark.parametrize("nb,hidden,sigma", [(2, 4, 0.8), (8, 128, 0.3), (5, 36, 0.5)])
 def test_radial_network_shapes(nb, hidden, sigma):
     x, y, r, src, dst, N = handmade([5, 20, 0, 16, 9], seed=nb)
