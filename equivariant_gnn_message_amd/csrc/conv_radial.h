@@ -157,8 +157,9 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
   // cycles.  Powers of two keep both operands inside the fp16 range: hidden
   // unit u is scaled by 2^-g_u, with sum_b |W1[b, u]| (a bound of |silu(z_u)|,
   // since 0 <= f_b <= 1) in [2^(13 + g_u), 2^(14 + g_u)); W2 row u by 2^g_u;
-  // column c by 2^-e_c so that its largest entry lies in [2^13, 2^14); the
-  // accumulated column is multiplied by 2^e_c.
+  // the columns of channel c (one per path) by 2^-e_c so that their largest
+  // entry lies in [2^13, 2^14).  Channels do not mix in the convolution, so
+  // 2^e_c is applied once, to the output row.
   //
   // Hidden unit u = 32 j + 4 i + q is element i of lane group q's A operand in
   // contraction step j, so the real units of the last step fill the lowest i;
@@ -168,8 +169,8 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
   __shared__ __attribute__((aligned(16))) float w1s[kRadialMaxHidden * kRadialMaxBasis];
   __shared__ float hsc[kRadialMaxHidden];    // 2^-g_u
   __shared__ int hexp[kRadialMaxHidden];     // g_u
-  __shared__ unsigned colmax[16 * NT];       // bits of max_u |W2[u, c]| 2^g_u (non-negative floats order as integers)
-  __shared__ float colsc[16 * NT];           // 2^e_c
+  __shared__ unsigned chmax[C];              // bits of max_{u,p} |W2[u, p C + c]| 2^g_u (non-negative floats order as integers)
+  __shared__ float chsc[C];                  // 2^e_c
   // partial output rows of receivers shared between waves ([wave][slot][NO * C]),
   // which slots are used (bit 0: slot 0, bit 1: slot 1, bit 2: the receiver in
   // slot 0 also continues after the wave), the receiver in slot 1
@@ -200,7 +201,7 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
 #pragma unroll
     for (int bb = 0; bb < kRadialMaxBasis; ++bb) w1s[tid * kRadialMaxBasis + bb] = wv[bb];
   }
-  if (tid < NPC) colmax[tid] = 0u;
+  if (tid < C) chmax[tid] = 0u;
   __syncthreads();
   {
     // thread: column c, steps 2 hf and 2 hf + 1 (64 rows); the loads are
@@ -229,11 +230,11 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
           v = c < NPC && u < H ? __builtin_amdgcn_ldexpf(v, hexp[u]) : 0.0f;
           m = fmaxf(m, fabsf(v));
         }
-    if (c < NPC) atomicMax(&colmax[c], __float_as_uint(m));
+    if (c < NPC) atomicMax(&chmax[c % C], __float_as_uint(m));
     __syncthreads();
-    const float cm = c < NPC ? __uint_as_float(colmax[c]) : 0.0f;
+    const float cm = __uint_as_float(chmax[cc % C]);
     const int e = cm > 0.0f ? __builtin_amdgcn_frexp_expf(cm) - 14 : 0;
-    if (hf == 0 && c < NPC) colsc[c] = __builtin_amdgcn_ldexpf(1.0f, e);
+    if (hf == 0 && c < C) chsc[c] = __builtin_amdgcn_ldexpf(1.0f, e);
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -374,14 +375,17 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
   // The edge length and the four sender indices a lane needs for a tile are
   // fetched one tile ahead (across receiver boundaries), so that neither the
   // network nor the gathers of a tile wait for them.
-  auto tile_ids = [&](int e0, int end, float& rv, int (&sv)[4]) {
-    rv = prm.r[e0 + n < end ? e0 + n : end - 1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = e0 + 4 * q + i < end ? prm.src[e0 + 4 * q + i] : 0;
+  // Lane (q, n) holds those of edge e0 + n; the senders of its own four edges
+  // (e0 + 4 q + i) are taken from lanes 4 q + i of its row when needed.
+  auto tile_ids = [&](int e0, int end, float& rv, int& sv) {
+    const int e = e0 + n < end ? e0 + n : end - 1;
+    rv = prm.r[e];
+    sv = prm.src[e];
   };
+  auto sender = [&](int sv, int i) { return __shfl(sv, (lane & 48) | (4 * q + i), 64); };
   int b = 0, beg = 0, end = 0;
   float r_cur = 0.0f;
-  int s_cur[4] = {0, 0, 0, 0};
+  int s_cur = 0;
   if (p_lo < p_hi) {
     recv(p_lo, b, beg, end);
     const int t0 = ts > P ? ts - P : 0;
@@ -404,7 +408,7 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
     const int e_stop = beg + 16 * thi;
     for (int e0 = beg + 16 * tlo; e0 < e_stop; e0 += 16) {
       float r_next = 0.0f;
-      int s_next[4] = {0, 0, 0, 0};
+      int s_next = 0;
       if (e0 + 16 < e_stop) {
         tile_ids(e0 + 16, end, r_next, s_next);
       } else if (more && begn < endn) {
@@ -413,8 +417,9 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
       // rows of this lane's first two edges, in flight during the network
       const int eq = e0 + 4 * q;
       RadialRows<LY> ra, rb;
-      if (eq < end) radial_load<LY>(ra, prm, eq, s_cur[0], n);
-      if (eq + 1 < end) radial_load<LY>(rb, prm, eq + 1, s_cur[1], n);
+      const int a0 = sender(s_cur, 0), a1 = sender(s_cur, 1), a2 = sender(s_cur, 2), a3 = sender(s_cur, 3);
+      if (eq < end) radial_load<LY>(ra, prm, eq, a0, n);
+      if (eq + 1 < end) radial_load<LY>(rb, prm, eq + 1, a1, n);
 
       // --- radial basis of edge e0 + n
       const float rr = r_cur;
@@ -468,9 +473,6 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
           D[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh1, D[t + 1], 0, 0, 0);
         }
       }
-      // columns back to their scale (tile t holds columns 16 t .. 16 t + 15)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) D[t] *= colsc[16 * t + n];
 
       // --- tensor product and mixing of edges e0 + 4q + r, channels n, n + 16;
       // the rows of edge r + 2 load while edge r is processed
@@ -490,17 +492,16 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
       };
       if (eq < end) {
         edge(ra, 0);
-        if (eq + 2 < end) radial_load<LY>(ra, prm, eq + 2, s_cur[2], n);
+        if (eq + 2 < end) radial_load<LY>(ra, prm, eq + 2, a2, n);
       }
       if (eq + 1 < end) {
         edge(rb, 1);
-        if (eq + 3 < end) radial_load<LY>(rb, prm, eq + 3, s_cur[3], n);
+        if (eq + 3 < end) radial_load<LY>(rb, prm, eq + 3, a3, n);
       }
       if (eq + 2 < end) edge(ra, 2);
       if (eq + 3 < end) edge(rb, 3);
       r_cur = r_next;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_cur[i] = s_next[i];
+      s_cur = s_next;
     }
 
     // the four lane groups hold partial sums of different edges
@@ -513,11 +514,12 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
       }
     if (tlo == 0 && thi == nt) {
       float* orow = prm.out + (size_t)b * NO * C;
+      const float sc0 = prm.inv_avg * chsc[n], sc1 = prm.inv_avg * chsc[n + 16];
 #pragma unroll
       for (int o = 0; o < NO; ++o) {
         if ((o & 3) != q) continue;
-        __builtin_nontemporal_store(acc[o][0] * prm.inv_avg, orow + o * C + n);
-        __builtin_nontemporal_store(acc[o][1] * prm.inv_avg, orow + o * C + n + 16);
+        __builtin_nontemporal_store(acc[o][0] * sc0, orow + o * C + n);
+        __builtin_nontemporal_store(acc[o][1] * sc1, orow + o * C + n + 16);
       }
     } else {
       // shared with a neighbouring wave: slot 0 holds a receiver that began in
@@ -558,7 +560,7 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
         sum += part[(w2 * 2) * (NO * C) + idx];
         if (!(f & 4)) break;
       }
-      __builtin_nontemporal_store(sum * prm.inv_avg, prm.out + (size_t)bb * NO * C + idx);
+      __builtin_nontemporal_store(sum * (prm.inv_avg * chsc[idx % C]), prm.out + (size_t)bb * NO * C + idx);
     }
   }
 }
