@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, AMD published
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix, AMD published
+PEAK_FP16_MFMA_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix, AMD published
 METRIC = "edges/sec + achieved HBM GB/s (% of peak) for fused TP conv fwd/bwd, 1 MI355X"
 
 
@@ -405,21 +406,20 @@ def cold_forward_ms(run, reps=10, flush_mib=512):
 
 
 def _timed(fn, steps, warmup):
-    """Mean HIP-event time (ms) of fn() on torch's current stream (the launch stream)."""
-    import numpy as np
+    """Mean time (ms) per call of fn() over `steps` back-to-back calls, from one HIP-event pair
+    on torch's current stream (the launch stream); one pair per region keeps the event records'
+    own cost (a few microseconds each) out of short kernels' times."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    evs = []
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
     for _ in range(steps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
         fn()
-        b.record()
-        evs.append((a, b))
+    b.record()
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return a.elapsed_time(b) / steps
 
 
 def bench_mode(args):
@@ -620,6 +620,10 @@ def bench_radial(args):
     unfused_ms = _timed(unfused, args.steps, args.warmup)
     nb, hid = w1.shape
     flops = 2.0 * Ec * (nb * hid + hid * P * C)
+    # second-layer matrix work as issued: tiles of 16 edges of one receiver, hidden units padded
+    # to steps of 32, three fp16 products per fp32 product
+    deg = np.bincount(inp.receivers, minlength=N)
+    issued = 3 * 2.0 * 16 * (-(-hid // 32) * 32) * P * C * float(np.sum((deg + 15) // 16))
     tf = flops / (fused_ms * 1e-3) / 1e12
     # compulsory bytes: per edge y, r and the sender index; per node x, out and row_ptr
     byt = 4.0 * (Ec * ((w.lmax + 1) ** 2 + 2) + N * (w.num_x + w.num_out) * C + N + 1)
@@ -639,8 +643,12 @@ def bench_radial(args):
            "scalar_bytes_not_moved": 2.0 * Ec * P * C * 4,
            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
                         "frac": tf / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
-                        "kernel": "conv_fwd_radial (network layers; the tensor product runs on the VALU)",
-                        "algorithmic_flops": flops}}
+                        "kernel": ("conv_fwd_radial: the network's fp32 products at fp32 accuracy against the "
+                                   "fp32 matrix peak; the second layer issues three fp16 matrix products per "
+                                   "fp32 product (two-part operands), the tensor product runs on the VALU"),
+                        "algorithmic_flops": flops,
+                        "fp16_issued_TFLOPs": issued / (fused_ms * 1e-3) / 1e12,
+                        "fp16_peak_TFLOPs": PEAK_FP16_MFMA_TFLOPS}}
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits
         from oracle import conv, radial

@@ -459,19 +459,30 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
           ah[i] = (_Float16)h;
           al[i] = (_Float16)(h - (float)ah[i]);
         }
-        // three products per tile, two tiles interleaved
+        // three products per tile, two tiles interleaved; the next pair's B
+        // operands load while the current pair multiplies
         const f16x8* bj = w2s + j * NT * 2 * 64 + lane;
+        f16x8 bv[4] = {bj[0], bj[64], bj[128], bj[192]};
+        sfor<0, NT / 2>([&](auto pc) {
+          constexpr int t = 2 * decltype(pc)::value;
+          f16x8 nb[4];
+          if constexpr (t + 2 < NT) {
 #pragma unroll
-        for (int t = 0; t < NT; t += 2) {
-          const f16x8 bh0 = bj[(2 * t) * 64], bl0 = bj[(2 * t + 1) * 64];
-          const f16x8 bh1 = bj[(2 * t + 2) * 64], bl1 = bj[(2 * t + 3) * 64];
-          D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh0, D[t], 0, 0, 0);
-          D[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh1, D[t + 1], 0, 0, 0);
-          D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl0, D[t], 0, 0, 0);
-          D[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl1, D[t + 1], 0, 0, 0);
-          D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh0, D[t], 0, 0, 0);
-          D[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh1, D[t + 1], 0, 0, 0);
-        }
+            for (int k = 0; k < 4; ++k) nb[k] = bj[(2 * t + 4 + k) * 64];
+          }
+          __builtin_amdgcn_sched_barrier(0);   // the loads stay ahead of the products
+          D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv[0], D[t], 0, 0, 0);
+          D[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv[2], D[t + 1], 0, 0, 0);
+          D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv[1], D[t], 0, 0, 0);
+          D[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv[3], D[t + 1], 0, 0, 0);
+          D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bv[0], D[t], 0, 0, 0);
+          D[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bv[2], D[t + 1], 0, 0, 0);
+          if constexpr (t + 2 < NT) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) bv[k] = nb[k];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
 
       // --- tensor product and mixing of edges e0 + 4q + r, channels n, n + 16;
