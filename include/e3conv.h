@@ -188,7 +188,11 @@ e3conv_status e3conv_forward_masked(e3conv_plan_t plan, e3conv_dtype in_dtype, c
  *   excluded; the cutoff makes their weight vanish at r = r_max.
  * - Compiled for layouts of 32 channels and at most 8 paths (the gate-points
  *   layout) in RECEIVER ordering; other plans give E3CONV_ERR_UNSUPPORTED.
- * - order and num_real_nodes as e3conv_forward_masked. */
+ * - order and num_real_nodes as e3conv_forward_masked.
+ * - Arithmetic: fp32 inputs and outputs at fp32-level accuracy.  The second
+ *   layer's products run as three fp16 matrix products of operands split in
+ *   two fp16 parts, with power-of-two scales chosen from the weights so that
+ *   no finite weight overflows or loses relative precision beyond 2^-22. */
 e3conv_status e3conv_forward_radial(e3conv_plan_t plan, const float* x, const float* y, const float* r,
                                     const float* w1, const float* w2, int32_t num_basis,
                                     int32_t hidden, float r_max, float sigma, const int32_t* src,
