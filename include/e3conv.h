@@ -191,8 +191,8 @@ e3conv_status e3conv_forward_masked(e3conv_plan_t plan, e3conv_dtype in_dtype, c
  * - order and num_real_nodes as e3conv_forward_masked.
  * - Arithmetic: fp32 inputs and outputs at fp32-level accuracy.  The second
  *   layer's products run as three fp16 matrix products of operands split in
- *   two fp16 parts, with power-of-two scales chosen from the weights so that
- *   no finite weight overflows or loses relative precision beyond 2^-22. */
+ *   two fp16 parts, with power-of-two scales chosen from the weights that keep
+ *   every operand inside the fp16 range. */
 e3conv_status e3conv_forward_radial(e3conv_plan_t plan, const float* x, const float* y, const float* r,
                                     const float* w1, const float* w2, int32_t num_basis,
                                     int32_t hidden, float r_max, float sigma, const int32_t* src,

@@ -149,6 +149,35 @@ def test_radial_network_shapes(nb, hidden, sigma):
     assert err <= 1e-5
 
 
+@pytest.mark.parametrize("s1,s2,spread", [(1e-3, 1e5, 0), (30.0, 1e-6, 0), (1.0, 1.0, 6)],
+                         ids=["small-w1-large-w2", "large-w1-small-w2", "channel-spread"])
+def test_radial_weight_scales(s1, s2, spread):
+    """Weights far outside the fp16 range, and channels whose magnitudes differ by up to 1e6:
+    the kernel's power-of-two operand scales must keep fp32-level accuracy."""
+    x, y, r, src, dst, N = handmade([5, 20, 0, 16, 9, 33], seed=11)
+    _, w1, w2 = synth.radial_inputs(synth.make_inputs(1, num_graphs=1))
+    L = lay()
+    w1 = (w1 * s1).astype(np.float32)
+    w2 = (w2 * s2).astype(np.float32)
+    if spread:
+        # channel c of every path scaled by 10^(-spread c / (C - 1))
+        ch = 10.0 ** (-spread * np.arange(L.channels) / (L.channels - 1))
+        w2 = (w2.reshape(w2.shape[0], L.num_paths, L.channels) * ch).reshape(w2.shape).astype(np.float32)
+    ref = radial.forward_radial(L, x, y, r, w1, w2, 2.0, 0.5, src, dst, N)
+    got = run(x, y, r, w1, w2, src, dst, N)
+    err = rel_err(got, ref)
+    say(f"[radial scales] w1 x{s1:g}, w2 x{s2:g}, spread {spread}: max|err|/RMS = {err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= 1e-5
+    if spread:
+        # the smallest channel keeps its own relative accuracy, not just the global one
+        c = L.channels - 1
+        rms_c = math.sqrt(float(np.mean(ref[..., c] ** 2)))
+        err_c = float(np.abs(got[..., c] - ref[..., c]).max()) / rms_c
+        say(f"  channel {c}: max|err|/RMS = {err_c:.3e}")
+        assert err_c <= 1e-5
+
+
 @pytest.mark.parametrize("use_order", [False, True], ids=["index", "clustered"])
 def test_radial_padding_and_order(use_order):
     inp = synth.make_inputs(1, num_graphs=4)
