@@ -515,7 +515,7 @@ e3conv_status e3conv_linear_backward(e3conv_plan_t p, int c_out, float scale, co
       b.C = grad_w;   b.c_i = c_out;   b.c_j = 1;        b.c_comp = 0;  b.c_block = C * c_out;
       b.M = (int)C; b.N = c_out; b.K = (int)N;
       // split the node reduction so the grid has a few thousand work-groups
-      const long tiles = ((C + 63) / 64) * ((c_out + 127) / 128) * NO;
+      const long tiles = ((C + 127) / 128) * ((c_out + 127) / 128) * NO;   // 128 x 128 tiles
       long splits = (4096 + tiles - 1) / tiles;
       const long max_splits = (N + 255) / 256;
       if (splits > max_splits) splits = max_splits;
