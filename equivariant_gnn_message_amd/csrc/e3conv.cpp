@@ -466,6 +466,13 @@ e3conv_status linear_setup(e3conv_plan_t p, int c_out, float scale, int64_t N, e
   return E3CONV_OK;
 }
 
+// out = in W_k and grad_in = grad_out W_k^T: the row-streaming kernel when the
+// weight block fits its LDS tiling (K, N <= 128), else the tiled kernel.
+hipError_t linear_by_rows(const e3c::LinearGemm& g, hipStream_t s) {
+  if (g.K <= 128 && g.N <= 128) return e3c::launch_linear_rows(g, s);
+  return e3c::launch_linear_gemm(g, 1, s);
+}
+
 }  // namespace
 
 e3conv_status e3conv_linear(e3conv_plan_t p, int c_out, float scale, const float* w, const float* in,
@@ -480,7 +487,7 @@ e3conv_status e3conv_linear(e3conv_plan_t p, int c_out, float scale, const float
   g.B = w;    g.b_k = c_out;       g.b_j = 1;  g.b_comp = 0;     g.b_block = C * c_out;
   g.C = out;  g.c_i = NO * c_out;  g.c_j = 1;  g.c_comp = c_out; g.c_block = 0;
   g.M = (int)N; g.N = c_out; g.K = (int)C; g.k_chunk = (int)C;
-  const hipError_t err = e3c::launch_linear_gemm(g, 1, static_cast<hipStream_t>(stream));
+  const hipError_t err = linear_by_rows(g, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "linear launch");
   return ok();
 }
@@ -502,7 +509,7 @@ e3conv_status e3conv_linear_backward(e3conv_plan_t p, int c_out, float scale, co
     a.B = w;        a.b_k = 1;          a.b_j = c_out; a.b_comp = 0; a.b_block = C * c_out;
     a.C = grad_in;  a.c_i = NO * C;     a.c_j = 1;  a.c_comp = C;  a.c_block = 0;
     a.M = (int)N; a.N = (int)C; a.K = c_out; a.k_chunk = c_out;
-    const hipError_t err = e3c::launch_linear_gemm(a, 1, s);
+    const hipError_t err = linear_by_rows(a, s);
     if (err != hipSuccess) return hip_fail(err, "linear backward launch");
   }
   if (grad_w) {
@@ -514,9 +521,10 @@ e3conv_status e3conv_linear_backward(e3conv_plan_t p, int c_out, float scale, co
       b.B = grad_out; b.b_k = NO * c_out; b.b_j = 1;    b.b_comp = c_out; b.b_block = 0;
       b.C = grad_w;   b.c_i = c_out;   b.c_j = 1;        b.c_comp = 0;  b.c_block = C * c_out;
       b.M = (int)C; b.N = c_out; b.K = (int)N;
-      // split the node reduction so the grid has a few thousand work-groups
+      // split the node reduction so the grid has about 512 work-groups (more splits
+      // multiply the atomic additions into grad_w)
       const long tiles = ((C + 127) / 128) * ((c_out + 127) / 128) * NO;   // 128 x 128 tiles
-      long splits = (4096 + tiles - 1) / tiles;
+      long splits = (512 + tiles - 1) / tiles;
       const long max_splits = (N + 255) / 256;
       if (splits > max_splits) splits = max_splits;
       if (splits < 1) splits = 1;

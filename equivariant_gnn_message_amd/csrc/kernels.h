@@ -149,6 +149,9 @@ struct LinearGemm {
 };
 
 hipError_t launch_linear_gemm(const LinearGemm& g, int k_splits, hipStream_t stream);
+// Rows variant for B shared by the components of an irrep block (b_comp == 0),
+// A contiguous along k, K <= 128, N <= 128, stores (no K split).
+hipError_t launch_linear_rows(const LinearGemm& g, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
 
 // Streaming reference kernels (copy when dst != nullptr, else read only).

@@ -203,6 +203,175 @@ __global__ void __launch_bounds__(256) linear_gemm(LinearGemm g) {
       }
 }
 
+// Row-streaming variant for the GEMMs whose B is one weight block shared by all
+// components of an irrep block (out = in W_k and grad_in = grad_out W_k^T: A
+// contiguous along k, K <= 128, N <= 128).  A work-group splits W_k once into
+// LDS (three bf16 planes, 96 KiB at 128 x 128, laid out so that a B operand
+// is 16 contiguous bytes per lane) and its waves stream 16-row tiles of A
+// straight from memory into the A operands (lane (m, q) reads A[m][32 s + 8 q
+// .. + 7], splitting it in registers), the next tile's rows in flight during
+// the current tile's products.  Row tiles are numbered component-major, so a
+// work-group's contiguous range spans few irrep blocks (W_k is restaged at
+// each change).
+constexpr int RW = 8;                     // waves per work-group
+constexpr int RKS = 4, RNT = 8;           // at most 4 K steps of 32, 8 column tiles of 16
+
+// KSC, NTC > 0: K = 32 KSC, N = 16 NTC and A rows 16-byte aligned (checked by
+// the launcher): static loops, one row pointer per tile, rows past M read row
+// M - 1 and are not stored (an output row depends on its own input row only).
+// KSC = NTC = 0: any K, N <= 128 with masked loads and stores.
+template <int KSC, int NTC>
+__global__ void __launch_bounds__(64 * RW) linear_rows(LinearGemm g, int tiles_total, int tiles_per_block,
+                                                         int node_tiles) {
+  __shared__ __attribute__((aligned(16))) bf16x8 Ws[3 * RKS * RNT * 64];   // [plane][s][t][q][n]
+  constexpr bool FIX = KSC > 0;
+  constexpr int PS = RKS * RNT * 64;   // plane size (16-byte units)
+
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int m = lane & 15, q = lane >> 4;
+  const int KS = FIX ? KSC : (g.K + 31) >> 5, NT = FIX ? NTC : (g.N + 15) >> 4;
+  const int t0 = blockIdx.x * tiles_per_block;
+  const int t1 = t0 + tiles_per_block < tiles_total ? t0 + tiles_per_block : tiles_total;
+  const bool a_vec = (g.a_i & 3) == 0 && (g.a_comp & 3) == 0 && (g.K & 7) == 0 &&
+                     (reinterpret_cast<unsigned long>(g.A) & 15) == 0;
+  const bool b_vec = g.b_k == 1 && (g.b_j & 3) == 0 && (g.K & 7) == 0 &&
+                     (reinterpret_cast<unsigned long>(g.B) & 15) == 0 && (g.b_block & 3) == 0;
+
+  // raw rows of a tile: k = 32 s + 8 q + i of row n0 + m
+  auto fetch = [&](int tau, float (&raw)[RKS][8]) {
+    const int o = tau / node_tiles, row = (tau % node_tiles) * 16 + m;
+    const float* Ao = g.A + (long)o * g.a_comp;
+    if constexpr (FIX) {
+      const f32x4* rp = reinterpret_cast<const f32x4*>(Ao + (long)(row < g.M ? row : g.M - 1) * g.a_i + 8 * q);
+#pragma unroll
+      for (int st = 0; st < KSC; ++st) {
+        const f32x4 lo = rp[8 * st], hi = rp[8 * st + 1];
+        raw[st][0] = lo.x; raw[st][1] = lo.y; raw[st][2] = lo.z; raw[st][3] = lo.w;
+        raw[st][4] = hi.x; raw[st][5] = hi.y; raw[st][6] = hi.z; raw[st][7] = hi.w;
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < RKS; ++st) {
+        int n = row < g.M ? g.K - (32 * st + 8 * q) : 0;
+        n = n < 8 ? (n > 0 ? n : 0) : 8;
+        load8(n > 0 ? Ao + (long)row * g.a_i + 32 * st + 8 * q : g.A, 1, n, a_vec && n == 8, raw[st]);
+      }
+    }
+  };
+
+  for (int base = t0; base < t1;) {
+    const int blk = g.comp_block[base / node_tiles];
+    int o_end = base / node_tiles;
+    while (o_end < g.num_comp && g.comp_block[o_end] == blk) ++o_end;
+    const int te = o_end * node_tiles < t1 ? o_end * node_tiles : t1;
+
+    // W_k, split into three planes: unit (s, q, t, n) holds B[32 s + 8 q + i][16 t + n], i < 8
+    __syncthreads();   // the previous block's W is no longer read
+    const float* Bk = g.B + (long)blk * g.b_block;
+    for (int u = threadIdx.x; u < RKS * 4 * RNT * 16; u += 64 * RW) {
+      const int n = u & 15, tt = (u >> 4) & 7, qq = (u >> 7) & 3, st = u >> 9;
+      const int j = 16 * tt + n, k0 = 32 * st + 8 * qq;
+      int cnt = j < g.N ? g.K - k0 : 0;
+      cnt = cnt < 8 ? (cnt > 0 ? cnt : 0) : 8;
+      float v[8];
+      load8(cnt > 0 ? Bk + (long)k0 * g.b_k + (long)j * g.b_j : g.B, g.b_k, cnt, b_vec && cnt == 8, v);
+      bf16x8 p0, p1, p2;
+      split3(v, p0, p1, p2);
+      const int idx = (st * RNT + tt) * 64 + qq * 16 + n;
+      Ws[idx] = p0;
+      Ws[PS + idx] = p1;
+      Ws[2 * PS + idx] = p2;
+    }
+    __syncthreads();
+
+    float raw[RKS][8];
+    int tau = base + wid;
+    if (tau < te) fetch(tau, raw);
+    for (; tau < te; tau += RW) {
+      bf16x8 a0[RKS], a1[RKS], a2[RKS];
+#pragma unroll
+      for (int st = 0; st < RKS; ++st)
+        if (!FIX || st < KSC) split3(raw[st], a0[st], a1[st], a2[st]);
+      if (tau + RW < te) fetch(tau + RW, raw);   // next tile's rows in flight
+
+      f32x4 acc[RNT];
+#pragma unroll
+      for (int tt = 0; tt < RNT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int o = tau / node_tiles, n0 = (tau % node_tiles) * 16;
+      float* Co = g.C + (long)o * g.c_comp + (long)blk * g.c_block;
+      if constexpr (FIX) {
+        // groups of up to four column tiles: four independent products between dependent ones
+        constexpr int GT = NTC < 4 ? NTC : 4;
+#pragma unroll
+        for (int st = 0; st < KSC; ++st)
+#pragma unroll
+          for (int t0g = 0; t0g < NTC; t0g += GT) {
+            bf16x8 b0[GT], b1[GT], b2[GT];
+#pragma unroll
+            for (int u = 0; u < GT; ++u) {
+              const int idx = (st * RNT + t0g + u) * 64 + lane;
+              b0[u] = Ws[idx];
+              b1[u] = Ws[PS + idx];
+              b2[u] = Ws[2 * PS + idx];
+            }
+#pragma unroll
+            for (int u = 0; u < GT; ++u) acc[t0g + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[st], b0[u], acc[t0g + u], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < GT; ++u) acc[t0g + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[st], b1[u], acc[t0g + u], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < GT; ++u) acc[t0g + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[st], b0[u], acc[t0g + u], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < GT; ++u) acc[t0g + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[st], b2[u], acc[t0g + u], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < GT; ++u) acc[t0g + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[st], b1[u], acc[t0g + u], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < GT; ++u) acc[t0g + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2[st], b0[u], acc[t0g + u], 0, 0, 0);
+            // one group's operands at a time (hoisting every group's LDS reads exceeds the registers)
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        // D[4 q + r][n] of column tile tt: row n0 + 4 q + r, column 16 tt + m
+        float* cp = Co + (long)(n0 + 4 * q) * g.c_i + m;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (n0 + 4 * q + r < g.M) {
+#pragma unroll
+            for (int tt = 0; tt < NTC; ++tt) __builtin_nontemporal_store(g.alpha * acc[tt][r], cp + 16 * tt);
+          }
+          cp += g.c_i;
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < RKS; ++st) {
+          if (st >= KS) break;
+#pragma unroll
+          for (int tt = 0; tt < RNT; ++tt) {
+            if (tt >= NT) break;
+            const int idx = (st * RNT + tt) * 64 + lane;
+            const bf16x8 b0 = Ws[idx], b1 = Ws[PS + idx], b2 = Ws[2 * PS + idx];
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[st], b0, acc[tt], 0, 0, 0);
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[st], b1, acc[tt], 0, 0, 0);
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[st], b0, acc[tt], 0, 0, 0);
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[st], b2, acc[tt], 0, 0, 0);
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[st], b1, acc[tt], 0, 0, 0);
+            acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2[st], b0, acc[tt], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int tt = 0; tt < RNT; ++tt) {
+          const int j = 16 * tt + m;
+          if (tt >= NT || j >= g.N) continue;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = n0 + 4 * q + r;
+            if (row < g.M) __builtin_nontemporal_store(g.alpha * acc[tt][r], Co + (long)row * g.c_i + j);
+          }
+        }
+      }
+    }
+    base = te;
+  }
+}
+
 __global__ void linear_fill_zero(float* __restrict__ p, size_t n) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
@@ -215,6 +384,28 @@ hipError_t launch_linear_gemm(const LinearGemm& g, int k_splits, hipStream_t str
   const long gx = (g.M + TM - 1) / TM, gy = (g.N + TN - 1) / TN, gz = (long)g.num_comp * k_splits;
   if (gx > 0x7fffffffL || gy > 65535 || gz > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL(linear_gemm, dim3((unsigned)gx, (unsigned)gy, (unsigned)gz), dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_rows(const LinearGemm& g, hipStream_t stream) {
+  if (g.M <= 0 || g.N <= 0 || g.num_comp <= 0) return hipSuccess;
+  if (g.K > 32 * RKS || g.N > 16 * RNT || g.a_k != 1 || g.c_j != 1 || g.b_comp != 0 || g.atomic)
+    return hipErrorInvalidValue;
+  const long node_tiles = (g.M + 15) / 16, total = node_tiles * g.num_comp;
+  if (total > 0x7fffffffL) return hipErrorInvalidValue;
+  // one work-group per CU holds a W block; ranges of at least a tile per wave
+  long blocks = (total + RW - 1) / RW;
+  if (blocks > 256) blocks = 256;
+  const long per = (total + blocks - 1) / blocks;
+  blocks = (total + per - 1) / per;
+  const bool rows_aligned = (g.a_i & 3) == 0 && (g.a_comp & 3) == 0 &&
+                            (reinterpret_cast<unsigned long>(g.A) & 15) == 0;
+  auto kernel = linear_rows<0, 0>;
+  if (rows_aligned && g.K == 128 && g.N == 128) kernel = linear_rows<4, 8>;
+  else if (rows_aligned && g.K == 64 && g.N == 64) kernel = linear_rows<2, 4>;
+  else if (rows_aligned && g.K == 32 && g.N == 32) kernel = linear_rows<1, 2>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * RW), 0, stream, g, (int)total, (int)per,
+                     (int)node_tiles);
   return hipGetLastError();
 }
 

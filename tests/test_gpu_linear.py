@@ -26,9 +26,11 @@ def icuda(a):
 
 
 @pytest.mark.parametrize("idx,C,Co,N", [(2, 128, 128, 301), (2, 128, 64, 1000), (0, 8, 16, 64),
-                                        (3, 64, 32, 257), (1, 32, 48, 5), (2, 128, 128, 20000)],
+                                        (3, 64, 32, 257), (1, 32, 48, 5), (2, 128, 128, 20000),
+                                        (0, 20, 24, 33), (1, 12, 136, 77), (3, 64, 64, 300),
+                                        (1, 32, 32, 1000)],
                          ids=["mace-301", "mace-64out-1000", "tiny-64", "big-257", "gate-5",
-                              "mace-full"])
+                              "mace-full", "k20-unaligned", "wide-136", "big-64x64", "gate-32x32"])
 def test_linear_parity(idx, C, Co, N):
     import torch
     w = synth.WORKLOADS[idx]
