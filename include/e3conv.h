@@ -272,7 +272,9 @@ e3conv_status e3conv_backward_ex(e3conv_plan_t plan, e3conv_dtype in_dtype, cons
  *            output order, then u, then v);
  *   in       device float (num_nodes, num_out, C), e.g. e3conv_forward's out;
  *   out      device float (num_nodes, num_out, C_out), fully overwritten.
- * fp32 products and sums on the matrix cores; asynchronous on hip_stream.
+ * fp32 products at fp32 accuracy and fp32 sums on the matrix cores (each
+ * operand split into three bf16 parts, six partial products per product);
+ * asynchronous on hip_stream.
  * channels_out > 0, scale finite, num_out <= 128 components, else
  * E3CONV_ERR_INVALID_ARGUMENT / E3CONV_ERR_UNSUPPORTED. */
 e3conv_status e3conv_linear(e3conv_plan_t plan, int channels_out, float scale,
