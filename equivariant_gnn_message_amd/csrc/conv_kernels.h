@@ -696,6 +696,185 @@ __global__ void __launch_bounds__(256) conv_jvp(JvpParams prm) {
   }
 }
 
+// conv_jvp with the edge loop software-pipelined like conv_fwd_pipe: the
+// primal and tangent rows of the next edge are loaded while the current edge
+// is accumulated (the non-pipelined kernel spends most of its time waiting for
+// its loads).
+template <class LY, typename IN, int CPL>
+struct JvpBuf {
+  EdgeBuf<LY, IN, CPL> p, t;   // (x, y, s) and (dx, dy, ds)
+};
+
+template <class LY, typename IN, int CPL>
+__device__ __forceinline__ void jvp_accumulate(const JvpBuf<LY, IN, CPL>& buf, float (&acc)[LY::NO][CPL],
+                                               float (&dacc)[LY::NO][CPL]) {
+  constexpr int NY = LY::NY, NP = LY::NP;
+  float yv[NY], dyv[NY];
+#pragma unroll
+  for (int j = 0; j < NY; ++j) {
+    yv[j] = buf.p.y.get(j);
+    dyv[j] = buf.t.y.get(j);
+  }
+  sfor<0, NP>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    constexpr PathInfo P = LY::T.path[p];
+    constexpr int D1 = 2 * P.l1 + 1, D3 = 2 * P.l3 + 1;
+    float K[D3][D1], dK[D3][D1];
+    build_k<LY, p, D3, D1>(yv, K);
+    build_k<LY, p, D3, D1>(dyv, dK);
+    sfor<0, D3>([&](auto m3c) {
+      constexpr int m3 = decltype(m3c)::value;
+      float t[CPL], dt[CPL];
+      sfor<0, D1>([&](auto m1c) {
+        constexpr int m1 = decltype(m1c)::value;
+        if constexpr (k_nonzero(LY::T, p, m3, m1)) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const float xv = buf.p.x[P.o1 + m1].get(c), dxv = buf.t.x[P.o1 + m1].get(c);
+            if constexpr (first_m1(LY::T, p, m3) == m1) {
+              t[c] = K[m3][m1] * xv;
+              dt[c] = __builtin_fmaf(dK[m3][m1], xv, K[m3][m1] * dxv);
+            } else {
+              t[c] = __builtin_fmaf(K[m3][m1], xv, t[c]);
+              dt[c] = __builtin_fmaf(K[m3][m1], dxv, dt[c]);
+              dt[c] = __builtin_fmaf(dK[m3][m1], xv, dt[c]);
+            }
+          }
+        }
+      });
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float sv = buf.p.s[p].get(c), dsv = buf.t.s[p].get(c);
+        acc[P.o3 + m3][c] = __builtin_fmaf(sv, t[c], acc[P.o3 + m3][c]);
+        dacc[P.o3 + m3][c] = __builtin_fmaf(sv, dt[c], __builtin_fmaf(dsv, t[c], dacc[P.o3 + m3][c]));
+      }
+    });
+  });
+}
+
+// PX: the sender rows (x, dx) are prefetched with the rest; without it they
+// are loaded just before their edge is accumulated (fewer registers).
+template <class LY, typename IN, int CPL, int GPR, bool PX>
+__global__ void __launch_bounds__(256) conv_jvp_pipe(JvpParams prm) {
+  constexpr int C = LY::C, NO = LY::NO;
+  constexpr int LPG = C / CPL;
+  static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
+  constexpr int G = 64 / LPG;
+  static_assert(G % GPR == 0, "groups per receiver must divide groups per wave");
+  constexpr int RPW = G / GPR;
+
+  const IN* __restrict__ x = static_cast<const IN*>(prm.x);
+  const IN* __restrict__ y = static_cast<const IN*>(prm.y);
+  const IN* __restrict__ s = static_cast<const IN*>(prm.s);
+  const IN* __restrict__ dx = static_cast<const IN*>(prm.dx);
+  const IN* __restrict__ dy = static_cast<const IN*>(prm.dy);
+  const IN* __restrict__ ds = static_cast<const IN*>(prm.ds);
+  const int* __restrict__ src = prm.src;
+  const int* __restrict__ row_ptr = prm.row_ptr;
+
+  const int lane = threadIdx.x & 63;
+  const int li = lane % LPG;
+  const int grp = lane / LPG;
+  const int gi = grp % GPR;
+  const int slot = grp / GPR;
+  const int bl = logical_wave() * RPW + slot;
+  const bool valid = bl < prm.num_nodes;
+  const int b = valid ? (prm.order ? prm.order[bl] : bl) : 0;
+  const int c0 = li * CPL;
+
+  float acc[NO][CPL], dacc[NO][CPL];
+#pragma unroll
+  for (int o = 0; o < NO; ++o)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      acc[o][c] = 0.0f;
+      dacc[o][c] = 0.0f;
+    }
+
+  int beg = 0, end = 0;
+  if (valid) {
+    beg = row_ptr[b];
+    end = b < prm.num_real ? row_ptr[b + 1] : beg;
+  }
+
+  constexpr int NX = LY::NX, NY = LY::NY, NP = LY::NP;
+  // the edge's rows: y, dy, s, ds (and x, dx of sender a when PX)
+  auto load = [&](JvpBuf<LY, IN, CPL>& buf, int e, int a) {
+    load_raw<IN, NY, true>(y + (size_t)e * NY, buf.p.y);
+    load_raw<IN, NY, true>(dy + (size_t)e * NY, buf.t.y);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      load_raw<IN, CPL, true>(s + ((size_t)e * NP + p) * C + c0, buf.p.s[p]);
+      load_raw<IN, CPL, true>(ds + ((size_t)e * NP + p) * C + c0, buf.t.s[p]);
+    }
+    if constexpr (PX) {
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        load_raw<IN, CPL, false>(x + ((size_t)a * NX + i) * C + c0, buf.p.x[i]);
+        load_raw<IN, CPL, false>(dx + ((size_t)a * NX + i) * C + c0, buf.t.x[i]);
+      }
+    }
+  };
+  auto load_x = [&](JvpBuf<LY, IN, CPL>& buf, int a) {
+    if constexpr (!PX) {
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        load_raw<IN, CPL, false>(x + ((size_t)a * NX + i) * C + c0, buf.p.x[i]);
+        load_raw<IN, CPL, false>(dx + ((size_t)a * NX + i) * C + c0, buf.t.x[i]);
+      }
+    }
+  };
+  JvpBuf<LY, IN, CPL> b0, b1;
+  int e = beg + gi;
+  int a = e < end ? src[e] : 0;
+  if (e < end) load(b0, e, a);
+  int en = e + GPR;
+  int an = en < end ? src[en] : 0;
+  while (e < end) {
+    load_x(b0, a);
+    if (en < end) load(b1, en, an);
+    int en2 = en + GPR;
+    int an2 = en2 < end ? src[en2] : 0;
+    jvp_accumulate<LY, IN, CPL>(b0, acc, dacc);
+    e = en;
+    a = an;
+    en = en2;
+    an = an2;
+    if (e >= end) break;
+    load_x(b1, a);
+    if (en < end) load(b0, en, an);
+    en2 = en + GPR;
+    an2 = en2 < end ? src[en2] : 0;
+    jvp_accumulate<LY, IN, CPL>(b1, acc, dacc);
+    e = en;
+    a = an;
+    en = en2;
+    an = an2;
+  }
+
+  if constexpr (GPR > 1) {
+#pragma unroll
+    for (int o = 0; o < NO; ++o)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int d = LPG; d < LPG * GPR; d <<= 1) {
+          acc[o][c] += __shfl_xor(acc[o][c], d, 64);
+          dacc[o][c] += __shfl_xor(dacc[o][c], d, 64);
+        }
+  }
+
+  if (valid) {
+    const size_t row = (size_t)b * NO * C + c0;
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+      if (o % GPR != gi) continue;
+      store_row<CPL>(prm.out_dot + row + (size_t)o * C, dacc[o], prm.inv_avg);
+      if (prm.out) store_row<CPL>(prm.out + row + (size_t)o * C, acc[o], prm.inv_avg);
+    }
+  }
+}
+
 // ----------------------------------------------------------- backward -------
 
 // Edges into a padding receiver (node mask) carry no gradient: their grad_y
@@ -1226,6 +1405,16 @@ hipError_t launch_bwd_pipe(const BwdParams& p, hipStream_t st) {
   const long waves = (p.num_nodes + RPW - 1) / RPW;
   const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
   hipLaunchKernelGGL((conv_bwd_pipe<LY, CPL, GPR, GEN>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+template <class LY, typename IN, int CPL, int GPR, bool PX>
+hipError_t launch_jvp_pipe(const JvpParams& p, hipStream_t st) {
+  constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
+  if (p.num_nodes <= 0) return hipSuccess;
+  const long waves = (p.num_nodes + RPW - 1) / RPW;
+  const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
+  hipLaunchKernelGGL((conv_jvp_pipe<LY, IN, CPL, GPR, PX>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

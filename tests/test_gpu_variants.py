@@ -162,13 +162,14 @@ def test_masked_rejects_bad_count():
         plan.forward(x, y, s, src, row_ptr, num_real_nodes=-1)
 
 
-@pytest.mark.parametrize("idx,n,ordering", [(0, None, 0), (1, None, 0), (2, 601, 0), (3, 601, 0),
-                                            (2, 401, 1)],
-                         ids=["w0", "w1", "w2-n601", "w3bf16-n601", "w2-n401-sender"])
-def test_jvp_parity(idx, n, ordering):
+@pytest.mark.parametrize("idx,n,ordering,force_bf", [(0, None, 0, False), (1, None, 0, False),
+                                                     (2, 601, 0, False), (3, 601, 0, False),
+                                                     (2, 401, 1, False), (2, 501, 0, True)],
+                         ids=["w0", "w1", "w2-n601", "w3bf16-n601", "w2-n401-sender", "w2bf16-n501"])
+def test_jvp_parity(idx, n, ordering, force_bf):
     import torch
     inp = synth.make_inputs(idx, num_nodes=n) if n else synth.make_inputs(idx)
-    bf = inp.workload.dtype == "bf16"
+    bf = inp.workload.dtype == "bf16" or force_bf
     lay = lay_of(inp)
     x, y, s = inp.as_f32("x"), inp.as_f32("y"), inp.as_f32("s")
     src, dst, N = inp.senders, inp.receivers, inp.num_nodes
@@ -197,7 +198,9 @@ def test_jvp_parity(idx, n, ordering):
     errs = [rel_err(out.cpu().numpy(), ref), rel_err(out_dot.cpu().numpy(), ref_dot),
             rel_err(only_dot.cpu().numpy(), ref_dot)]
     say(f"  max|err|/RMS out {errs[0]:.3e} out_dot {errs[1]:.3e} (tangent only {errs[2]:.3e})")
-    assert max(errs) <= tolerance(inp)
+    # operands rounded to bf16 on both sides: the kernel adds fp32 rounding only (the
+    # tight bf16 bar of test_gpu_bf16_tight)
+    assert max(errs) <= (2e-4 if force_bf else tolerance(inp))
 
 
 def test_backward_ex_optional_outputs_and_accumulation():
