@@ -55,7 +55,8 @@ __device__ __forceinline__ int radial_lower_bound(const int* row_ptr, int n, lon
   int lo = 0, hi = n;   // the answer lies in [lo, hi]; hi always satisfies the condition
   while (hi - lo >= 64) {
     const int step = (hi - lo + 63) >> 6;
-    const int idx = lo + (lane + 1) * step < hi ? lo + (lane + 1) * step : hi;   // lane 63 samples hi
+    const long cand = lo + (long)(lane + 1) * step;
+    const int idx = cand < hi ? (int)cand : hi;   // lane 63 samples hi
     const unsigned long long m = __ballot((long)row_ptr[idx] + 8L * idx >= v);
     const int k = (int)__builtin_ctzll(m);
     const int nhi = __builtin_amdgcn_readlane(idx, k);

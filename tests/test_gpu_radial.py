@@ -149,6 +149,22 @@ def test_radial_network_shapes(nb, hidden, sigma):
     assert err <= 1e-5
 
 
+def test_radial_graph_without_edges():
+    """No edges at all: every output row is zero (receivers and padding alike)."""
+    import torch
+    L = lay()
+    N = 37
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((N, L.num_x, L.channels)).astype(np.float32)
+    _, w1, w2 = synth.radial_inputs(synth.make_inputs(1, num_graphs=1))
+    empty_i = np.zeros(0, np.int32)
+    y = np.zeros((0, L.num_y), np.float32)
+    r = np.zeros(0, np.float32)
+    got = run(x, y, r, w1, w2, empty_i, empty_i, N)
+    say(f"[radial empty] N={N}: max|out| = {np.abs(got).max():.1e}")
+    assert np.all(got == 0.0)
+
+
 @pytest.mark.parametrize("s1,s2,spread", [(1e-3, 1e5, 0), (30.0, 1e-6, 0), (1.0, 1.0, 6)],
                          ids=["small-w1-large-w2", "large-w1-small-w2", "channel-spread"])
 def test_radial_weight_scales(s1, s2, spread):
