@@ -9,23 +9,25 @@
 //
 // The scalars never reach memory: the (E, NP, C) tensor that would otherwise
 // be written by the network and read back by the convolution is formed per
-// receiver in registers.
+// edge in registers.
 //
-// Per tile of 16 edges of one receiver (one wave):
+// Per tile of 16 edges (one wave): four quads, each up to four consecutive
+// edges of one receiver (quads of different receivers can share a tile):
 // * lane (m, q) = (lane % 16, lane / 16) evaluates the basis for edge m of the
-//   tile and the hidden units u = 32 j + 4 i + q (i < 8) of contraction step j,
-//   which is the A operand of v_mfma_f32_16x16x32_f16 (A[m][8 q + i]);
+//   tile (slot m % 4 of quad m / 4) and the hidden units u = 32 j + 4 i + q
+//   (i < 8) of contraction step j, which is the A operand of
+//   v_mfma_f32_16x16x32_f16 (A[m][8 q + i]);
 // * s (16 edges x NP*C) = h W2 is accumulated over hidden/32 steps in NP*C/16
 //   accumulator tiles, from two-part fp16 operands (fp32-level accuracy, see
 //   the kernel); W2 is staged once per work-group in LDS;
 // * the accumulator layout hands lane (g, n) = (lane / 16, lane % 16) the
-//   scalars of edges 4g .. 4g+3 of the tile for channels n and n + 16 of every
-//   path (column p*C + c lies in tile 2p + c/16), so each lane runs the tensor
-//   product and mixing of its 4 edges for those two channels;
-// * the partial sums of the 4 lane groups are combined with cross-lane
-//   shuffles; a receiver's tiles are summed in registers by the wave that
-//   holds them, or through LDS when neighbouring waves share the receiver,
-//   and each output row is written once.
+//   scalars of edges 4g .. 4g+3 of the tile, i.e. quad g, for channels n and
+//   n + 16 of every path (column p*C + c lies in tile 2p + c/16), so each lane
+//   runs the tensor product and mixing of its quad for those two channels;
+// * the four groups' partial sums are combined per receiver by a segmented
+//   scan across the groups and added to the receiver's row in LDS; a row is
+//   written once, when the receiver's last quad has been added (by the wave
+//   holding its first quad when neighbouring waves share the receiver).
 #pragma once
 
 #include "conv_kernels.h"
@@ -262,15 +264,18 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
   const float center_step = prm.r_max / (float)(NB - 1);
   const float half_turns = 0.5f / prm.r_max;   // cos(pi r / r_max) = cos(2 pi (r / (2 r_max)))
 
-  // Work distribution.  Work-group ranges of receivers are cut at equal
-  // shares of row_ptr[b] + 8 b (edges plus the expected padding of a
-  // receiver's last tile) in index order, at equal receiver counts when a
-  // processing order is given.  Within a work-group the tiles (16 edges of one
-  // receiver) are split evenly over the 8 waves, so a receiver can be shared
-  // by neighbouring waves: each wave writes the receivers it holds entirely,
-  // keeps the partial rows of its first and last receiver in LDS when they
-  // continue in another wave, and after a barrier the wave holding the first
-  // part of such a receiver adds the others' parts and writes the row.
+  // Work distribution.  The unit of work is a quad: up to four consecutive
+  // edges of one receiver (a receiver of d edges has ceil(d / 4) quads), and a
+  // tile is four consecutive quads, one per lane group, possibly of different
+  // receivers.  Work-group ranges of receivers are cut at equal shares of
+  // row_ptr[b] + 8 b in index order (edges plus a margin per receiver), at
+  // equal receiver counts when a processing order is given.  Within a
+  // work-group the tiles are split evenly over the 8 waves, so a receiver can
+  // be shared by neighbouring waves: each wave writes the receivers it holds
+  // entirely, keeps the partial rows of its first and last receiver in LDS
+  // when they continue in another wave, and after a barrier the wave holding
+  // the first part of such a receiver adds the others' parts and writes the
+  // row.
   const int N = prm.num_nodes;
   const int nblk = (int)gridDim.x;
   const int blk = (int)(blockIdx.x & 7) * (nblk >> 3) + (int)(blockIdx.x >> 3);   // XCD-contiguous
@@ -292,70 +297,74 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
     beg = prm.row_ptr[b];
     end = b < prm.num_real ? prm.row_ptr[b + 1] : beg;
   };
-  // tiles of the receivers at positions c0 + lane (< B1), their inclusive prefix
-  // within the chunk, and the chunk's total
-  auto chunk = [&](int c0, int& nt, int& incl) {
-    nt = 0;
-    if (c0 + lane < B1) {
-      int bb, bg, en;
-      recv(c0 + lane, bb, bg, en);
-      nt = (en - bg + 15) >> 4;
-    }
-    int v = nt;
+  auto wave_scan = [&](int v) {   // inclusive prefix sum over the wave's lanes
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int t = __shfl_up(v, d, 64);
       if (lane >= d) v += t;
     }
-    incl = v;
-    return __builtin_amdgcn_readlane(v, 63);
+    return v;
   };
-  int nt0, incl0;
-  int T = chunk(B0, nt0, incl0);
+  // quads of the receivers at positions c0 + lane (< B1), their inclusive
+  // prefix within the chunk, and the chunk's total
+  auto chunk = [&](int c0, int& nu, int& incl) {
+    nu = 0;
+    if (c0 + lane < B1) {
+      int bb, bg, en;
+      recv(c0 + lane, bb, bg, en);
+      nu = (en - bg + 3) >> 2;
+    }
+    incl = wave_scan(nu);
+    return __builtin_amdgcn_readlane(incl, 63);
+  };
+  int nu0, incl0;
+  int Q = chunk(B0, nu0, incl0);
   for (int c0 = B0 + 64; c0 < B1; c0 += 64) {
     int a, c;
-    T += chunk(c0, a, c);
+    Q += chunk(c0, a, c);
   }
-  // first position i with (tiles up to and including i) >= v, for 1 <= v <= T:
-  // the receiver holding tile v - 1; also its inclusive prefix and tile count
-  auto locate = [&](int v, int& at, int& a_incl, int& a_nt) {
+  // first position i with (quads up to and including i) >= v, for 1 <= v <= Q:
+  // the receiver holding quad v - 1; also its inclusive prefix and quad count
+  auto locate = [&](int v, int& at, int& a_incl, int& a_nu) {
     unsigned long long m = __ballot(B0 + lane < B1 && incl0 >= v);
     if (m) {
       const int k = (int)__builtin_ctzll(m);
       at = B0 + k;
       a_incl = __builtin_amdgcn_readlane(incl0, k);
-      a_nt = __builtin_amdgcn_readlane(nt0, k);
+      a_nu = __builtin_amdgcn_readlane(nu0, k);
       return;
     }
     int R = __builtin_amdgcn_readlane(incl0, 63);
     for (int c0 = B0 + 64; c0 < B1; c0 += 64) {
-      int nt, incl;
-      const int tot = chunk(c0, nt, incl);
+      int nu, incl;
+      const int tot = chunk(c0, nu, incl);
       m = __ballot(c0 + lane < B1 && R + incl >= v);
       if (m) {
         const int k = (int)__builtin_ctzll(m);
         at = c0 + k;
         a_incl = R + __builtin_amdgcn_readlane(incl, k);
-        a_nt = __builtin_amdgcn_readlane(nt, k);
+        a_nu = __builtin_amdgcn_readlane(nu, k);
         return;
       }
       R += tot;
     }
     at = B1;
     a_incl = R;
-    a_nt = 0;
+    a_nu = 0;
   };
-  // this wave's tiles [ts, te) of the work-group's T; positions [p_lo, p_hi) it
-  // visits (with the receivers without tiles that lie between its tiles and the
-  // previous wave's), P = tiles before p_lo
-  const int ts = (int)((long)T * wid / kRadialWaves), te = (int)((long)T * (wid + 1) / kRadialWaves);
+  // this wave's tiles [ts, te) of the work-group's TT, i.e. quads [us, ue);
+  // positions [p_lo, p_hi) it visits (with the receivers without quads that
+  // lie between its quads and the previous wave's), P = quads before p_lo
+  const int TT = (Q + 3) >> 2;
+  const int ts = (int)((long)TT * wid / kRadialWaves), te = (int)((long)TT * (wid + 1) / kRadialWaves);
+  const int us = 4 * ts, ue = 4 * te < Q ? 4 * te : Q;
   int p_lo = B0, P = 0;
-  if (ts > 0) {
+  if (us > 0) {
     int at, ai, an;
-    locate(ts, at, ai, an);
-    if (ai == ts) {
+    locate(us, at, ai, an);
+    if (ai == us) {
       p_lo = at + 1;
-      P = ts;
+      P = us;
     } else {
       p_lo = at;
       P = ai - an;
@@ -364,65 +373,151 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
   int p_hi;
   if (wid == kRadialWaves - 1) {
     p_hi = B1;
-  } else if (te == ts) {
+  } else if (ue == us) {
     p_hi = p_lo;
   } else {
     int at, ai, an;
-    locate(te, at, ai, an);
+    locate(ue, at, ai, an);
     p_hi = at + 1;
   }
+
+  // Partial rows are accumulated in this wave's two LDS slots: slot 0 for a
+  // receiver that began in an earlier wave (only the wave's first can), slot
+  // 1 for the others (cleared after each is written out; the last one is kept
+  // there when it continues in a later wave).
+  float* slot0 = part + (wid * 2) * (NO * C);
+  float* slot1 = slot0 + NO * C;
+  for (int idx = lane; idx < 2 * NO * C; idx += 64) slot0[idx] = 0.0f;
   if (lane == 0) part_flags[wid] = 0;
 
-  // The edge length and the four sender indices a lane needs for a tile are
-  // fetched one tile ahead (across receiver boundaries), so that neither the
-  // network nor the gathers of a tile wait for them.
-  // Lane (q, n) holds those of edge e0 + n; the senders of its own four edges
-  // (e0 + 4 q + i) are taken from lanes 4 q + i of its row when needed.
-  auto tile_ids = [&](int e0, int end, float& rv, int& sv) {
-    const int e = e0 + n < end ? e0 + n : end - 1;
-    rv = prm.r[e];
-    sv = prm.src[e];
+  // Window of up to 64 receivers in lanes: lane k holds position wstart + k
+  // (< p_hi): node, edge range, quad count and inclusive quad prefix; WU =
+  // quads before wstart.  Loading a window writes the zero rows of its
+  // receivers without quads.
+  int wstart = p_lo, WU = P;
+  int w_b = 0, w_beg = 0, w_end = 0, w_incl = 0, w_tot = 0;
+  auto load_window = [&]() {
+    const int pos = wstart + lane;
+    w_b = 0;
+    w_beg = 0;
+    w_end = 0;
+    if (pos < p_hi) recv(pos, w_b, w_beg, w_end);
+    w_incl = wave_scan((w_end - w_beg + 3) >> 2);
+    w_tot = __builtin_amdgcn_readlane(w_incl, 63);
+    unsigned long long zm = __ballot(pos < p_hi && w_end == w_beg);
+    while (zm) {
+      const int k = (int)__builtin_ctzll(zm);
+      zm &= zm - 1;
+      float* zrow = prm.out + (size_t)__builtin_amdgcn_readlane(w_b, k) * NO * C;
+      for (int idx = lane; idx < NO * C; idx += 64) __builtin_nontemporal_store(0.0f, zrow + idx);
+    }
+  };
+  if (p_lo < p_hi) load_window();
+
+  // Quad U (us <= U < ue): its receiver's node, first edge and edge count, and
+  // the receiver's first and last quads (absolute indices in the work-group).
+  struct Quad {
+    int b, es, c, first, last;
+  };
+  auto describe = [&](int U) {
+    Quad d = {0, 0, 0, 0, 0};
+    if (U >= ue) return d;
+    unsigned long long m = __ballot(wstart + lane < p_hi && WU + w_incl > U);
+    while (!m && wstart + 64 < p_hi) {   // past the window: the next one
+      WU += w_tot;
+      wstart += 64;
+      load_window();
+      m = __ballot(wstart + lane < p_hi && WU + w_incl > U);
+    }
+    if (!m) return d;   // not reached: every quad below ue lies before p_hi
+    const int k = (int)__builtin_ctzll(m);
+    const int beg = __builtin_amdgcn_readlane(w_beg, k), end = __builtin_amdgcn_readlane(w_end, k);
+    const int nu = (end - beg + 3) >> 2;
+    d.b = __builtin_amdgcn_readlane(w_b, k);
+    d.first = WU + __builtin_amdgcn_readlane(w_incl, k) - nu;
+    d.last = d.first + nu - 1;
+    d.es = beg + 4 * (U - d.first);
+    const int rem = end - d.es;
+    d.c = rem < 4 ? rem : 4;
+    return d;
+  };
+
+  // The edge length and sender index of a lane's A-operand edge (slot m & 3 of
+  // the tile's quad m >> 2; the last edge of that quad for empty slots) are
+  // fetched one tile ahead, so that neither the network nor the gathers wait
+  // for them; the senders of a group's four edges are taken from lanes 4 q + i
+  // of its row when needed.
+  auto pick_es = [&](const Quad (&qd)[4], int g) {
+    return g == 0 ? qd[0].es : g == 1 ? qd[1].es : g == 2 ? qd[2].es : qd[3].es;
+  };
+  auto pick_c = [&](const Quad (&qd)[4], int g) {
+    return g == 0 ? qd[0].c : g == 1 ? qd[1].c : g == 2 ? qd[2].c : qd[3].c;
+  };
+  auto tile_ids = [&](const Quad (&qd)[4], float& rv, int& sv) {
+    const int g = n >> 2, slot = n & 3;
+    const int c = pick_c(qd, g);
+    if (c > 0) {
+      const int e = pick_es(qd, g) + (slot < c ? slot : c - 1);
+      rv = prm.r[e];
+      sv = prm.src[e];
+    } else {
+      rv = 0.0f;
+      sv = 0;
+    }
   };
   auto sender = [&](int sv, int i) { return __shfl(sv, (lane & 48) | (4 * q + i), 64); };
-  int b = 0, beg = 0, end = 0;
+
+  // Writing out a receiver's partial row held in a slot: the whole row when
+  // it lies entirely in this wave, else kept for the fixup after the barrier.
+  auto finish = [&](const Quad& rq) {
+    const bool open_start = rq.first < us, open_end = rq.last >= ue;
+    if (open_start) {   // slot 0: began in an earlier wave
+      if (lane == 0) part_flags[wid] |= open_end ? 5 : 1;
+    } else if (open_end) {   // slot 1: continues in a later wave
+      if (lane == 0) {
+        part_flags[wid] |= 2;
+        part_recv[wid] = rq.b;
+      }
+    } else {
+      float* orow = prm.out + (size_t)rq.b * NO * C;
+      for (int idx = lane; idx < NO * C; idx += 64) {
+        __builtin_nontemporal_store(slot1[idx] * (prm.inv_avg * chsc[idx % C]), orow + idx);
+        slot1[idx] = 0.0f;
+      }
+    }
+  };
+
+  Quad cur[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) cur[g] = describe(us + g);
   float r_cur = 0.0f;
   int s_cur = 0;
-  if (p_lo < p_hi) {
-    recv(p_lo, b, beg, end);
-    const int t0 = ts > P ? ts - P : 0;
-    if (beg + 16 * t0 < end) tile_ids(beg + 16 * t0, end, r_cur, s_cur);
-  }
+  if (us < ue) tile_ids(cur, r_cur, s_cur);
+  Quad run = {-1, 0, 0, 0, 0};   // receiver whose partial row is accumulating
+  float* run_slot = slot1;
 
-  for (int i = p_lo; i < p_hi; ++i) {
-    const bool more = i + 1 < p_hi;
-    int bn = 0, begn = 0, endn = 0;
-    if (more) recv(i + 1, bn, begn, endn);
-    const int nt = (end - beg + 15) >> 4;
-    const int tlo = ts > P ? ts - P : 0;
-    const int thi = te - P < nt ? te - P : nt;
-    P += nt;
+  for (int t = ts; t < te; ++t) {
+    Quad nxt[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) nxt[g] = describe(4 * (t + 1) + g);
+    float r_next = 0.0f;
+    int s_next = 0;
+    if (t + 1 < te) tile_ids(nxt, r_next, s_next);
+
+    // this group's quad: edges es_q .. es_q + c_q - 1
+    const int es_q = pick_es(cur, q), c_q = pick_c(cur, q);
+    // rows of this lane's first two edges, in flight during the network
+    RadialRows<LY> ra, rb;
+    const int a0 = sender(s_cur, 0), a1 = sender(s_cur, 1);
+    if (c_q > 0) radial_load<LY>(ra, prm, es_q, a0, n);
+    if (c_q > 1) radial_load<LY>(rb, prm, es_q + 1, a1, n);
 
     float acc[NO][2];
 #pragma unroll
     for (int o = 0; o < NO; ++o) acc[o][0] = acc[o][1] = 0.0f;
 
-    const int e_stop = beg + 16 * thi;
-    for (int e0 = beg + 16 * tlo; e0 < e_stop; e0 += 16) {
-      float r_next = 0.0f;
-      int s_next = 0;
-      if (e0 + 16 < e_stop) {
-        tile_ids(e0 + 16, end, r_next, s_next);
-      } else if (more && begn < endn) {
-        tile_ids(begn, endn, r_next, s_next);
-      }
-      // rows of this lane's first two edges, in flight during the network
-      const int eq = e0 + 4 * q;
-      RadialRows<LY> ra, rb;
-      const int a0 = sender(s_cur, 0), a1 = sender(s_cur, 1), a2 = sender(s_cur, 2), a3 = sender(s_cur, 3);
-      if (eq < end) radial_load<LY>(ra, prm, eq, a0, n);
-      if (eq + 1 < end) radial_load<LY>(rb, prm, eq + 1, a1, n);
 
-      // --- radial basis of edge e0 + n
+      // --- radial basis of this lane's edge (A-operand role)
       const float rr = r_cur;
       const float cut = 0.5f * (1.0f + __cosf(6.283185307179586f * (rr * half_turns)));
       float f[kRadialMaxBasis];
@@ -486,8 +581,8 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
         });
       }
 
-      // --- tensor product and mixing of edges e0 + 4q + r, channels n, n + 16;
-      // the rows of edge r + 2 load while edge r is processed
+      // --- tensor product and mixing of the group's quad (edges es_q + r), channels n,
+      // n + 16; the rows of edge r + 2 load while edge r is processed
       auto edge = [&](const RadialRows<LY>& R, int r) {
         float sv[NP][2];
 #pragma unroll
@@ -502,61 +597,69 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
         }
         radial_edge<LY>(yv, R.x, sv, acc);
       };
-      if (eq < end) {
+      // senders of edges 2 and 3 (lanes of the same row share c_q, so the
+      // source lanes of the shuffles are active)
+      if (c_q > 0) {
         edge(ra, 0);
-        if (eq + 2 < end) radial_load<LY>(ra, prm, eq + 2, a2, n);
+        if (c_q > 2) radial_load<LY>(ra, prm, es_q + 2, sender(s_cur, 2), n);
       }
-      if (eq + 1 < end) {
+      if (c_q > 1) {
         edge(rb, 1);
-        if (eq + 3 < end) radial_load<LY>(rb, prm, eq + 3, a3, n);
+        if (c_q > 3) radial_load<LY>(rb, prm, es_q + 3, sender(s_cur, 3), n);
       }
-      if (eq + 2 < end) edge(ra, 2);
-      if (eq + 3 < end) edge(rb, 3);
-      r_cur = r_next;
-      s_cur = s_next;
-    }
+      if (c_q > 2) edge(ra, 2);
+      if (c_q > 3) edge(rb, 3);
 
-    // the four lane groups hold partial sums of different edges
+    // Combine the groups' partial sums per receiver: a segmented inclusive
+    // scan over the four groups (quads of one receiver are contiguous), after
+    // which the last group of each receiver's run in this tile holds the run's
+    // sum; that group adds it to the receiver's row in LDS (lane (q, n): its
+    // channels n and n + 16).  A receiver's row is written out when a quad of
+    // another receiver follows it.
+    {
+      const int bq = q == 0 ? cur[0].b : q == 1 ? cur[1].b : q == 2 ? cur[2].b : cur[3].b;
+      const bool s1 = q >= 1 && (q == 1 ? cur[0].b : q == 2 ? cur[1].b : cur[2].b) == bq;
+      const bool s2 = q >= 2 && (q == 2 ? cur[0].b : cur[1].b) == bq;
 #pragma unroll
-    for (int o = 0; o < NO; ++o)
+      for (int o = 0; o < NO; ++o)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        acc[o][c] += __shfl_xor(acc[o][c], 16, 64);
-        acc[o][c] += __shfl_xor(acc[o][c], 32, 64);
+        for (int c = 0; c < 2; ++c) {
+          const float t1 = __shfl_up(acc[o][c], 16, 64);
+          acc[o][c] += s1 ? t1 : 0.0f;
+          const float t2 = __shfl_up(acc[o][c], 32, 64);
+          acc[o][c] += s2 ? t2 : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (cur[g].c == 0) continue;
+      if (cur[g].b != run.b) {
+        if (run.b >= 0) finish(run);
+        run = cur[g];
+        run_slot = run.first < us ? slot0 : slot1;
       }
-    if (tlo == 0 && thi == nt) {
-      float* orow = prm.out + (size_t)b * NO * C;
-      const float sc0 = prm.inv_avg * chsc[n], sc1 = prm.inv_avg * chsc[n + 16];
+      const bool seg_end = g == 3 || cur[g + 1].c == 0 || cur[g + 1].b != cur[g].b;
+      if (seg_end && q == g) {
 #pragma unroll
-      for (int o = 0; o < NO; ++o) {
-        if ((o & 3) != q) continue;
-        __builtin_nontemporal_store(acc[o][0] * sc0, orow + o * C + n);
-        __builtin_nontemporal_store(acc[o][1] * sc1, orow + o * C + n + 16);
-      }
-    } else {
-      // shared with a neighbouring wave: slot 0 holds a receiver that began in
-      // an earlier wave, slot 1 one that continues in a later wave
-      const int slot = tlo > 0 ? 0 : 1;
-      float* prow = part + (wid * 2 + slot) * (NO * C);
-#pragma unroll
-      for (int o = 0; o < NO; ++o) {
-        if ((o & 3) != q) continue;
-        prow[o * C + n] = acc[o][0];
-        prow[o * C + n + 16] = acc[o][1];
-      }
-      if (lane == 0) {
-        part_flags[wid] |= slot == 0 ? (thi < nt ? 5 : 1) : 2;
-        if (slot == 1) part_recv[wid] = b;
+        for (int o = 0; o < NO; ++o) {
+          run_slot[o * C + n] += acc[o][0];
+          run_slot[o * C + n + 16] += acc[o][1];
+        }
       }
     }
-    if (more) {
-      // after a receiver without tiles here the next one's first tile was not fetched
-      if (tlo == thi && begn < endn) tile_ids(begn, endn, r_cur, s_cur);
-      b = bn;
-      beg = begn;
-      end = endn;
-    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) cur[g] = nxt[g];
+    r_cur = r_next;
+    s_cur = s_next;
   }
+  if (run.b >= 0) finish(run);
+  // receivers without quads after this wave's last one (up to p_hi)
+  while (wstart + 64 < p_hi) {
+    WU += w_tot;
+    wstart += 64;
+    load_window();
+  }
+
 
   // Receivers shared between waves: the wave holding the first part adds the
   // parts of the following waves (waves without tiles hold none) up to the one
