@@ -9,7 +9,8 @@
 // and its reverse is two more GEMMs:
 //     grad_in[:, o, :] = alpha * grad_out[:, o, :] @ W_k^T,
 //     grad_W_k        += alpha * in[:, o, :]^T @ grad_out[:, o, :]  (summed over o in block k).
-// One tiled kernel serves all three through element strides: 128 x 128 output
+// A tiled kernel serves all three through element strides (the row-streaming
+// kernel further down takes out and grad_in when K, N <= 128): 128 x 128 output
 // tiles per work-group of four waves (128 columns cover C_out <= 128 in one
 // tile, so each input row is read from memory once; 128 rows share each read
 // and split of B), 32-deep K chunks, each wave a 64 x 64 quadrant of 4 x 4
