@@ -124,6 +124,46 @@ __global__ void __launch_bounds__(256) linear_gemm(LinearGemm g) {
   }
   const bool b_vec = b_kc && (g.b_j & 3) == 0 && ((reinterpret_cast<unsigned long>(B) & 15) == 0);
 
+  // Full tiles whose operands are contiguous across rows/columns and strided
+  // along k (grad_W: A = in^T, B = grad_out over the node axis): threads
+  // 0..127 read A, 128..255 read B, each eight 16-byte rows (four rows or
+  // columns at eight consecutive k), which are four staging units.
+  const bool kt = g.a_i == 1 && g.b_j == 1 && (g.a_k & 3) == 0 && (g.b_k & 3) == 0 &&
+                  (reinterpret_cast<unsigned long>(A) & 15) == 0 && (reinterpret_cast<unsigned long>(B) & 15) == 0 &&
+                  i0 + TM <= g.M && j0 + TN <= g.N;
+  const int kt_c4 = t & 31, kt_r = (t >> 5) & 3;   // 4 rows/columns from 4 kt_c4, k run kt_r
+  const float* kt_p = t < 128 ? A + (long)(i0 + 4 * kt_c4) : B + (long)(j0 + 4 * kt_c4);
+  const long kt_s = t < 128 ? g.a_k : g.b_k;
+  f32x4 kraw[8];
+  int kt_n = 0;
+  auto fetch_kt = [&](int k0) {
+    int n = kend - (k0 + 8 * kt_r);
+    kt_n = n < 8 ? (n > 0 ? n : 0) : 8;
+    const float* p = kt_p + (long)(k0 + 8 * kt_r) * kt_s;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kraw[i] = *reinterpret_cast<const f32x4*>(i < kt_n ? p + i * kt_s : kt_p);
+  };
+  auto stage_kt = [&]() {
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = i < kt_n ? kraw[i][c4] : 0.0f;
+      bf16x8 p0, p1, p2;
+      split3(v, p0, p1, p2);
+      const int row = 4 * kt_c4 + c4;
+      if (t < 128) {
+        As[0][row][kt_r] = p0;
+        As[1][row][kt_r] = p1;
+        As[2][row][kt_r] = p2;
+      } else {
+        Bs[0][row][kt_r] = p0;
+        Bs[1][row][kt_r] = p1;
+        Bs[2][row][kt_r] = p2;
+      }
+    }
+  };
+
   float ra[2][8], rb[2][8];
   auto fetch = [&](int k0) {
     const bool full = k0 + TK <= kend;
@@ -158,11 +198,18 @@ __global__ void __launch_bounds__(256) linear_gemm(LinearGemm g) {
       Bs[2][ub_j[r]][ub_c[r]] = p2;
     }
   };
-  if (kbeg < kend) fetch(kbeg);
+  if (kbeg < kend) {
+    if (kt) fetch_kt(kbeg);
+    else fetch(kbeg);
+  }
   for (int k0 = kbeg; k0 < kend; k0 += TK) {
-    stage();
+    if (kt) stage_kt();
+    else stage();
     __syncthreads();
-    if (k0 + TK < kend) fetch(k0 + TK);
+    if (k0 + TK < kend) {
+      if (kt) fetch_kt(k0 + TK);
+      else fetch(k0 + TK);
+    }
     // A[m][8 q + i] and B[8 q + i][n] of lane (q, m or n) = (lk, lr)
     bf16x8 av[3][MT], bv[3][NTW];
 #pragma unroll
