@@ -626,10 +626,11 @@ def bench_radial(args):
     unfused_ms = _timed(unfused, args.steps, args.warmup)
     nb, hid = w1.shape
     flops = 2.0 * Ec * (nb * hid + hid * P * C)
-    # second-layer matrix work as issued: tiles of 16 edges of one receiver, hidden units padded
-    # to steps of 32, three fp16 products per fp32 product
+    # second-layer matrix work as issued: tiles of four quads (up to four edges of one receiver;
+    # per-work-group rounding of the tile count ignored), hidden units padded to steps of 32,
+    # three fp16 products per fp32 product
     deg = np.bincount(inp.receivers, minlength=N)
-    issued = 3 * 2.0 * 16 * (-(-hid // 32) * 32) * P * C * float(np.sum((deg + 15) // 16))
+    issued = 3 * 2.0 * 16 * (-(-hid // 32) * 32) * P * C * float(np.sum((deg + 3) // 4)) / 4
     tf = flops / (fused_ms * 1e-3) / 1e12
     # compulsory bytes: per edge y, r and the sender index; per node x, out and row_ptr
     byt = 4.0 * (Ec * ((w.lmax + 1) ** 2 + 2) + N * (w.num_x + w.num_out) * C + N + 1)
