@@ -28,6 +28,10 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, AMD published
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix, AMD published
 PEAK_FP16_MFMA_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix, AMD published
+# Vector fp32 FMA without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x
+# 2.4 GHz (a wave-64 instruction occupies its SIMD for four cycles).  The
+# published 157.3 TFLOP/s counts packed FP32, which this build does not emit.
+PEAK_FP32_VALU_TFLOPS = 78.6
 METRIC = "edges/sec + achieved HBM GB/s (% of peak) for fused TP conv fwd/bwd, 1 MI355X"
 
 
@@ -127,6 +131,46 @@ def alg_bytes(w, N, E, b_in):
     fwd = N * nx * C * b_in + E * (ny * b_in + P * C * b_in + 4) + 4 * (N + 1) + N * no * C * 4
     bwd = 4 * (2 * N * nx * C + N * no * C + (N + 1) + E * (2 * ny + 2 * P * C + 1))
     return fwd, bwd
+
+
+def _conv_counts(plan):
+    import numpy as np
+    ix, iy, ip, io, v = (np.asarray(a) for a in plan.coefficients())
+    nz = v != 0
+    nnz = int(nz.sum())
+    nnz_k = len(set(zip(ip[nz].tolist(), ix[nz].tolist(), io[nz].tolist())))
+    smul = sum(min(2 * q["l1"] + 1, 2 * q["l3"] + 1) for q in plan.paths())
+    return nnz, nnz_k, smul
+
+
+def forward_flops_per_edge(plan):
+    """Arithmetic the forward needs per edge with K^p(y) built once per edge:
+    2 flops per CG term for K, then per channel one product per nonzero of
+    each K^p and min(2 l1 + 1, 2 l3 + 1) products for the scalar s (applied
+    before or after K, whichever is smaller)."""
+    nnz, nnz_k, smul = _conv_counts(plan)
+    return 2 * nnz + 2 * plan.channels * (nnz_k + smul)
+
+
+def jvp_flops_per_edge(plan):
+    """Forward mode: K(y) and K(dy) per edge; per channel K(y)(s x),
+    K(y)(s dx + ds x) and K(dy)(s x)."""
+    nnz, nnz_k, smul = _conv_counts(plan)
+    return 4 * nnz + 6 * plan.channels * (nnz_k + smul)
+
+
+def roofline(kernel, ms, nbytes, flops=None, traffic=None):
+    """The roof of a kernel is HBM unless its arithmetic at the vector-ALU
+    peak takes longer than its bytes at the HBM peak (above the ridge)."""
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    r = {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+         "frac": gbps / PEAK_HBM_GBPS, "traffic": traffic, "kernel": kernel, "algorithmic_bytes": nbytes}
+    if flops and flops / PEAK_FP32_VALU_TFLOPS / 1e12 > nbytes / PEAK_HBM_GBPS / 1e9:
+        tf = flops / (ms * 1e-3) / 1e12
+        r.update({"bound": "alu", "achieved": tf, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                  "frac": tf / PEAK_FP32_VALU_TFLOPS, "algorithmic_flops": flops,
+                  "hbm_GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS})
+    return r
 
 
 def kernel_source_files():
@@ -361,10 +405,11 @@ def main():
         res["bwd_hbm_frac"] = res["bwd_hbm_GBps"] / PEAK_HBM_GBPS
         res["step_hbm_frac"] = (fwd_bytes + bwd_bytes) / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS
         kernel, kbytes, kms = "conv_bwd", bwd_bytes, bwd_ms
-    achieved = kbytes / (kms * 1e-3) / 1e9
-    res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                       "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic_from_profiles(kernel, args.workload),
-                       "kernel": kernel, "algorithmic_bytes": kbytes}
+    fwd_flops = forward_flops_per_edge(plan) * Ecount
+    res["fwd_alg_flops"] = fwd_flops
+    res["fwd_valu_TFLOPs"] = fwd_flops / (fwd_ms * 1e-3) / 1e12
+    res["roofline"] = roofline(kernel, kms, kbytes, fwd_flops if kernel == "conv_fwd" else None,
+                               traffic_from_profiles(kernel, args.workload))
     if not args.no_cpu_baseline:
         base, ref_rows, nrows = cpu_baseline(inp, args.cpu_sample_edges, w.backward)
         res["cpu_baseline"] = base
@@ -522,9 +567,8 @@ def bench_mode(args):
         res[f"{k}_hbm_GBps"] = by / (ms * 1e-3) / 1e9
         res[f"{k}_hbm_frac"] = by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS
     k, (ms, by) = max(kernels.items(), key=lambda kv: kv[1][0])
-    res["roofline"] = {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS,
-                       "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, "traffic": None,
-                       "kernel": k, "algorithmic_bytes": by}
+    flops = {"forward": forward_flops_per_edge(plan) * Ec, "jvp": jvp_flops_per_edge(plan) * Ec}
+    res["roofline"] = roofline(k, ms, by, flops.get(k))
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_mode(args.mode, inp, args.cpu_sample_edges)
     print(json.dumps(res), flush=True)
 
