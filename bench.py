@@ -11,7 +11,9 @@ plan and the receiver CSR are built once per graph, outside the timed region
 
 Prints one JSON line: edges/s of whole steps, plus the roofline of the
 dominant kernel (algorithmic bytes / average duration from HIP events on the
-launch stream) and the CPU oracle timed on a bounded sample.
+launch stream, against HBM; algorithmic flops against the vector-ALU peak
+when the kernel's arithmetic intensity is above the ridge point) and the CPU
+oracle timed on a bounded sample.
 """
 
 import argparse
