@@ -465,7 +465,12 @@ __device__ __forceinline__ void edge_accumulate(const EdgeBuf<LY, IN, CPL>& buf,
   });
 }
 
-template <class LY, typename IN, int CPL, int GPR>
+// UL: the sender index two edges ahead and the next edge's rows are loaded
+// unconditionally, clamped to the receiver's last edge past its end (a
+// conditional load, merged into the loop variable, makes the compiler wait
+// for every load in flight, the next edge's rows included). Which form is
+// faster depends on the layout.
+template <class LY, typename IN, int CPL, int GPR, bool UL = false>
 __global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm) {
   constexpr int C = LY::C, NO = LY::NO;
   constexpr int LPG = C / CPL;
@@ -508,17 +513,28 @@ __global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm) {
   int en = e + GPR;
   int an = en < end ? src[en] : 0;
   while (e < end) {
-    if (en < end) load_edge<LY, IN, CPL>(b1, x, y, s, en, an, c0);
     int en2 = en + GPR;
-    int an2 = en2 < end ? src[en2] : 0;
+    int an2;
+    if constexpr (UL) {
+      an2 = src[en2 < end ? en2 : end - 1];
+      load_edge<LY, IN, CPL>(b1, x, y, s, en < end ? en : end - 1, an, c0);
+    } else {
+      if (en < end) load_edge<LY, IN, CPL>(b1, x, y, s, en, an, c0);
+      an2 = en2 < end ? src[en2] : 0;
+    }
     edge_accumulate<LY, IN, CPL>(b0, acc);
     e = en;
     en = en2;
     an = an2;
     if (e >= end) break;
-    if (en < end) load_edge<LY, IN, CPL>(b0, x, y, s, en, an, c0);
     en2 = en + GPR;
-    an2 = en2 < end ? src[en2] : 0;
+    if constexpr (UL) {
+      an2 = src[en2 < end ? en2 : end - 1];
+      load_edge<LY, IN, CPL>(b0, x, y, s, en < end ? en : end - 1, an, c0);
+    } else {
+      if (en < end) load_edge<LY, IN, CPL>(b0, x, y, s, en, an, c0);
+      an2 = en2 < end ? src[en2] : 0;
+    }
     edge_accumulate<LY, IN, CPL>(b1, acc);
     e = en;
     en = en2;
@@ -830,21 +846,23 @@ __global__ void __launch_bounds__(256) conv_jvp_pipe(JvpParams prm) {
   if (e < end) load(b0, e, a);
   int en = e + GPR;
   int an = en < end ? src[en] : 0;
+  // Unconditional loads, clamped to the receiver's last edge past its end
+  // (a conditional load makes the compiler wait for all loads in flight).
   while (e < end) {
-    load_x(b0, a);
-    if (en < end) load(b1, en, an);
     int en2 = en + GPR;
-    int an2 = en2 < end ? src[en2] : 0;
+    int an2 = src[en2 < end ? en2 : end - 1];
+    load_x(b0, a);
+    load(b1, en < end ? en : end - 1, an);
     jvp_accumulate<LY, IN, CPL>(b0, acc, dacc);
     e = en;
     a = an;
     en = en2;
     an = an2;
     if (e >= end) break;
-    load_x(b1, a);
-    if (en < end) load(b0, en, an);
     en2 = en + GPR;
-    an2 = en2 < end ? src[en2] : 0;
+    an2 = src[en2 < end ? en2 : end - 1];
+    load_x(b1, a);
+    load(b0, en < end ? en : end - 1, an);
     jvp_accumulate<LY, IN, CPL>(b1, acc, dacc);
     e = en;
     a = an;
@@ -1326,19 +1344,23 @@ __global__ void __launch_bounds__(256) conv_bwd_pipe(BwdParams prm) {
   }
   int en = e + GPR;
   int an = en < end ? src[en] : 0;
+  // The sender index two edges ahead and the next edge's rows are loaded
+  // unconditionally, clamped to the receiver's last edge past its end: a
+  // conditional load, merged into the loop variable, makes the compiler wait
+  // for every memory operation in flight, this edge's gradient stores included.
   while (e < end) {
-    if (en < end) load_bwd_edge<LY, CPL, LPG>(b1, x, y, s, en, an, li);
     int en2 = en + GPR;
-    int an2 = en2 < end ? src[en2] : 0;
+    int an2 = src[en2 < end ? en2 : end - 1];
+    load_bwd_edge<LY, CPL, LPG>(b1, x, y, s, en < end ? en : end - 1, an, li);
     bwd_edge<LY, CPL, LPG, GEN>(b0, gv, prm, e, a, li);
     e = en;
     a = an;
     en = en2;
     an = an2;
     if (e >= end) break;
-    if (en < end) load_bwd_edge<LY, CPL, LPG>(b0, x, y, s, en, an, li);
     en2 = en + GPR;
-    an2 = en2 < end ? src[en2] : 0;
+    an2 = src[en2 < end ? en2 : end - 1];
+    load_bwd_edge<LY, CPL, LPG>(b0, x, y, s, en < end ? en : end - 1, an, li);
     bwd_edge<LY, CPL, LPG, GEN>(b1, gv, prm, e, a, li);
     e = en;
     a = an;
@@ -1366,13 +1388,13 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <class LY, typename IN, int CPL, int GPR>
+template <class LY, typename IN, int CPL, int GPR, bool UL = false>
 hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t st) {
   constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
   if (p.num_nodes <= 0) return hipSuccess;
   const long waves = (p.num_nodes + RPW - 1) / RPW;
   const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
-  hipLaunchKernelGGL((conv_fwd_pipe<LY, IN, CPL, GPR>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((conv_fwd_pipe<LY, IN, CPL, GPR, UL>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
