@@ -509,8 +509,11 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
     // rows of this lane's first two edges, in flight during the network
     RadialRows<LY> ra, rb;
     const int a0 = sender(s_cur, 0), a1 = sender(s_cur, 1);
-    if (c_q > 0) radial_load<LY>(ra, prm, es_q, a0, n);
-    if (c_q > 1) radial_load<LY>(rb, prm, es_q + 1, a1, n);
+    // (unconditional, clamped like the loads of edges 2 and 3 below, and kept
+    // ahead of the network by the scheduling barrier)
+    radial_load<LY>(ra, prm, c_q > 0 ? es_q : 0, a0, n);
+    radial_load<LY>(rb, prm, c_q > 0 ? es_q + (c_q > 1 ? 1 : 0) : 0, a1, n);
+    __builtin_amdgcn_sched_barrier(0);
 
     float acc[NO][2];
 #pragma unroll
@@ -597,16 +600,16 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
         }
         radial_edge<LY>(yv, R.x, sv, acc);
       };
-      // senders of edges 2 and 3 (lanes of the same row share c_q, so the
-      // source lanes of the shuffles are active)
-      if (c_q > 0) {
-        edge(ra, 0);
-        if (c_q > 2) radial_load<LY>(ra, prm, es_q + 2, sender(s_cur, 2), n);
-      }
-      if (c_q > 1) {
-        edge(rb, 1);
-        if (c_q > 3) radial_load<LY>(rb, prm, es_q + 3, sender(s_cur, 3), n);
-      }
+      // Rows of edges 2 and 3, loaded unconditionally: past the quad's end
+      // the index is clamped to its last edge (whose sender tile_ids also
+      // repeats), and an empty quad reads edge 0 and node 0. A conditional
+      // load here would make the compiler wait for every load in flight.
+      const int e2 = c_q > 0 ? es_q + (c_q > 2 ? 2 : c_q - 1) : 0;
+      const int e3 = c_q > 0 ? es_q + (c_q > 3 ? 3 : c_q - 1) : 0;
+      if (c_q > 0) edge(ra, 0);
+      radial_load<LY>(ra, prm, e2, sender(s_cur, 2), n);
+      if (c_q > 1) edge(rb, 1);
+      radial_load<LY>(rb, prm, e3, sender(s_cur, 3), n);
       if (c_q > 2) edge(ra, 2);
       if (c_q > 3) edge(rb, 3);
 
