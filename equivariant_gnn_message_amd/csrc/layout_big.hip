@@ -32,7 +32,7 @@ const KernelSet* kernels_big() {
     {kF32, E3C_N(kF32), kBF16, E3C_N(kBF16), kBwd, E3C_N(kBwd), launch_bwd_pipe<L, 2, 2, true>,
      launch_jvp<L, float, 2, 2>, launch_jvp_pipe<L, bf16_bits, 2, 2, false>},
     {kSenderF32, 1, kSenderBF16, 1, kSenderBwd, 1, launch_bwd_pipe<LS, 2, 2, true>,
-     launch_jvp<LS, float, 2, 2>, launch_jvp<LS, bf16_bits, 2, 2>},
+     launch_jvp<LS, float, 2, 2>, launch_jvp_pipe<LS, bf16_bits, 2, 2, false>},
   };
   return &k;
 }

@@ -164,8 +164,10 @@ def test_masked_rejects_bad_count():
 
 @pytest.mark.parametrize("idx,n,ordering,force_bf", [(0, None, 0, False), (1, None, 0, False),
                                                      (2, 601, 0, False), (3, 601, 0, False),
-                                                     (2, 401, 1, False), (2, 501, 0, True)],
-                         ids=["w0", "w1", "w2-n601", "w3bf16-n601", "w2-n401-sender", "w2bf16-n501"])
+                                                     (2, 401, 1, False), (2, 501, 0, True),
+                                                     (3, 401, 1, False)],
+                         ids=["w0", "w1", "w2-n601", "w3bf16-n601", "w2-n401-sender", "w2bf16-n501",
+                              "w3bf16-n401-sender"])
 def test_jvp_parity(idx, n, ordering, force_bf):
     import torch
     inp = synth.make_inputs(idx, num_nodes=n) if n else synth.make_inputs(idx)
