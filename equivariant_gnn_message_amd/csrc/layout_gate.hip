@@ -13,8 +13,9 @@ constexpr CGValues<L::NNZ> kCG = L::CG;
 
 // Variant 0 of each list is the default (the fastest measured on MI355X for
 // the workload of this layout); the others stay selectable for comparison.
-const FwdLauncher kF32[] = {launch_fwd_pipe<L, float, 4, 4>, launch_fwd<L, float, 4, 4>,
-                            launch_fwd_pipe<L, float, 4, 2>, launch_fwd_pipe<L, float, 2, 2>};
+const FwdLauncher kF32[] = {launch_fwd_pipe<L, float, 4, 4, true>, launch_fwd<L, float, 4, 4>,
+                            launch_fwd_pipe<L, float, 4, 2>, launch_fwd_pipe<L, float, 2, 2>,
+                            launch_fwd_pipe<L, float, 4, 4>};
 const FwdLauncher kBF16[] = {launch_fwd_pipe<L, bf16_bits, 4, 4>, launch_fwd<L, bf16_bits, 4, 4>};
 const BwdLauncher kBwd[] = {launch_bwd<L, 2, 4>, launch_bwd<L, 1, 2>, launch_bwd_pipe<L, 2, 4>};
 
