@@ -12,8 +12,10 @@ plan and the receiver CSR are built once per graph, outside the timed region
 Prints one JSON line: edges/s of whole steps, plus the roofline of the
 dominant kernel (algorithmic bytes / average duration from HIP events on the
 launch stream, against HBM; algorithmic flops against the vector-ALU peak
-when the kernel's arithmetic intensity is above the ridge point) and the CPU
-oracle timed on a bounded sample.
+when the kernel's arithmetic intensity is above the ridge point), the CPU
+oracle timed on the whole workload over the host cores with the full-output
+parity of the GPU result against it, and the forwards of the MACE-scale and
+large bf16 workloads against both roofs.
 """
 
 import argparse
@@ -49,7 +51,10 @@ def parse():
     ap.add_argument("--no-order", action="store_true",
                     help="process receivers in index order (no locality schedule)")
     ap.add_argument("--cluster", type=int, default=512, help="receivers per locality cluster")
-    ap.add_argument("--cpu-sample-edges", type=int, default=12000)
+    ap.add_argument("--cpu-sample-edges", type=int, default=12000,
+                    help="edges of the single-threaded oracle sample of the --mode variants")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="default run: skip the extra forward figures of workloads 2 and 3")
     ap.add_argument("--sweep", action="store_true",
                     help="time every compiled kernel variant (one JSON line each) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -229,35 +234,111 @@ def traffic_from_profiles(kernel, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, sample_edges, with_backward):
-    """The oracle, as it stands, on the first receivers covering ~sample_edges edges."""
+def host_cores():
+    """Cores this process may use: its affinity set, capped by OMP_NUM_THREADS and by 16 (the
+    host share of one GPU on the MI355X boxes)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, min(16, n))
+
+
+_POOL = {}   # operands and shared result buffers inherited by the forked oracle workers
+
+
+def _shared_f64(shape):
+    """A float64 array in an anonymous shared mapping (written by forked workers)."""
+    import mmap
     import numpy as np
+    n = int(np.prod(shape)) * 8
+    buf = mmap.mmap(-1, max(n, 8))
+    return np.frombuffer(buf, dtype=np.float64, count=int(np.prod(shape))).reshape(shape)
+
+
+def _oracle_chunk(k):
+    """Worker: oracle forward (and reverse) on the receiver-aligned edge range k."""
     from threadpoolctl import threadpool_limits
 
     from oracle import conv
+    P = _POOL
+    e0, e1 = P["bounds"][k], P["bounds"][k + 1]
+    b0, b1 = P["rows"][k], P["rows"][k + 1]
+    with threadpool_limits(1):
+        if e1 > e0:
+            rcv = P["receivers"][e0:e1] - b0
+            P["out"][b0:b1] = conv.forward(P["lay"], P["x"], P["y"][e0:e1], P["s"][e0:e1],
+                                           P["senders"][e0:e1], rcv, b1 - b0)
+            if P["backward"]:
+                dx, dy, ds = conv.backward(P["lay"], P["x"], P["y"][e0:e1], P["s"][e0:e1], P["g"],
+                                           P["senders"][e0:e1], P["receivers"][e0:e1], P["num_nodes"])
+                P["dx"][k] = dx
+                P["dy"][e0:e1] = dy
+                P["ds"][e0:e1] = ds
+    return e1 - e0
+
+
+def cpu_baseline(inp, with_backward, workers):
+    """The oracle, as it stands, on the whole workload: the receivers are cut into `workers`
+    ranges of about equal edge counts, each run by one single-threaded process (forked before
+    the GPU is touched, so no worker holds a device).  Returns the baseline record and the
+    oracle's outputs (out, and dx, dy, ds with the reverse pass) for the parity check."""
+    import multiprocessing as mp
+    import numpy as np
+
+    from oracle import conv, so3
 
     w = inp.workload
     lay = conv.make_layout(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
-    ptr = np.searchsorted(inp.receivers, np.arange(inp.num_nodes + 1))
-    nrows = int(np.searchsorted(ptr, sample_edges))
-    nrows = max(1, min(nrows, inp.num_nodes))
-    e1 = int(ptr[nrows])
-    x = inp.as_f32("x")
-    y = inp.as_f32("y")[:e1] if inp.y.dtype != np.float32 else inp.y[:e1]
-    s = inp.s[:e1]
-    if s.dtype == np.uint16:
-        from equivariant_gnn_message_amd import synth
-        s = synth.bf16_to_f32(s).reshape(s.shape)
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        out = conv.forward(lay, x, y, s, inp.senders[:e1], inp.receivers[:e1], nrows)
-        if with_backward:
-            conv.backward(lay, x, y, s, inp.g, inp.senders[:e1], inp.receivers[:e1], inp.num_nodes)
-        dt = time.perf_counter() - t0
-    return {"value": e1 / dt, "unit": "edges/s", "cores": 1, "kind": "oracle",
-            "sample": f"receivers 0..{nrows - 1} ({e1} edges) of the same graph, "
-                      f"{'forward + reverse' if with_backward else 'forward'}, fp64 numpy, "
-                      f"{dt:.1f} s"}, out, nrows
+    for q in lay.paths:                       # CG tables built once, outside the timed region
+        so3.real_cg(q.l1, q.l2, q.l3)
+    N, E = inp.num_nodes, inp.num_edges
+    ptr = np.searchsorted(inp.receivers, np.arange(N + 1))
+    cuts = np.searchsorted(ptr, np.linspace(0, E, workers + 1), side="left")
+    cuts[0], cuts[-1] = 0, N
+    rows = np.maximum.accumulate(cuts)
+    _POOL.clear()
+    _POOL.update(lay=lay, x=inp.as_f32("x"), y=inp.as_f32("y"), s=inp.as_f32("s"), g=inp.g,
+                 senders=inp.senders, receivers=inp.receivers, num_nodes=N, backward=with_backward,
+                 rows=rows, bounds=ptr[rows], out=_shared_f64((N, lay.num_out, lay.channels)))
+    if with_backward:
+        _POOL.update(dx=_shared_f64((workers, N, lay.num_x, lay.channels)),
+                     dy=_shared_f64((E, lay.num_y)), ds=_shared_f64((E, lay.num_paths, lay.channels)))
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        done = sum(pool.map(_oracle_chunk, range(workers), chunksize=1))
+    dt = time.perf_counter() - t0
+    assert done == E
+    res = {"out": _POOL["out"]}
+    if with_backward:
+        res.update(dx=_POOL["dx"].sum(axis=0), dy=_POOL["dy"], ds=_POOL["ds"])
+    what = "forward + reverse" if with_backward else "forward"
+    base = {"value": E / dt, "unit": "edges/s", "cores": workers, "kind": "oracle",
+            "sample": (f"the whole workload ({E} edges, {N} receivers): {what}, fp64 numpy, "
+                       f"{workers} single-threaded processes over receiver-aligned edge ranges"),
+            "wall_s": dt, "edges_per_s_per_core": E / dt / workers}
+    _POOL.clear()
+    return base, res
+
+
+def parity_full(got, ref):
+    """max|got - ref| / RMS(ref) over whole tensors (chunked to bound host memory)."""
+    import numpy as np
+    g = got.reshape(-1)
+    r = ref.reshape(-1)
+    step = 1 << 24
+    err = 0.0
+    ss = 0.0
+    for i in range(0, r.size, step):
+        rr = r[i:i + step]
+        err = max(err, float(np.max(np.abs(g[i:i + step].astype(np.float64) - rr))) if rr.size else 0.0)
+        ss += float(np.dot(rr, rr))
+    rms = math.sqrt(ss / max(r.size, 1))
+    return err / rms if rms > 0 else err
 
 
 def main():
@@ -272,9 +353,7 @@ def main():
         return
 
     import numpy as np
-    import torch
 
-    from equivariant_gnn_message_amd import e3conv as E
     from equivariant_gnn_message_amd import synth
 
     if args.mode != "conv":
@@ -286,6 +365,16 @@ def main():
     inp = synth.make_inputs(args.workload)
     t_gen = time.perf_counter() - t0
     N, Ecount = inp.num_nodes, inp.num_edges
+
+    # The oracle runs first: its worker processes are forked before this process touches the
+    # GPU, so none of them holds the device.  Its outputs are kept for the parity check.
+    base = ref = None
+    if not args.no_cpu_baseline:
+        base, ref = cpu_baseline(inp, w.backward, host_cores())
+
+    import torch
+
+    from equivariant_gnn_message_amd import e3conv as E
     dev = torch.device("cuda:0")
 
     def t(a):
@@ -412,16 +501,95 @@ def main():
     res["fwd_valu_TFLOPs"] = fwd_flops / (fwd_ms * 1e-3) / 1e12
     res["roofline"] = roofline(kernel, kms, kbytes, fwd_flops if kernel == "conv_fwd" else None,
                                traffic_from_profiles(kernel, args.workload))
-    if not args.no_cpu_baseline:
-        base, ref_rows, nrows = cpu_baseline(inp, args.cpu_sample_edges, w.backward)
-        res["cpu_baseline"] = base
-        got = out[:nrows].double().cpu().numpy()
-        rms = math.sqrt(float(np.mean(ref_rows ** 2)))
-        res["parity_sample_max_rel_err"] = float(np.abs(got - ref_rows).max()) / rms
-    else:
-        res["cpu_baseline"] = None
+    res["cpu_baseline"] = base
+    if ref is not None:
+        # the GPU outputs of the last timed step against the oracle, element by element
+        tol = 2e-2 if w.dtype == "bf16" else 1e-5
+        par = {"out": parity_full(out.cpu().numpy(), ref["out"])}
+        if w.backward:
+            for name, t_gpu, key in (("grad_x", grads[0], "dx"), ("grad_y", grads[1], "dy"),
+                                     ("grad_s", grads[2], "ds")):
+                par[name] = parity_full(t_gpu.cpu().numpy(), ref[key])
+        res["parity_full"] = {"max_abs_err_over_rms": par, "tolerance": tol,
+                              "pass": all(v <= tol for v in par.values())}
+    del ref
     res["input_gen_s"] = t_gen
+    if w.backward and w.idx == 4 and not args.no_extra:
+        # workload 2 (MACE-scale forward) is the forward of this step: same graph and operands
+        res["w2_forward"] = forward_block(plan, w, fwd_times, fwd_bytes, N, Ecount)
+        del x, y, s, g, grads, out, order, order_dev, src, dst, row_ptr
+        torch.cuda.empty_cache()
+        res["w3_forward"] = bench_forward_workload(3, args)
     print(json.dumps(res), flush=True)
+
+
+def alg_forward_flops(plan):
+    """Algorithmic forward flops per edge: 2 per CG term for K^p(y), then per channel one
+    product per nonzero of each K^p and one mixing product per output component of each path
+    (sum over paths of 2 l3 + 1), whatever order a kernel applies them in."""
+    nnz, nnz_k, _ = _conv_counts(plan)
+    mix = sum(2 * q["l3"] + 1 for q in plan.paths())
+    return 2 * nnz + 2 * plan.channels * (nnz_k + mix)
+
+
+def forward_block(plan, w, times, nbytes, N, Ecount):
+    """One forward's figures against both roofs: HBM bytes and vector-ALU flops."""
+    import numpy as np
+    ms = float(np.mean(times))
+    flops = alg_forward_flops(plan) * Ecount
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"{w.name}: forward, N={N} E={Ecount}, {w.irreps_in} (x) SH lmax {w.lmax} -> "
+                        f"{w.irreps_out}, {'bf16 storage / fp32 accumulation' if w.dtype == 'bf16' else 'fp32'}",
+            "ms": ms, "ms_stats": time_stats(times), "edges_per_s": Ecount / (ms * 1e-3),
+            "algorithmic_bytes": nbytes, "hbm_GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS,
+            "algorithmic_flops": flops, "valu_TFLOPs": tf, "valu_frac": tf / PEAK_FP32_VALU_TFLOPS,
+            "bound": "alu" if flops / PEAK_FP32_VALU_TFLOPS / 1e12 > nbytes / PEAK_HBM_GBPS / 1e9 else "hbm"}
+
+
+def bench_forward_workload(idx, args):
+    """Forward of workload idx (full size, default kernel, clustered receiver order), timed
+    per call with HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    from equivariant_gnn_message_amd import e3conv as E
+    from equivariant_gnn_message_amd import synth
+
+    w = synth.WORKLOADS[idx]
+    inp = synth.make_inputs(idx)
+    N, Ec = inp.num_nodes, inp.num_edges
+    b_in = 2 if w.dtype == "bf16" else 4
+
+    def t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    x, y, s = t(inp.x), t(inp.y), t(inp.s)
+    src = t(inp.senders)
+    row_ptr = E.e3conv_csr_from_receivers(t(inp.receivers), N)
+    order = torch.from_numpy(E.e3conv_receiver_order(row_ptr.cpu().numpy(), inp.senders, N, Ec,
+                                                     args.cluster)).cuda()
+    del inp
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    out = torch.empty((N, w.num_out, w.channels), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        plan.forward(x, y, s, src, row_ptr, out=out, order=order)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        plan.forward(x, y, s, src, row_ptr, out=out, order=order)
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) for a, b in ev]
+    blk = forward_block(plan, w, times, alg_bytes(w, N, Ec, b_in)[0], N, Ec)
+    del x, y, s, src, row_ptr, order, out
+    torch.cuda.empty_cache()
+    return blk
 
 
 def time_stats(times):

@@ -18,8 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libe3conv.so")
 
-SOURCES = ["host_core.cpp", "e3conv.cpp", "kernels.hip", "layout_tiny.hip", "layout_gate.hip",
-           "layout_mace.hip", "layout_big.hip", "linear.hip"]
+SOURCES = ["host_core.cpp", "e3conv.cpp", "kernels.hip", "validate.hip", "layout_tiny.hip",
+           "layout_gate.hip", "layout_mace.hip", "layout_big.hip", "linear.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]
@@ -51,10 +51,26 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False):
+def _stale(src):
+    """True if the object of src is missing or older than any source or header."""
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".h", ".hip", ".cpp"))
+            and (f == src or f.endswith(".h"))]
+    deps.append(os.path.join(INCLUDE, "e3conv.h"))
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(verbose=False, incremental=False):
+    """Compile every source (or, with incremental=True, only those whose object is
+    older than the source or any header) and link libe3conv.so."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    todo = [s for s in SOURCES if not incremental or _stale(s)]
+    with ThreadPoolExecutor(max(1, len(todo))) as ex:
+        list(ex.map(lambda s: _compile(s, verbose), todo))
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
     if verbose:
@@ -67,4 +83,4 @@ def build(verbose=False):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))

@@ -1122,29 +1122,58 @@ struct BwdBuf {
   float s[LY::NP][CPL];
 };
 
-template <class LY, int CPL, int LPG>
+// Q: the lane holds channels li*CPL .. li*CPL+CPL-1 (one vector access per
+// row); otherwise channels li, li+LPG, ... (one 4-byte access per channel).
+template <class LY, int CPL, int LPG, bool Q = false>
 __device__ __forceinline__ void load_bwd_edge(BwdBuf<LY, CPL>& buf, const float* __restrict__ x,
                                               const float* __restrict__ y,
                                               const float* __restrict__ s, int e, int a, int li) {
   constexpr int C = LY::C, NX = LY::NX, NY = LY::NY, NP = LY::NP;
   load_row<float, NY>(y + (size_t)e * NY, buf.y);
-  const float* xrow = x + (size_t)a * NX * C + li;
+  if constexpr (Q) {
+    const float* xrow = x + (size_t)a * NX * C + li * CPL;
 #pragma unroll
-  for (int i = 0; i < NX; ++i)
+    for (int i = 0; i < NX; ++i) load_ch<float, CPL, false>(xrow + i * C, buf.x[i]);
+    const float* srow = s + (size_t)e * NP * C + li * CPL;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) buf.x[i][c] = xrow[i * C + c * LPG];
-  const float* srow = s + (size_t)e * NP * C + li;
+    for (int p = 0; p < NP; ++p) load_ch<float, CPL, true>(srow + p * C, buf.s[p]);
+  } else {
+    const float* xrow = x + (size_t)a * NX * C + li;
 #pragma unroll
-  for (int p = 0; p < NP; ++p)
+    for (int i = 0; i < NX; ++i)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) buf.s[p][c] = __builtin_nontemporal_load(srow + p * C + c * LPG);
+      for (int c = 0; c < CPL; ++c) buf.x[i][c] = xrow[i * C + c * LPG];
+    const float* srow = s + (size_t)e * NP * C + li;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) buf.s[p][c] = __builtin_nontemporal_load(srow + p * C + c * LPG);
+  }
+}
+
+// Orders a wave's LDS accesses around an exchange between its lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // GEN: honour optional outputs (nullptr: not computed) and accumulation flags;
 // the default instantiations assume all three outputs, overwritten.
-template <class LY, int CPL, int LPG, bool GEN = false>
+// Q: contiguous channel quads (see load_bwd_edge); the grad_x partials are
+// then re-laid through the group's LDS rows xt (NX * C floats) so that each
+// atomic instruction of the group covers consecutive channels.
+// after(p) runs once path p's last use of the edge's s[p] is done (the tiled
+// kernel reloads s[p] with the next edge's row there).
+struct NoAfterPath {
+  template <class P>
+  __device__ __forceinline__ void operator()(P) const {}
+};
+
+template <class LY, int CPL, int LPG, bool GEN = false, bool Q = false, class After = NoAfterPath>
 __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float (&gv)[LY::NO][CPL],
-                                         const BwdParams& prm, int e, int a, int li) {
+                                         const BwdParams& prm, int e, int a, int li,
+                                         float* xt = nullptr, After after = After{}) {
   constexpr int C = LY::C, NX = LY::NX, NY = LY::NY, NP = LY::NP;
   constexpr int NYP = pow2_ceil(NY);
   constexpr int STEPS = ilog2(LPG);
@@ -1159,7 +1188,7 @@ __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float
   const bool want_s = !GEN || prm.gs;
   const bool want_y = !GEN || prm.gy;
   const bool want_x = !GEN || prm.gx;
-  float* gsrow = want_s ? prm.gs + (size_t)e * NP * C + li : nullptr;
+  float* gsrow = want_s ? prm.gs + (size_t)e * NP * C + (Q ? li * CPL : li) : nullptr;
   // Accumulating into grad_s: fetch the edge's rows up front, in one batch,
   // rather than one dependent load per path before its store.
   float gs_prev[GEN ? NP : 1][CPL];
@@ -1167,9 +1196,14 @@ __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float
   if constexpr (GEN) {
     if (acc_s) {
 #pragma unroll
-      for (int p = 0; p < NP; ++p)
+      for (int p = 0; p < NP; ++p) {
+        if constexpr (Q) {
+          load_ch<float, CPL, true>(gsrow + p * C, gs_prev[p]);
+        } else {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) gs_prev[p][c] = __builtin_nontemporal_load(gsrow + p * C + c * LPG);
+          for (int c = 0; c < CPL; ++c) gs_prev[p][c] = __builtin_nontemporal_load(gsrow + p * C + c * LPG);
+        }
+      }
     }
   }
 
@@ -1215,16 +1249,19 @@ __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float
         for (int c = 0; c < CPL; ++c) ds[c] = 0.0f;
       }
     });
-    if constexpr (GEN) {
-      if (want_s) {
+    if (want_s) {
+      if constexpr (GEN) {
+        if (acc_s) {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          __builtin_nontemporal_store(acc_s ? ds[c] + gs_prev[p][c] : ds[c], gsrow + p * C + c * LPG);
+          for (int c = 0; c < CPL; ++c) ds[c] += gs_prev[p][c];
         }
       }
-    } else {
+      if constexpr (Q) {
+        store_row<CPL>(gsrow + p * C, ds, 1.0f);
+      } else {
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) __builtin_nontemporal_store(ds[c], gsrow + p * C + c * LPG);
+        for (int c = 0; c < CPL; ++c) __builtin_nontemporal_store(ds[c], gsrow + p * C + c * LPG);
+      }
     }
 
     if (want_y) sfor<0, D1>([&](auto m1c) {
@@ -1250,14 +1287,39 @@ __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float
         });
       }
     });
+    after(pc);
   });
 
   if (want_x) {
+    if constexpr (Q) {
+      // lane li holds channels li*CPL + c; after the exchange it holds li + c*LPG
 #pragma unroll
-    for (int i = 0; i < NX; ++i)
+      for (int i = 0; i < NX; ++i) {
+        float v[CPL];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c)
-        unsafeAtomicAdd(prm.gx + ((size_t)a * NX + i) * C + li + c * LPG, dxp[i][c]);
+        for (int c = 0; c < CPL; ++c) v[c] = dxp[i][c];
+        if constexpr (CPL == 4) {
+          *reinterpret_cast<f32x4*>(xt + i * C + li * 4) = f32x4{v[0], v[1], v[2], v[3]};
+        } else if constexpr (CPL == 2) {
+          *reinterpret_cast<f32x2*>(xt + i * C + li * 2) = f32x2{v[0], v[1]};
+        } else {
+          xt[i * C + li] = v[0];
+        }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < NX; ++i)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          unsafeAtomicAdd(prm.gx + ((size_t)a * NX + i) * C + li + c * LPG, xt[i * C + li + c * LPG]);
+      wave_lds_sync();
+    } else {
+#pragma unroll
+      for (int i = 0; i < NX; ++i)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          unsafeAtomicAdd(prm.gx + ((size_t)a * NX + i) * C + li + c * LPG, dxp[i][c]);
+    }
   }
   if (!want_y) return;
 
@@ -1369,6 +1431,167 @@ __global__ void __launch_bounds__(256) conv_bwd_pipe(BwdParams prm) {
   }
 }
 
+// ------------------------------------------------- edge-tiled backward ------
+//
+// The reverse pass sums nothing at the receivers (every output is per edge, or
+// per sender through grad_x), so it need not walk receivers: the edges are cut
+// into tiles of about T consecutive edges in storage order, one per wave.  The
+// waves resident at one time then sweep a narrow, advancing window of the s
+// and grad_s rows (the largest streams), which the memory system serves faster
+// than one separate stream per receiver (measured on MI355X: this order beats
+// the receiver-locality order even though its sender rows then miss L2).  A
+// wave holds 64/LPG groups, each on its own edge (tile edges grp, grp + G,
+// ...); a lane holds CPL consecutive channels, so s and grad_s move in 16-byte
+// accesses, and the grad_x partials are re-laid through LDS so that each atomic
+// instruction covers consecutive channels.  Each group tracks the receiver of
+// its edge (found once by a wave-parallel search of row_ptr, then advanced edge
+// by edge) and reloads the cotangent row g[b]/N when it changes.
+
+// Largest b in [0, num_nodes) with row_ptr[b] <= e (the receiver of edge e when
+// e < row_ptr[num_nodes] = num_edges), by 64 probes per round.  The first
+// round probes the 64 receivers around e * num_nodes / num_edges (where the
+// answer lies when degrees do not drift far from their mean); otherwise the
+// search narrows [0, num_nodes) by 64x per round.
+__device__ __forceinline__ int find_receiver(const int* __restrict__ row_ptr, int num_nodes,
+                                             int num_edges, int e) {
+  const int lane = threadIdx.x & 63;
+  long lo = 0, hi = num_nodes;
+  {
+    long g0 = (long)e * num_nodes / num_edges - 31;
+    g0 = g0 < 0 ? 0 : (g0 + 64 > num_nodes ? (num_nodes > 64 ? num_nodes - 64 : 0) : g0);
+    const long k = g0 + lane;
+    const bool le = k < num_nodes && row_ptr[k < num_nodes ? k : 0] <= e;
+    const unsigned long long m = __ballot(le);
+    const int cnt = __popcll(m);
+    // the guess brackets e when probe g0 is <= e and the probe after the last
+    // true one (if inside the window) is > e
+    // (the probes <= e are a prefix of the lanes: row_ptr is non-decreasing)
+    if ((m & 1ull) && (cnt < 64 || g0 + 64 >= num_nodes)) {
+      lo = g0 + cnt - 1;          // the next receiver starts after e, or there is none
+      hi = lo + 1;
+    } else if (m & 1ull) {
+      lo = g0 + 63;               // all 64 probes <= e: the answer lies above
+    } else {
+      hi = g0;                    // row_ptr[g0] > e (so g0 > 0): the answer lies below
+    }
+  }
+  while (hi - lo > 1) {
+    const long step = (hi - lo + 63) / 64;
+    const long k = lo + (long)lane * step;
+    const bool le = k < hi && row_ptr[k < hi ? k : lo] <= e;
+    const int cnt = __popcll(__ballot(le));
+    lo += (long)(cnt - 1) * step;
+    hi = lo + step < hi ? lo + step : hi;
+  }
+  return __builtin_amdgcn_readfirstlane((int)lo);
+}
+
+// One tile: the edges [e0, e1).
+template <class LY, int CPL, bool GEN>
+__device__ __forceinline__ void bwd_tile(const BwdParams& prm, long e0, int e1, float* xt, int li,
+                                         int grp) {
+  constexpr int C = LY::C, NX = LY::NX, NO = LY::NO;
+  constexpr int LPG = C / CPL;
+  constexpr int G = 64 / LPG;
+  // edges of padding receivers (b >= num_real) carry no gradient
+  const int e_real = prm.num_real < prm.num_nodes ? prm.row_ptr[prm.num_real] : prm.num_edges;
+  const int e_lim = e1 < e_real ? e1 : e_real;
+
+  if ((int)e0 < e_lim) {
+    int e = (int)e0 + grp;
+    int b = find_receiver(prm.row_ptr, prm.num_nodes, prm.num_edges, (int)e0);
+    while (prm.row_ptr[b + 1] <= (e < e_lim ? e : e_lim - 1)) ++b;   // this group's first edge
+    int bend = prm.row_ptr[b + 1];
+    float gv[NO][CPL];
+    auto load_g = [&]() {
+      const float* grow = prm.g + (size_t)b * NO * C + li * CPL;
+#pragma unroll
+      for (int o = 0; o < NO; ++o) {
+        load_ch<float, CPL, false>(grow + o * C, gv[o]);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) gv[o][c] *= prm.inv_avg;
+      }
+    };
+    load_g();
+    const int last = e_lim - 1;
+    // y and x rows: two buffers (the next edge's load while this one is used);
+    // s rows: one buffer, s[p] replaced by the next edge's row as soon as path
+    // p is done with it, which keeps a whole edge of s in flight at the cost
+    // of one row of registers.
+    BwdBuf<LY, CPL> b0, b1;
+    int a = prm.src[e < last ? e : last];
+    load_bwd_edge<LY, CPL, LPG, true>(b0, prm.x, prm.y, prm.s, e < last ? e : last, a, li);
+    int en = e + G;
+    int an = prm.src[en < last ? en : last];
+    auto step = [&](BwdBuf<LY, CPL>& cur, BwdBuf<LY, CPL>& nxt) {
+      // the next edge's rows (and the sender two edges ahead) are loaded
+      // unconditionally, clamped to the tile's last edge
+      const int en2 = en + G;
+      const int an2 = prm.src[en2 < last ? en2 : last];
+      const int ec = en < last ? en : last;
+      load_row<float, LY::NY>(prm.y + (size_t)ec * LY::NY, nxt.y);
+#pragma unroll
+      for (int i = 0; i < NX; ++i)
+        load_ch<float, CPL, false>(prm.x + ((size_t)an * NX + i) * C + li * CPL, nxt.x[i]);
+      const float* snext = prm.s + (size_t)ec * LY::NP * C + li * CPL;
+      auto reload = [&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        load_ch<float, CPL, true>(snext + p * C, cur.s[p]);
+      };
+      if (e <= last) {
+        if (e >= bend) {
+          do { ++b; } while (prm.row_ptr[b + 1] <= e);
+          bend = prm.row_ptr[b + 1];
+          load_g();
+        }
+        bwd_edge<LY, CPL, LPG, GEN, true>(cur, gv, prm, e, a, li, xt, reload);
+      } else {
+        sfor<0, LY::NP>(reload);
+      }
+#pragma unroll
+      for (int p = 0; p < LY::NP; ++p)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) nxt.s[p][c] = cur.s[p][c];
+      e = en;
+      a = an;
+      en = en2;
+      an = an2;
+    };
+    // wave-uniform trip count: steps of G edges until the tile is done
+    for (int k0 = (int)e0; k0 <= last; k0 += 2 * G) {
+      step(b0, b1);
+      if (k0 + G > last) break;
+      step(b1, b0);
+    }
+  }
+  // padding edges of this tile
+  if (e_lim < e1) {
+    const int z0 = e_lim > (int)e0 ? e_lim : (int)e0;
+    zero_edge_grads<LY>(prm, z0 + grp, e1, G, li, LPG);
+  }
+}
+
+// The edges are cut into prm.tiles ranges of nearly equal length (differing by
+// at most one edge); wave w runs range w.
+template <class LY, int CPL, bool GEN = false>
+__global__ void __launch_bounds__(256) conv_bwd_tile(BwdParams prm) {
+  constexpr int C = LY::C, NX = LY::NX;
+  constexpr int LPG = C / CPL;
+  static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
+  constexpr int G = 64 / LPG;
+  __shared__ float xt_all[4][G][NX * C];
+
+  const int lane = threadIdx.x & 63;
+  const int li = lane % LPG;
+  const int grp = lane / LPG;
+  const long w = logical_wave();
+  if (w >= prm.tiles) return;
+  const long e0 = w * prm.num_edges / prm.tiles;
+  const int e1 = (int)((w + 1) * prm.num_edges / prm.tiles);
+  if (e0 >= e1) return;
+  bwd_tile<LY, CPL, GEN>(prm, e0, e1, xt_all[threadIdx.x >> 6][grp], li, grp);
+}
+
 __global__ void fill_zero(float* __restrict__ p, size_t n) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -1427,6 +1650,27 @@ hipError_t launch_bwd_pipe(const BwdParams& p, hipStream_t st) {
   const long waves = (p.num_nodes + RPW - 1) / RPW;
   const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
   hipLaunchKernelGGL((conv_bwd_pipe<LY, CPL, GPR, GEN>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+// One wave per tile of about T edges.
+template <class LY, int CPL, int T, bool GEN = false>
+hipError_t launch_bwd_tile(const BwdParams& prm, hipStream_t st) {
+  BwdParams p = prm;
+  if (p.num_nodes <= 0) return hipSuccess;
+  if (p.gx && !(p.flags & kAccumulateX)) {
+    const size_t nx = (size_t)p.num_nodes * LY::NX * LY::C;
+    const unsigned zb = (unsigned)((nx + 255) / 256 < 8192 ? (nx + 255) / 256 : 8192);
+    hipLaunchKernelGGL(fill_zero, dim3(zb), dim3(256), 0, st, p.gx, nx);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (p.num_edges <= 0) return hipSuccess;
+  const auto kernel = conv_bwd_tile<LY, CPL, GEN>;
+  const long tiles = ((long)p.num_edges + T - 1) / T;
+  p.tiles = (int)tiles;
+  const long blocks = ((tiles + 3) / 4 + 7) / 8 * 8;   // whole rounds of the 8 XCDs (logical_wave)
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

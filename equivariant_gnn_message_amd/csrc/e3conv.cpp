@@ -1,5 +1,5 @@
 // C ABI of the convolution library (declarations and contracts in e3conv.h).
-#include "../../include/e3conv.h"
+#include "e3conv.h"
 
 #include <hip/hip_runtime_api.h>
 
@@ -53,6 +53,16 @@ e3conv_status ok() {
 e3conv_status hip_fail(hipError_t err, const char* what) {
   return fail(E3CONV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(err));
 }
+
+}  // namespace
+
+namespace e3c {
+e3conv_status api_fail(e3conv_status st, const std::string& msg) { return fail(st, msg); }
+e3conv_status api_ok() { return ok(); }
+e3conv_status api_hip_fail(hipError_t err, const char* what) { return hip_fail(err, what); }
+}  // namespace e3c
+
+namespace {
 
 // block code for kernel lookup: unique l in ascending order, else 0 (no kernel)
 uint32_t block_code(const std::vector<Irrep>& blocks) {
@@ -443,6 +453,33 @@ e3conv_status e3conv_backward_ex(e3conv_plan_t p, e3conv_dtype dt, const void* x
   return ok();
 }
 
+e3conv_status e3conv_second_derivatives(e3conv_plan_t p, e3conv_dtype dt, const void* x,
+                                        const void* y, const void* s, const int32_t* src,
+                                        const int32_t* row_ptr, const int32_t* order, int64_t N,
+                                        int64_t E, int64_t num_real_nodes, const float* g,
+                                        const float* cx, const float* cy, const float* cs,
+                                        float* dx, float* dy, float* ds, float* dg, void* stream) {
+  if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (dt != E3CONV_F32) return fail(E3CONV_ERR_UNSUPPORTED, "second derivatives are fp32 only");
+  if (N > 0 && (!g || !cx || !dx || !dg)) return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  if (E > 0 && (!cy || !cs || !dy || !ds)) return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  // L2 = <cx, grad_x> + <cy, grad_y> + <cs, grad_s> = <g, D conv(x, y, s)[cx, cy, cs]>.  The
+  // convolution is trilinear, so each partial derivative is a reverse pass with one operand
+  // replaced by its cotangent, and dL2/dg is the forward-mode derivative along (cx, cy, cs).
+  e3conv_status st = e3conv_backward_ex(p, dt, cx, y, s, src, row_ptr, order, N, E, num_real_nodes,
+                                        g, nullptr, dy, ds, 0u, nullptr, 0, stream);
+  if (st != E3CONV_OK) return st;
+  st = e3conv_backward_ex(p, dt, x, cy, s, src, row_ptr, order, N, E, num_real_nodes, g, dx, nullptr,
+                          ds, E3CONV_ACCUMULATE_GRAD_S, nullptr, 0, stream);
+  if (st != E3CONV_OK) return st;
+  st = e3conv_backward_ex(p, dt, x, y, cs, src, row_ptr, order, N, E, num_real_nodes, g, dx, dy,
+                          nullptr, E3CONV_ACCUMULATE_GRAD_X | E3CONV_ACCUMULATE_GRAD_Y, nullptr, 0,
+                          stream);
+  if (st != E3CONV_OK) return st;
+  return e3conv_jvp(p, dt, x, y, s, cx, cy, cs, src, row_ptr, order, N, E, num_real_nodes, nullptr,
+                    dg, stream);
+}
+
 // ------------------------------------------------------------- linear ---
 
 namespace {
@@ -573,36 +610,6 @@ e3conv_status e3conv_stream_reference(const void* src, void* dst, size_t bytes, 
     return fail(E3CONV_ERR_INVALID_ARGUMENT, "buffers must be 16-byte aligned");
   const hipError_t err = e3c::launch_stream(src, dst, bytes, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "stream launch");
-  return ok();
-}
-
-e3conv_status e3conv_validate_graph(const int32_t* src, const int32_t* row_ptr, int64_t N,
-                                    int64_t E, int on_device) {
-  if (N < 0 || E < 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "negative size");
-  if (E >= (int64_t)1 << 31 || N >= ((int64_t)1 << 31) - 1)
-    return fail(E3CONV_ERR_INVALID_ARGUMENT, "sizes must fit int32 indices");
-  if (!row_ptr || (E > 0 && !src)) return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL pointer");
-  if (!on_device) {
-    if (row_ptr[0] != 0) return fail(E3CONV_ERR_GRAPH, "row_ptr[0] != 0");
-    if (row_ptr[N] != E) return fail(E3CONV_ERR_GRAPH, "row_ptr[num_nodes] != num_edges");
-    for (int64_t i = 0; i < N; ++i)
-      if (row_ptr[i + 1] < row_ptr[i] || row_ptr[i + 1] > E)
-        return fail(E3CONV_ERR_GRAPH, "row_ptr decreases or overflows at node " + std::to_string(i));
-    for (int64_t e = 0; e < E; ++e)
-      if (src[e] < 0 || src[e] >= N)
-        return fail(E3CONV_ERR_GRAPH, "sender out of range at edge " + std::to_string(e));
-    return ok();
-  }
-  int* bad = nullptr;
-  hipError_t err = hipMalloc(&bad, sizeof(int));
-  if (err != hipSuccess) return hip_fail(err, "hipMalloc");
-  int host_bad = 0;
-  err = hipMemcpy(bad, &host_bad, sizeof(int), hipMemcpyHostToDevice);
-  if (err == hipSuccess) err = e3c::launch_validate_graph(src, row_ptr, (int)N, (int)E, bad, nullptr);
-  if (err == hipSuccess) err = hipMemcpy(&host_bad, bad, sizeof(int), hipMemcpyDeviceToHost);
-  (void)hipFree(bad);
-  if (err != hipSuccess) return hip_fail(err, "validate");
-  if (host_bad) return fail(E3CONV_ERR_GRAPH, std::to_string(host_bad) + " violations in the graph");
   return ok();
 }
 

@@ -4,7 +4,9 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cstdint>
+#include <string>
 
+#include "e3conv.h"
 #include "layout.h"
 
 namespace e3c {
@@ -39,6 +41,7 @@ struct BwdParams {
   float inv_avg;
   int num_real;         // edges into receivers b >= num_real get zero grad_y / grad_s
   int flags;            // kAccumulate*: add into the output instead of overwriting it
+  int tiles;            // edge ranges of the edge-tiled kernel (set by its launcher)
 };
 
 // BwdParams::flags.  Only the general reverse launchers honour them and
@@ -160,8 +163,14 @@ hipError_t launch_stream(const void* src, void* dst, size_t bytes, hipStream_t s
 hipError_t launch_csr_from_receivers(const int* dst, int num_edges, int num_nodes, int* row_ptr,
                                      hipStream_t stream);
 
-// Writes into *bad (device int, pre-zeroed by the launcher) the count of violations.
-hipError_t launch_validate_graph(const int* src, const int* row_ptr, int num_nodes, int num_edges,
-                                 int* bad, hipStream_t stream);
+// Ints of a graph-check result: violation count, first bad row_ptr index,
+// first edge with an out-of-range sender, reserved.
+constexpr int kValidateResultInts = 4;
+
+// Status reporting of the C ABI (the thread's last-error detail), shared by
+// the source files that implement entry points.
+e3conv_status api_fail(e3conv_status st, const std::string& msg);
+e3conv_status api_ok();
+e3conv_status api_hip_fail(hipError_t err, const char* what);
 
 }  // namespace e3c

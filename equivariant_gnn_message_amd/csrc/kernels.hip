@@ -1,4 +1,4 @@
-// Graph utilities, streaming references and the layout registry.
+// Receiver CSR, streaming references and the layout registry.
 #include "conv_kernels.h"
 
 namespace e3c {
@@ -16,23 +16,6 @@ __global__ void csr_kernel(const int* __restrict__ dst, int num_edges, int num_n
     if (dst[mid] < b) lo = mid + 1; else hi = mid;
   }
   row_ptr[b] = lo;
-}
-
-__global__ void validate_kernel(const int* __restrict__ src, const int* __restrict__ row_ptr,
-                                int num_nodes, int num_edges, int* __restrict__ bad) {
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i <= num_nodes) {
-    const int r = row_ptr[i];
-    bool ok = r >= 0 && r <= num_edges;
-    if (i == 0) ok = ok && r == 0;
-    if (i == num_nodes) ok = ok && r == num_edges;
-    if (i < num_nodes) ok = ok && row_ptr[i + 1] >= r;
-    if (!ok) atomicAdd(bad, 1);
-  }
-  if (i < num_edges) {
-    const int a = src[i];
-    if (a < 0 || a >= num_nodes) atomicAdd(bad, 1);
-  }
 }
 
 // Streaming references.  Each work-group moves one contiguous chunk and exits,
@@ -58,8 +41,11 @@ __global__ void __launch_bounds__(256) stream_copy_kernel(const f32x4* __restric
   }
 }
 
-__global__ void __launch_bounds__(256) stream_read_kernel(const f32x4* __restrict__ src, size_t n4,
-                                                         float* __restrict__ out) {
+// Written only if a lane's sum equals 1234.5678f (never for the calibration
+// data): keeps the read-only pass's loads alive without touching its input.
+__device__ float stream_sink;
+
+__global__ void __launch_bounds__(256) stream_read_kernel(const f32x4* __restrict__ src, size_t n4) {
   const size_t beg = (size_t)blockIdx.x * (2 * kStreamPerBlock);
   const size_t end = beg + 2 * kStreamPerBlock < n4 ? beg + 2 * kStreamPerBlock : n4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -71,7 +57,7 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const f32x4* __restric
     }
   }
   const float v = acc.x + acc.y + acc.z + acc.w;
-  if (v == 1234.5678f) out[0] = v;   // keeps the loads alive; never true for the calibration data
+  if (v == 1234.5678f) stream_sink = v;
 }
 
 }  // namespace
@@ -87,7 +73,7 @@ hipError_t launch_stream(const void* src, void* dst, size_t bytes, hipStream_t s
                        static_cast<const f32x4*>(src), static_cast<f32x4*>(dst), n4);
   } else {
     hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const f32x4*>(src), n4, const_cast<float*>(static_cast<const float*>(src)));
+                       static_cast<const f32x4*>(src), n4);
   }
   return hipGetLastError();
 }
@@ -104,15 +90,6 @@ hipError_t launch_csr_from_receivers(const int* dst, int num_edges, int num_node
   const unsigned blocks = (unsigned)((num_nodes + 1 + 255) / 256);
   hipLaunchKernelGGL(csr_kernel, dim3(blocks), dim3(256), 0, stream, dst, num_edges, num_nodes,
                      row_ptr);
-  return hipGetLastError();
-}
-
-hipError_t launch_validate_graph(const int* src, const int* row_ptr, int num_nodes, int num_edges,
-                                 int* bad, hipStream_t stream) {
-  const long n = (num_nodes + 1 > num_edges ? num_nodes + 1 : num_edges);
-  const unsigned blocks = (unsigned)((n + 255) / 256);
-  hipLaunchKernelGGL(validate_kernel, dim3(blocks), dim3(256), 0, stream, src, row_ptr, num_nodes,
-                     num_edges, bad);
   return hipGetLastError();
 }
 

@@ -16,8 +16,9 @@ const FwdLauncher kF32[] = {launch_fwd_pipe<L, float, 4, 2>, launch_fwd<L, float
                             launch_fwd_pipe<L, float, 2, 1>, launch_fwd_pipe<L, float, 4, 1>};
 const FwdLauncher kBF16[] = {launch_fwd_pipe<L, bf16_bits, 4, 2>, launch_fwd<L, bf16_bits, 2, 1>,
                              launch_fwd_pipe<L, bf16_bits, 2, 1>};
-const BwdLauncher kBwd[] = {launch_bwd_pipe<L, 2, 1>, launch_bwd<L, 4, 2>, launch_bwd<L, 2, 1>,
-                            launch_bwd_pipe<L, 4, 2>};
+const BwdLauncher kBwd[] = {launch_bwd_tile<L, 4, 16>, launch_bwd_pipe<L, 2, 1>, launch_bwd<L, 4, 2>,
+                            launch_bwd<L, 2, 1>, launch_bwd_pipe<L, 4, 2>, launch_bwd_tile<L, 4, 8>,
+                            launch_bwd_tile<L, 4, 32>};
 
 const FwdLauncher kSenderF32[] = {launch_fwd_pipe<LS, float, 4, 2>};
 const FwdLauncher kSenderBF16[] = {launch_fwd_pipe<LS, bf16_bits, 4, 2>};

@@ -37,7 +37,8 @@ EXPORTED = [
     "e3conv_plan_coefficients", "e3conv_plan_supported", "e3conv_forward", "e3conv_forward_masked",
     "e3conv_forward_radial", "e3conv_jvp", "e3conv_backward_workspace_size", "e3conv_backward", "e3conv_backward_ex",
     "e3conv_linear", "e3conv_linear_backward", "e3conv_csr_from_receivers",
-    "e3conv_validate_graph", "e3conv_receiver_order", "e3conv_stream_reference",
+    "e3conv_validate_graph", "e3conv_validate_graph_async", "e3conv_receiver_order",
+    "e3conv_stream_reference", "e3conv_second_derivatives",
     "e3conv_plan_set_variant",
     "e3conv_plan_num_variants",
     "e3conv_status_string", "e3conv_last_error_detail",
@@ -63,6 +64,11 @@ def load_library(path=LIB_PATH):
     global _lib
     if _lib is not None:
         return _lib
+    # torch first: its HIP runtime is then the one the library's dependency
+    # resolves to, so device pointers and streams from torch are valid for the
+    # library (loading the library first binds it to a second runtime copy,
+    # which then sees no device).
+    import torch  # noqa: F401
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is not built; run `python -m equivariant_gnn_message_amd.build` first")
@@ -99,6 +105,9 @@ def load_library(path=LIB_PATH):
         "e3conv_stream_reference": ([P, P, ctypes.c_size_t, P], ctypes.c_int),
         "e3conv_csr_from_receivers": ([P, I64, I64, P, P], ctypes.c_int),
         "e3conv_validate_graph": ([P, P, I64, I64, ctypes.c_int], ctypes.c_int),
+        "e3conv_validate_graph_async": ([P, P, I64, I64, P, P], ctypes.c_int),
+        "e3conv_second_derivatives": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P, P, P, P,
+                                       P, P, P, P, P], ctypes.c_int),
         "e3conv_plan_set_variant": ([P, ctypes.c_int, ctypes.c_int], ctypes.c_int),
         "e3conv_plan_num_variants": ([P, ctypes.c_int, I32P, I32P], ctypes.c_int),
         "e3conv_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -123,8 +132,10 @@ def _ptr(t):
 
 
 def _stream(stream):
+    """hipStream_t: a raw handle (int), a torch stream object, or None for torch's current
+    stream."""
     if stream is not None:
-        return ctypes.c_void_p(int(stream))
+        return ctypes.c_void_p(int(getattr(stream, "cuda_stream", stream)))
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -390,6 +401,41 @@ def e3conv_validate_graph(src, row_ptr, num_nodes, num_edges):
                                      int(num_edges), 0))
 
 
+def e3conv_validate_graph_async(src, row_ptr, num_nodes, num_edges, result=None, stream=None):
+    """Enqueue the device graph check; returns the int32[4] device result tensor
+    (violations, first bad row_ptr index, first bad edge, 0), read it after the stream."""
+    import torch
+    _need(src, "src", torch.int32)
+    _need(row_ptr, "row_ptr", torch.int32)
+    if result is None:
+        result = torch.empty(4, dtype=torch.int32, device=row_ptr.device)
+    _need(result, "result", torch.int32)
+    if result.numel() != 4:
+        raise ValueError("result must hold 4 int32")
+    _check(load_library().e3conv_validate_graph_async(_ptr(src), _ptr(row_ptr), int(num_nodes),
+                                                      int(num_edges), _ptr(result), _stream(stream)))
+    return result
+
+
+def e3conv_second_derivatives(handle, x, y, s, src, row_ptr, num_nodes, num_edges, num_real_nodes,
+                              grad_out, cot_x, cot_y, cot_s, d_x, d_y, d_s, d_grad_out, order=None,
+                              stream=None):
+    """Gradient of <cot_x, grad_x> + <cot_y, grad_y> + <cot_s, grad_s> (the reverse pass's
+    outputs) with respect to x, y, s and grad_out, written to d_x, d_y, d_s, d_grad_out."""
+    import torch
+    for t, name in ((x, "x"), (y, "y"), (s, "s"), (grad_out, "grad_out"), (cot_x, "cot_x"),
+                    (cot_y, "cot_y"), (cot_s, "cot_s"), (d_x, "d_x"), (d_y, "d_y"), (d_s, "d_s"),
+                    (d_grad_out, "d_grad_out")):
+        _need(t, name, torch.float32)
+    _check_graph_args(src, row_ptr, order)
+    _check(load_library().e3conv_second_derivatives(
+        handle, E3CONV_F32, _ptr(x), _ptr(y), _ptr(s), _ptr(src), _ptr(row_ptr), _ptr(order),
+        int(num_nodes), int(num_edges), int(num_real_nodes), _ptr(grad_out), _ptr(cot_x),
+        _ptr(cot_y), _ptr(cot_s), _ptr(d_x), _ptr(d_y), _ptr(d_s), _ptr(d_grad_out),
+        _stream(stream)))
+    return d_x, d_y, d_s, d_grad_out
+
+
 def e3conv_stream_reference(src, dst=None, stream=None):
     """Streaming reference: copy src into dst (same size), or read src only if dst is None."""
     nbytes = src.numel() * src.element_size()
@@ -562,6 +608,27 @@ class Plan:
         return gx, gy, gs
 
 
+    def second_derivatives(self, x, y, s, src, row_ptr, grad_out, cot_x, cot_y, cot_s,
+                           order=None, num_real_nodes=None, stream=None, out=None):
+        """(d_x, d_y, d_s, d_grad_out): gradient of <cot_x, grad_x> + <cot_y, grad_y> +
+        <cot_s, grad_s> for the reverse pass at (x, y, s) with cotangent grad_out."""
+        import torch
+        N, E = self._check_shapes(x, y, s, src, row_ptr)
+        if tuple(grad_out.shape) != (N, self.num_out, self.channels):
+            raise ValueError(f"grad_out must be (N, {self.num_out}, {self.channels})")
+        cot = tuple(t.contiguous() for t in (cot_x, cot_y, cot_s))
+        for t, ref, name in zip(cot, (x, y, s), ("cot_x", "cot_y", "cot_s")):
+            if tuple(t.shape) != tuple(ref.shape):
+                raise ValueError(f"{name} must have shape {tuple(ref.shape)}, got {tuple(t.shape)}")
+        if order is not None and order.numel() != N:
+            raise ValueError("order must have N entries")
+        if out is None:
+            out = (torch.empty_like(x), torch.empty_like(y), torch.empty_like(s),
+                   torch.empty_like(grad_out))
+        nr = N if num_real_nodes is None else int(num_real_nodes)
+        return e3conv_second_derivatives(self.handle, x, y, s, src, row_ptr, N, E, nr,
+                                         grad_out.contiguous(), *cot, *out, order=order, stream=stream)
+
 def _autograd_function():
     import torch
 
@@ -586,18 +653,9 @@ def _autograd_function():
         @staticmethod
         def backward(ctx, Gx, Gy, Gs):
             x, y, s, g = ctx.saved_tensors
-            plan = ctx.plan
             src, row_ptr, order, num_real = ctx.graph
-            Gx, Gy, Gs = (t.contiguous() for t in (Gx, Gy, Gs))
-            dx, dy, ds = torch.empty_like(x), torch.empty_like(y), torch.empty_like(s)
-            common = dict(order=order, num_real_nodes=num_real)
-            plan.backward(Gx, y, s, src, row_ptr, g, grads=(None, dy, ds), **common)
-            plan.backward(x, Gy, s, src, row_ptr, g, grads=(dx, None, ds),
-                          accumulate=(False, False, True), **common)
-            plan.backward(x, y, Gs, src, row_ptr, g, grads=(dx, dy, None),
-                          accumulate=(True, True, False), **common)
-            _, dg = plan.jvp(x, y, s, Gx, Gy, Gs, src, row_ptr, order=order, want_out=False,
-                             num_real_nodes=num_real)
+            dx, dy, ds, dg = ctx.plan.second_derivatives(x, y, s, src, row_ptr, g, Gx, Gy, Gs,
+                                                         order=order, num_real_nodes=num_real)
             return None, None, dx, dy, ds, dg
 
     class E3ConvFunction(torch.autograd.Function):

@@ -30,8 +30,9 @@
  *   normalization named on the e3j page);
  * - paths into the same output block add up.
  *
- * Memory and streams: every device pointer is owned by the caller; the library
- * never allocates device memory.  Tensors are dense, row-major, at least
+ * Memory and streams: every device pointer is owned by the caller; no compute
+ * call allocates device memory (only the synchronous checking convenience
+ * e3conv_validate_graph(on_device = 1) does).  Tensors are dense, row-major, at least
  * 16-byte aligned.  Indices are int32.  All device work is enqueued on the
  * caller's hipStream_t (passed as void*), asynchronously, with no implicit
  * synchronisation.  Errors are reported by status code; a human-readable
@@ -261,6 +262,29 @@ e3conv_status e3conv_backward_ex(e3conv_plan_t plan, e3conv_dtype in_dtype, cons
                                  float* grad_x, float* grad_y, float* grad_s, unsigned flags,
                                  void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Second derivatives of the training step (e3nn_mlx page: reverse over
+ * reverse).  With (grad_x, grad_y, grad_s) the reverse pass of L = <grad_out,
+ * out> at (x, y, s), and cotangents (cot_x, cot_y, cot_s) of those gradients,
+ * this writes the gradient of L2 = <cot_x, grad_x> + <cot_y, grad_y> +
+ * <cot_s, grad_s> with respect to x, y, s and grad_out:
+ *     d_x  = reverse(x, cot_y, s).grad_x + reverse(x, y, cot_s).grad_x,
+ *     d_y  = reverse(cot_x, y, s).grad_y + reverse(x, y, cot_s).grad_y,
+ *     d_s  = reverse(cot_x, y, s).grad_s + reverse(x, cot_y, s).grad_s,
+ *     d_grad_out = forward-mode derivative of out along (cot_x, cot_y, cot_s)
+ * (L2 = <grad_out, D out(x, y, s)[cot_x, cot_y, cot_s]>, and out is trilinear).
+ * Three general reverse passes and one forward-mode pass, enqueued on
+ * hip_stream; fp32 only.  Every array has the shape of its namesake (d_x and
+ * cot_x as x, d_grad_out as grad_out, ...); the outputs are overwritten.
+ * Graph arguments and num_real_nodes as e3conv_backward_ex. */
+e3conv_status e3conv_second_derivatives(e3conv_plan_t plan, e3conv_dtype in_dtype, const void* x,
+                                        const void* y, const void* s, const int32_t* src,
+                                        const int32_t* row_ptr, const int32_t* order,
+                                        int64_t num_nodes, int64_t num_edges,
+                                        int64_t num_real_nodes, const float* grad_out,
+                                        const float* cot_x, const float* cot_y,
+                                        const float* cot_s, float* d_x, float* d_y, float* d_s,
+                                        float* d_grad_out, void* hip_stream);
+
 /* Output linear: channel mixing within each output irrep block, the step
  * after the convolution (cuEquivariance page, Flax NNX layers, IrrepsLinear:
  * each block is mixed across its channels by a weight matrix and scaled by
@@ -310,12 +334,30 @@ e3conv_status e3conv_csr_from_receivers(const int32_t* receivers_sorted, int64_t
 e3conv_status e3conv_receiver_order(const int32_t* row_ptr, const int32_t* src, int64_t num_nodes,
                                     int64_t num_edges, int cluster, int32_t* order);
 
-/* Check a graph: row_ptr[0] = 0, non-decreasing, row_ptr[num_nodes] = num_edges,
- * every src in [0, num_nodes).  on_device = 0: host pointers; 1: device
- * pointers (runs a kernel on the default stream and waits for it).  Returns
- * E3CONV_OK or E3CONV_ERR_GRAPH with the first offending index in the detail. */
+/* Check a graph (the e3j Convolution page, __call__: indices lie in
+ * [0, num_nodes); the fused kernels need edges sorted by receiver): row_ptr[0]
+ * = 0, row_ptr non-decreasing and within [0, num_edges], row_ptr[num_nodes] =
+ * num_edges, every src in [0, num_nodes).  on_device = 0: host pointers, checked
+ * on the host.  on_device = 1: device pointers; a synchronous convenience that
+ * allocates a small device result buffer, runs the check on the default stream,
+ * waits for it and frees the buffer (use e3conv_validate_graph_async where
+ * that is not wanted).  Returns E3CONV_OK, or E3CONV_ERR_GRAPH with the
+ * first offending row_ptr index and/or edge in the detail. */
 e3conv_status e3conv_validate_graph(const int32_t* src, const int32_t* row_ptr,
                                     int64_t num_nodes, int64_t num_edges, int on_device);
+
+/* The device check of e3conv_validate_graph without allocation or
+ * synchronisation: enqueued on hip_stream, it writes into the caller's device
+ * buffer result (int32[4]): result[0] = number of violations (0: the graph is
+ * valid), result[1] = first index i with row_ptr[i] outside [0, num_edges]
+ * (or not 0 at i = 0, not num_edges at i = num_nodes) or with row_ptr[i + 1]
+ * < row_ptr[i] (INT32_MAX if none), result[2] = first edge whose sender is out of range
+ * (INT32_MAX if none), result[3] = 0.  The caller reads result after the
+ * stream reaches it.  E3CONV_ERR_INVALID_ARGUMENT for NULL pointers or sizes
+ * that do not fit int32 indices. */
+e3conv_status e3conv_validate_graph_async(const int32_t* src, const int32_t* row_ptr,
+                                          int64_t num_nodes, int64_t num_edges, int32_t* result,
+                                          void* hip_stream);
 
 /* Streaming reference (measurement aid, not part of the convolution): copies
  * `bytes` from src to dst with 16-byte non-temporal loads and stores, or, with
@@ -323,8 +365,7 @@ e3conv_status e3conv_validate_graph(const int32_t* src, const int32_t* row_ptr,
  * for plain streaming, the practical ceiling beside the published HBM peak,
  * and serves as the known-size kernel that scales memory counters.  bytes must
  * be a multiple of 16 and both buffers 16-byte aligned; asynchronous on
- * hip_stream.  A read-only pass never writes src unless its data sums to
- * 1234.5678 in some lane (calibration data must avoid that value). */
+ * hip_stream.  src is never written. */
 e3conv_status e3conv_stream_reference(const void* src, void* dst, size_t bytes, void* hip_stream);
 
 /* Tuning: select a kernel variant for this plan (0 = default).  Variants

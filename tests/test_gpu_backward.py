@@ -175,3 +175,83 @@ def test_autograd_function_matches_plan():
     for a, b in zip(grads, want):
         err = rel_err(a.cpu().numpy(), b.cpu().numpy())
         assert err <= 1e-5, err
+
+
+def _graph_with_degrees(deg, seed):
+    """Inputs of the training layout on a graph whose receiver b has deg[b] edges (senders
+    uniform, y spherical harmonics of random directions, x, s, g ~ N(0,1))."""
+    w = synth.WORKLOADS[4]
+    rng = np.random.default_rng(seed)
+    N = len(deg)
+    dst = np.repeat(np.arange(N), deg).astype(np.int32)
+    E_ = len(dst)
+    src = rng.integers(0, N, size=E_).astype(np.int32)
+    y = synth.spherical_harmonics(w.lmax, rng.standard_normal((E_, 3))).astype(np.float32)
+    x = rng.standard_normal((N, w.num_x, w.channels)).astype(np.float32)
+    s = rng.standard_normal((E_, w.num_paths, w.channels)).astype(np.float32)
+    g = rng.standard_normal((N, w.num_out, w.channels)).astype(np.float32)
+    return synth.Inputs(w, N, src, dst, x, y, s, g)
+
+
+DEGREE_PATTERNS = {
+    # one receiver owning every edge: tiles never change receiver
+    "one_hub": lambda rng: np.array([0, 0, 157, 0, 0], dtype=np.int64),
+    # 0-2 edges each: every tile crosses several receivers, empty rows in between
+    "sparse": lambda rng: rng.integers(0, 3, size=300),
+    # fewer edges than a tile, and a count that is not a multiple of the tile
+    "tiny": lambda rng: np.array([2, 0, 3], dtype=np.int64),
+    "ragged": lambda rng: np.concatenate([rng.integers(0, 40, size=60), [33]]),
+    # heavy tail: a few receivers with hundreds of edges among small ones
+    "heavy_tail": lambda rng: np.where(rng.random(400) < 0.02, rng.integers(100, 400, size=400),
+                                       rng.integers(0, 8, size=400)),
+}
+
+
+@pytest.mark.parametrize("pattern", sorted(DEGREE_PATTERNS))
+def test_backward_degree_patterns_all_variants(pattern):
+    """Every reverse variant on graphs built to stress tile and receiver boundaries."""
+    import torch
+    rng = np.random.default_rng(hash(pattern) % 1000)
+    inp = _graph_with_degrees(DEGREE_PATTERNS[pattern](rng), 7)
+    say(f"[backward degrees] {pattern} N={inp.num_nodes} E={inp.num_edges}")
+    dx_r, dy_r, ds_r = conv.backward(oracle_layout(inp), inp.x, inp.y, inp.s, inp.g, inp.senders,
+                                     inp.receivers, inp.num_nodes)
+    d = device_inputs(inp)
+    plan = plan_for(inp)
+    _, nb = plan.num_variants(E.E3CONV_F32)
+    for v in range(nb):
+        plan.set_variant(0, v)
+        gx, gy, gs = plan.backward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"], d["g"])
+        torch.cuda.synchronize()
+        errs = [rel_err(a.cpu().numpy(), b) for a, b in ((gx, dx_r), (gy, dy_r), (gs, ds_r))]
+        say(f"  variant {v}: max|err|/RMS dx {errs[0]:.3e} dy {errs[1]:.3e} ds {errs[2]:.3e}")
+        assert max(errs) <= 1e-5, (pattern, v, errs)
+
+
+def test_backward_padding_tail_every_variant():
+    """Node-mask padding (receivers from num_real_nodes on) through every default-path launcher:
+    their edges get zero grad_y / grad_s and send nothing to grad_x."""
+    import torch
+    rng = np.random.default_rng(3)
+    deg = rng.integers(0, 40, size=90)
+    inp = _graph_with_degrees(deg, 9)
+    n_real = 61
+    keep = inp.receivers < n_real
+    lay = oracle_layout(inp)
+    dx_r, dy_r, ds_r = conv.backward(lay, inp.x, inp.y[keep], inp.s[keep], inp.g,
+                                     inp.senders[keep], inp.receivers[keep], inp.num_nodes)
+    dy_full = np.zeros_like(inp.y, dtype=np.float64)
+    ds_full = np.zeros_like(inp.s, dtype=np.float64)
+    dy_full[keep], ds_full[keep] = dy_r, ds_r
+    d = device_inputs(inp)
+    plan = plan_for(inp)
+    _, nb = plan.num_variants(E.E3CONV_F32)
+    for v in range(nb):
+        plan.set_variant(0, v)
+        grads = tuple(torch.full_like(t, 7.0) for t in (d["x"], d["y"], d["s"]))
+        gx, gy, gs = plan.backward(d["x"], d["y"], d["s"], d["src"], d["row_ptr"], d["g"],
+                                   grads=grads, num_real_nodes=n_real)
+        torch.cuda.synchronize()
+        errs = [rel_err(a.cpu().numpy(), b) for a, b in ((gx, dx_r), (gy, dy_full), (gs, ds_full))]
+        assert max(errs) <= 1e-5, (v, errs)
+        assert float(gs[torch.from_numpy(~keep).cuda()].abs().max()) == 0.0
