@@ -3,7 +3,7 @@
 // fully connected network whose outputs weight the convolution's paths and
 // channels), for layouts of 32 channels, fp32.
 //
-//   f_k(r) = exp(-((r - mu_k) / sigma)^2) (1 + cos(pi r / r_max)) / 2,
+//   f_k(r) = exp(-((r - mu_k) / sigma)^2) (1 + cos(pi r / r_max)) / 2 (0 for r >= r_max),
 //   s[e]   = silu(f(r_e) W1) W2   -> (NP, C),
 //   out[b] = (1/N) sum_{e=(a->b)} (x[a] (x) y[e]) (.) s[e].
 //
@@ -522,7 +522,8 @@ __global__ void __launch_bounds__(64 * kRadialWaves) conv_fwd_radial(RadialParam
 
       // --- radial basis of this lane's edge (A-operand role)
       const float rr = r_cur;
-      const float cut = 0.5f * (1.0f + __cosf(6.283185307179586f * (rr * half_turns)));
+      // the cutoff vanishes from r_max on
+      const float cut = rr < prm.r_max ? 0.5f * (1.0f + __cosf(6.283185307179586f * (rr * half_turns))) : 0.0f;
       float f[kRadialMaxBasis];
 #pragma unroll
       for (int bb = 0; bb < kRadialMaxBasis; ++bb) {

@@ -174,7 +174,8 @@ e3conv_status e3conv_forward_masked(e3conv_plan_t plan, e3conv_dtype in_dtype, c
  * kernel (e3nn_mlx gate-points page: radial embedding of each edge length and
  * the fully connected network that maps it to the convolution's per-path,
  * per-channel weights; the network's two weight layers without biases):
- *     f_k(r) = exp(-((r - mu_k) / sigma)^2) * (1 + cos(pi r / r_max)) / 2,
+ *     f_k(r) = exp(-((r - mu_k) / sigma)^2) * (1 + cos(pi r / r_max)) / 2 for r < r_max,
+ *              0 for r >= r_max (the cosine cutoff vanishes from r_max on),
  *              mu_k = k r_max / (num_basis - 1),
  *     s[e]   = silu(f(r[e]) w1) w2, reshaped (num_paths, C), silu(z) = z / (1 + e^-z),
  * then out as e3conv_forward.  The scalars are formed per receiver in
@@ -185,8 +186,8 @@ e3conv_status e3conv_forward_masked(e3conv_plan_t plan, e3conv_dtype in_dtype, c
  * - w1 (num_basis, hidden), w2 (hidden, num_paths * C): fp32 device, row
  *   major; column p * C + c of w2 produces s[., p, c].
  * - 2 <= num_basis <= 8; hidden a multiple of 4 in [4, 128]; r_max, sigma > 0,
- *   else E3CONV_ERR_INVALID_ARGUMENT.  Edges with r >= r_max are not
- *   excluded; the cutoff makes their weight vanish at r = r_max.
+ *   else E3CONV_ERR_INVALID_ARGUMENT.  Edges with r >= r_max may be present:
+ *   their scalars, and so their messages, are zero.
  * - Compiled for layouts of 32 channels and at most 8 paths (the gate-points
  *   layout) in RECEIVER ordering; other plans give E3CONV_ERR_UNSUPPORTED.
  * - order and num_real_nodes as e3conv_forward_masked.

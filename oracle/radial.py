@@ -24,9 +24,10 @@ from . import conv
 
 
 def cutoff(r, r_max):
-    """Cosine cutoff (1 + cos(pi r / r_max)) / 2 on [0, r_max]."""
+    """Cosine cutoff: (1 + cos(pi r / r_max)) / 2 for r < r_max, 0 from r_max on (a cutoff
+    function vanishes beyond its radius; e3nn_mlx gate-points page, Scope: cosine cutoff)."""
     r = np.asarray(r, dtype=np.float64)
-    return 0.5 * (1.0 + np.cos(math.pi * r / r_max))
+    return np.where(r < r_max, 0.5 * (1.0 + np.cos(math.pi * r / r_max)), 0.0)
 
 
 def basis(r, num_basis, r_max, sigma):
@@ -78,7 +79,7 @@ def forward_radial_bruteforce(lay, x, y, r, w1, w2, r_max, sigma, senders, recei
     s = np.zeros((E, lay.num_paths * lay.channels))
     for e in range(E):
         re = float(r[e])
-        cut = 0.5 * (1.0 + math.cos(math.pi * re / r_max))
+        cut = 0.5 * (1.0 + math.cos(math.pi * re / r_max)) if re < r_max else 0.0
         f = [math.exp(-(((re - k * r_max / (nb - 1)) / sigma) ** 2)) * cut for k in range(nb)]
         for j in range(hid):
             z = sum(f[k] * w1[k, j] for k in range(nb))

@@ -149,6 +149,25 @@ def test_radial_network_shapes(nb, hidden, sigma):
     assert err <= 1e-5
 
 
+def test_radial_edges_beyond_the_cutoff():
+    """Edge lengths past r_max carry no message (the cutoff is zero there), also where the
+    cosine alone would not vanish (r = 1.5 r_max, 2 r_max)."""
+    x, y, r, src, dst, N = handmade([7, 30, 0, 18, 4], seed=21)
+    rng = np.random.default_rng(22)
+    far = rng.random(len(r)) < 0.4
+    r = np.where(far, rng.choice([2.0, 2.5, 3.0, 4.0], size=len(r)), r).astype(np.float32)
+    _, w1, w2 = synth.radial_inputs(synth.make_inputs(1, num_graphs=1))
+    ref = radial.forward_radial(lay(), x, y, r, w1, w2, 2.0, 0.5, src, dst, N)
+    got = run(x, y, r, w1, w2, src, dst, N)
+    err = rel_err(got, ref)
+    # the same graph without the far edges gives the same result
+    near = ~far
+    ref_near = radial.forward_radial(lay(), x, y[near], r[near], w1, w2, 2.0, 0.5, src[near], dst[near], N)
+    say(f"[radial beyond cutoff] {int(far.sum())} of {len(r)} edges past r_max: {err:.3e}")
+    assert err <= 1e-5
+    np.testing.assert_allclose(ref, ref_near, rtol=0, atol=1e-12 * max(1.0, float(np.abs(ref).max())))
+
+
 def test_radial_graph_without_edges():
     """No edges at all: every output row is zero (receivers and padding alike)."""
     import torch
