@@ -862,14 +862,17 @@ def bench_radial(args):
            "plain_forward_ms_with_precomputed_s": plain_ms,
            "unfused_ms_torch_network_then_forward": unfused_ms,
            "scalar_bytes_not_moved": 2.0 * Ec * P * C * 4,
-           "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                        "frac": tf / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
-                        "kernel": ("conv_fwd_radial: the network's fp32 products at fp32 accuracy against the "
-                                   "fp32 matrix peak; the second layer issues three fp16 matrix products per "
-                                   "fp32 product (two-part operands), the tensor product runs on the VALU"),
+           "roofline": {"bound": "mfma", "achieved": issued / (fused_ms * 1e-3) / 1e12,
+                        "peak": PEAK_FP16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                        "frac": issued / (fused_ms * 1e-3) / 1e12 / PEAK_FP16_MFMA_TFLOPS, "traffic": None,
+                        "kernel": ("conv_fwd_radial: the fp16 matrix work its network's second layer issues "
+                                   "(three fp16 products per fp32 product of two-part operands, tiles of four "
+                                   "quads, hidden units padded to 32) against the dense fp16 matrix peak; the "
+                                   "tensor product runs on the VALU"),
+                        "issued_fp16_flops": issued,
                         "algorithmic_flops": flops,
-                        "fp16_issued_TFLOPs": issued / (fused_ms * 1e-3) / 1e12,
-                        "fp16_peak_TFLOPs": PEAK_FP16_MFMA_TFLOPS}}
+                        "fp32_equivalent_TFLOPs": tf,
+                        "fp32_equivalent_frac_of_fp32_matrix_peak": tf / PEAK_FP32_MFMA_TFLOPS}}
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits
         from oracle import conv, radial
