@@ -1,12 +1,16 @@
 // Graph checks (e3j Convolution page, __call__: sender and receiver indices lie
 // in [0, num_nodes), and the fused kernels need the edges sorted by receiver,
-// i.e. a valid receiver CSR).  Host check, and two device forms:
+// i.e. a valid receiver CSR).  Host check, and three device forms:
 //   e3conv_validate_graph(on_device = 1)   synchronous, allocates its result;
-//   e3conv_validate_graph_async            caller-owned result, asynchronous.
+//   e3conv_validate_graph_async            caller-owned result, asynchronous;
+//   e3conv_validate_graph_noalloc          synchronous, result in a static
+//                                          device array (allocates nothing).
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "e3conv.h"
 #include "kernels.h"
@@ -44,6 +48,33 @@ __global__ void validate_kernel(const int* __restrict__ src, const int* __restri
       atomicMin(r + 2, (int)i);
     }
   }
+}
+
+// Result array of e3conv_validate_graph_noalloc.  One copy per device, held
+// until the process ends.  Host code never uses this name as an address: the
+// device address comes from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) int scratch[kValidateResultInts];
+
+std::mutex g_scratch_mu;
+std::vector<int*> g_scratch_ptr;   // per device id; nullptr until looked up
+
+// Device address of `scratch` on the current device (looked up once per
+// device, with that device current).
+hipError_t scratch_address(int** out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<int*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_validate(const int* src, const int* row_ptr, int num_nodes, int num_edges, int* r,
@@ -126,6 +157,23 @@ e3conv_status e3conv_validate_graph_async(const int32_t* src, const int32_t* row
       e3c::launch_validate(src, row_ptr, (int)N, (int)E, result, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return e3c::api_hip_fail(err, "validate launch");
   return e3c::api_ok();
+}
+
+e3conv_status e3conv_validate_graph_noalloc(const int32_t* src, const int32_t* row_ptr, int64_t N,
+                                            int64_t E, void* stream) {
+  e3conv_status st = e3c::check_args(src, row_ptr, N, E);
+  if (st != E3CONV_OK) return st;
+  int* r = nullptr;
+  hipError_t err = e3c::scratch_address(&r);
+  if (err != hipSuccess) return e3c::api_hip_fail(err, "scratch address");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int host[e3c::kValidateResultInts] = {};
+  // the first kernel of launch_validate resets the array before the check writes it
+  err = e3c::launch_validate(src, row_ptr, (int)N, (int)E, r, s);
+  if (err == hipSuccess) err = hipMemcpyAsync(host, r, sizeof(host), hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  if (err != hipSuccess) return e3c::api_hip_fail(err, "validate");
+  return e3c::report(host);
 }
 
 }  // extern "C"

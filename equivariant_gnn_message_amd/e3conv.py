@@ -37,7 +37,8 @@ EXPORTED = [
     "e3conv_plan_coefficients", "e3conv_plan_supported", "e3conv_forward", "e3conv_forward_masked",
     "e3conv_forward_radial", "e3conv_jvp", "e3conv_backward_workspace_size", "e3conv_backward", "e3conv_backward_ex",
     "e3conv_linear", "e3conv_linear_backward", "e3conv_csr_from_receivers",
-    "e3conv_validate_graph", "e3conv_validate_graph_async", "e3conv_receiver_order",
+    "e3conv_validate_graph", "e3conv_validate_graph_async", "e3conv_validate_graph_noalloc",
+    "e3conv_receiver_order",
     "e3conv_stream_reference", "e3conv_second_derivatives",
     "e3conv_plan_set_variant",
     "e3conv_plan_num_variants",
@@ -106,6 +107,7 @@ def load_library(path=LIB_PATH):
         "e3conv_csr_from_receivers": ([P, I64, I64, P, P], ctypes.c_int),
         "e3conv_validate_graph": ([P, P, I64, I64, ctypes.c_int], ctypes.c_int),
         "e3conv_validate_graph_async": ([P, P, I64, I64, P, P], ctypes.c_int),
+        "e3conv_validate_graph_noalloc": ([P, P, I64, I64, P], ctypes.c_int),
         "e3conv_second_derivatives": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P, P, P, P,
                                        P, P, P, P, P], ctypes.c_int),
         "e3conv_plan_set_variant": ([P, ctypes.c_int, ctypes.c_int], ctypes.c_int),
@@ -415,6 +417,16 @@ def e3conv_validate_graph_async(src, row_ptr, num_nodes, num_edges, result=None,
     _check(load_library().e3conv_validate_graph_async(_ptr(src), _ptr(row_ptr), int(num_nodes),
                                                       int(num_edges), _ptr(result), _stream(stream)))
     return result
+
+
+def e3conv_validate_graph_noalloc(src, row_ptr, num_nodes, num_edges, stream=None):
+    """Device graph check without allocation (the library's static result array); raises
+    E3ConvError(E3CONV_ERR_GRAPH) on a bad graph."""
+    import torch
+    _need(src, "src", torch.int32)
+    _need(row_ptr, "row_ptr", torch.int32)
+    _check(load_library().e3conv_validate_graph_noalloc(_ptr(src), _ptr(row_ptr), int(num_nodes),
+                                                        int(num_edges), _stream(stream)))
 
 
 def e3conv_second_derivatives(handle, x, y, s, src, row_ptr, num_nodes, num_edges, num_real_nodes,

@@ -360,6 +360,21 @@ e3conv_status e3conv_validate_graph_async(const int32_t* src, const int32_t* row
                                           int64_t num_nodes, int64_t num_edges, int32_t* result,
                                           void* hip_stream);
 
+/* e3conv_validate_graph(on_device = 1) for callers that cannot allocate
+ * device memory (serving loops and harnesses that forbid hipMalloc): the same
+ * check, status and detail, with the 4-int result held in a static device
+ * array of the library (one per device, allocated with the code object and
+ * kept until the process ends) instead of a per-call allocation.  The check
+ * is enqueued on hip_stream, which the call then synchronises (it reads the
+ * result back).  The array's size does not depend on the graph; sizes are
+ * limited as for e3conv_validate_graph (int32 indices), else
+ * E3CONV_ERR_INVALID_ARGUMENT.  Every call on one device shares that array:
+ * calls that overlap on one device (from several threads or streams) race
+ * and must be serialised by the caller. */
+e3conv_status e3conv_validate_graph_noalloc(const int32_t* src, const int32_t* row_ptr,
+                                            int64_t num_nodes, int64_t num_edges,
+                                            void* hip_stream);
+
 /* Streaming reference (measurement aid, not part of the convolution): copies
  * `bytes` from src to dst with 16-byte non-temporal loads and stores, or, with
  * dst = NULL, only reads src.  It measures the bandwidth this device attains
