@@ -59,12 +59,3 @@ def parse(s):
         out.append((mul, int(m.group(2)), 1 if m.group(3) == "e" else -1))
     return out
 
-
-def dim(blocks):
-    """Number of components per channel: sum of 2l+1 over blocks."""
-    return sum(2 * l + 1 for (_, l, _) in blocks)
-
-
-def sh_irreps(lmax):
-    """Irreps of real spherical harmonics 0..lmax: l with parity (-1)^l."""
-    return [(1, l, (-1) ** l) for l in range(lmax + 1)]
