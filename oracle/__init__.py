@@ -23,7 +23,8 @@ irreps  -- irreps string parser (``"8x0e+8x1o"``, ``"64x(0e+1o+2e)"``).
 so3     -- Racah complex CG, complex->real basis change, real CG tensors,
            real Wigner D matrices from the exponential map of generators.
 conv    -- path enumeration, brute-force and vectorised forward, backward.
-variants -- SENDER graph ordering, node_mask padding, forward-mode and second
+variants -- SENDER graph ordering, pair storage (one row of y and s per
+           undirected pair), node_mask padding, forward-mode and second
            derivatives, built from ``conv``.
 linear  -- the output linear (channel mixing per irrep block) and its gradients.
 radial  -- edge scalars from edge lengths (radial basis, cutoff, two-layer

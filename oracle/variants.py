@@ -15,6 +15,15 @@ Built from ``oracle.conv`` without new arithmetic of its own:
   padding nodes.  Read plainly: the messages of edges into padding receivers
   are dropped and the rows of padding nodes are zero; the reverse pass is the
   derivative of that function.
+* pair storage (same page, same note: every edge a -> b has its reverse
+  b -> a, y_ba = (-1)^l y_ab per l block, s_ba = s_ab).  Read plainly, those
+  assumptions let a symmetric graph keep one row of y and s per undirected
+  pair: a stored edge e = (a -> b) stands for itself and for its reverse
+  (b -> a) with features P y[e] (odd-l blocks negated) and scalars s[e].  The
+  function of the stored arrays is the RECEIVER convolution of those 2 E
+  directed edges (a stored self loop a -> a therefore counts twice); its
+  reverse pass follows by the chain rule: grad_y[e] = dy(a -> b) +
+  P dy(b -> a) and grad_s[e] = ds(a -> b) + ds(b -> a).
 * forward-mode derivative and second derivatives (e3nn_mlx page, "JVP and
   generated-kernel boundary"): the convolution is trilinear in (x, y, s), so
   by the product rule its derivative along (dx, dy, ds) is
@@ -46,6 +55,33 @@ def backward_sender(lay, x, y, s, g, senders, receivers, num_nodes):
     y_rev = np.asarray(y, dtype=np.float64) * sign
     dx, dy_rev, ds = conv.backward(lay, x, y_rev, s, g, receivers, senders, num_nodes)
     return dx, dy_rev * sign, ds
+
+
+def expand_pairs(lay, y, s, senders, receivers):
+    """The directed edges that the stored pairs stand for: the stored edges
+    (a -> b) with y and s, then their reverses (b -> a) with P y and s.
+    Returns (y2, s2, senders2, receivers2) of length 2 E."""
+    y = np.asarray(y, dtype=np.float64)
+    s = np.asarray(s, dtype=np.float64)
+    a = np.asarray(senders)
+    b = np.asarray(receivers)
+    return (np.concatenate([y, y * parity_sign(lay)]), np.concatenate([s, s]),
+            np.concatenate([a, b]), np.concatenate([b, a]))
+
+
+def forward_pairs(lay, x, y, s, senders, receivers, num_nodes):
+    """Pair storage: the RECEIVER convolution of every stored edge and its reverse."""
+    y2, s2, a2, b2 = expand_pairs(lay, y, s, senders, receivers)
+    return conv.forward(lay, x, y2, s2, a2, b2, num_nodes)
+
+
+def backward_pairs(lay, x, y, s, g, senders, receivers, num_nodes):
+    """Gradients of ``forward_pairs``: each stored row collects the gradients
+    of both directed edges it stands for (the reverse one through P)."""
+    y2, s2, a2, b2 = expand_pairs(lay, y, s, senders, receivers)
+    dx, dy2, ds2 = conv.backward(lay, x, y2, s2, g, a2, b2, num_nodes)
+    m = len(senders)
+    return dx, dy2[:m] + dy2[m:] * parity_sign(lay), ds2[:m] + ds2[m:]
 
 
 def edges_into_real(receivers, num_real):

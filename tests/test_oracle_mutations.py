@@ -153,3 +153,51 @@ def test_radial_mistakes_are_caught(monkeypatch, name):
     elif name == "half_period":       # cos(pi r / (2 r_max))
         monkeypatch.setattr(radial, "cutoff", lambda r, r_max: orig_cut(r, 2.0 * r_max))
     assert not radial_pins_ok()
+
+
+# ---------------------------------------------- pair storage (variants) -----
+
+def pair_pins_ok():
+    from .test_oracle_variants import pairs_backward_is_derivative, pairs_equal_receiver
+    return pairs_equal_receiver(2) and pairs_backward_is_derivative(2)
+
+
+def test_unpatched_pair_oracle_passes_its_pins():
+    assert pair_pins_ok()
+
+
+@pytest.mark.parametrize("name", ["reverse_y_unflipped", "reverse_edges_dropped",
+                                  "grad_y_fold_unflipped", "grad_s_one_direction",
+                                  "grad_x_one_direction"])
+def test_pair_mistakes_are_caught(monkeypatch, name):
+    from oracle import variants
+    expand = variants.expand_pairs
+
+    def fold(dy_sign, both_s, both_x):
+        def backward_pairs(lay, x, y, s, g, senders, receivers, num_nodes):
+            y2, s2, a2, b2 = expand(lay, y, s, senders, receivers)
+            m = len(senders)
+            dx, dy2, ds2 = conv.backward(lay, x, y2, s2, g, a2, b2, num_nodes)
+            if not both_x:
+                dx = conv.backward(lay, x, y2[:m], s2[:m], g, a2[:m], b2[:m], num_nodes)[0]
+            sign = variants.parity_sign(lay) if dy_sign else 1.0
+            return dx, dy2[:m] + dy2[m:] * sign, ds2[:m] + (ds2[m:] if both_s else 0.0)
+        return backward_pairs
+
+    if name == "reverse_y_unflipped":
+        def expand_bad(lay, y, s, senders, receivers):
+            y2, s2, a2, b2 = expand(lay, y, s, senders, receivers)
+            m = len(senders)
+            y2[m:] = y2[:m]
+            return y2, s2, a2, b2
+        monkeypatch.setattr(variants, "expand_pairs", expand_bad)
+    elif name == "reverse_edges_dropped":
+        monkeypatch.setattr(variants, "forward_pairs",
+                            lambda lay, x, y, s, a, b, n: conv.forward(lay, x, y, s, a, b, n))
+    elif name == "grad_y_fold_unflipped":
+        monkeypatch.setattr(variants, "backward_pairs", fold(False, True, True))
+    elif name == "grad_s_one_direction":
+        monkeypatch.setattr(variants, "backward_pairs", fold(True, False, True))
+    else:
+        monkeypatch.setattr(variants, "backward_pairs", fold(True, True, False))
+    assert not pair_pins_ok()

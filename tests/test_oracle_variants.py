@@ -190,3 +190,112 @@ def test_double_backward_central_difference_identity(idx):
         minus = L2(*[a - b for a, b in zip(p, dk)])
         comp = (dx, dy, ds, dg)[k]
         assert abs(np.vdot(comp, d[k]) - (plus - minus) / 2) <= 1e-10 * (abs(plus) + abs(minus) + 1.0)
+
+
+# --------------------------------------------------------- pair storage -----
+
+def radial_symmetric_case(idx, seed=0, n=40, side=3.0, r=1.4, C=3):
+    """Radius graph (both directions), geometric y and distance-based s: the
+    gate-points recipe, whose scalars are symmetric because |v_ab| = |v_ba|."""
+    lay = layout_of(idx, C)
+    rng = np.random.default_rng(seed)
+    pos = rng.uniform(0.0, side, (n, 3))
+    src, dst = synth.radius_graph(pos, r)
+    vec = synth.edge_vectors(pos, src, dst)
+    y = synth.spherical_harmonics(lay.lmax, vec)
+    s = synth.radial_mlp_scalars(np.linalg.norm(vec, axis=1), lay.num_paths * C, r)
+    s = s.reshape(len(src), lay.num_paths, C)
+    x = rng.standard_normal((n, lay.num_x, C))
+    g = rng.standard_normal((n, lay.num_out, C))
+    return lay, x, y, s, g, src, dst, n
+
+
+def pairs_equal_receiver(idx, seed=0):
+    """On a symmetric radius graph, the pairs stored once (sender < receiver)
+    give the directed RECEIVER forward, grad_x, and grad_s = the sum of the
+    two directed edges' grad_s (the reverse edges' features recomputed from
+    the reversed vectors, not by a sign table)."""
+    lay, x, y, s, g, src, dst, n = radial_symmetric_case(idx, seed)
+    keep = src < dst
+    ps, pd = src[keep], dst[keep]
+    ok = rel_max_err(variants.forward_pairs(lay, x, y[keep], s[keep], ps, pd, n),
+                     conv.forward(lay, x, y, s, src, dst, n)) < 1e-12
+    rx, ry, rs = conv.backward(lay, x, y, s, g, src, dst, n)
+    gx, gy, gs = variants.backward_pairs(lay, x, y[keep], s[keep], g, ps, pd, n)
+    # directed index of each stored pair's reverse edge
+    where = {(int(a), int(b)): e for e, (a, b) in enumerate(zip(src, dst))}
+    rev = np.array([where[(int(b), int(a))] for a, b in zip(ps, pd)])
+    ok = ok and rel_max_err(gx, rx) < 1e-12
+    ok = ok and rel_max_err(gs, rs[keep] + rs[rev]) < 1e-12
+    return ok
+
+
+def random_pairs(idx, seed=4, n=14, E=40):
+    lay = layout_of(idx)
+    rng = np.random.default_rng(seed)
+    src = rng.integers(0, n, E)
+    dst = rng.integers(0, n, E)
+    src[0] = dst[0]                                 # a stored self loop
+    src[1], dst[1] = src[2], dst[2]                 # a duplicate pair
+    x = rng.standard_normal((n, lay.num_x, lay.channels))
+    y = synth.spherical_harmonics(lay.lmax, rng.standard_normal((E, 3)))
+    s = rng.standard_normal((E, lay.num_paths, lay.channels))
+    g = rng.standard_normal((n, lay.num_out, lay.channels))
+    return lay, x, y, s, g, src, dst, n
+
+
+def pairs_backward_is_derivative(idx, seed=4):
+    """<grad, d> equals the directional derivative of <g, forward_pairs>
+    (trilinear: the central difference at h = 1 minus the cubic term)."""
+    lay, x, y, s, g, src, dst, n = random_pairs(idx, seed)
+    rng = np.random.default_rng(seed + 100)
+    d = [rng.standard_normal(a.shape) for a in (x, y, s)]
+    L = lambda a, b, c: np.vdot(g, variants.forward_pairs(lay, a, b, c, src, dst, n))
+    deriv = _directional(L, (x, y, s), d) - L(*d)
+    grads = variants.backward_pairs(lay, x, y, s, g, src, dst, n)
+    ok = True
+    for k in range(3):                          # each operand on its own
+        dk = [np.zeros_like(a) for a in d]
+        dk[k] = d[k]
+        dir_k = _directional(L, (x, y, s), dk)
+        ok = ok and abs(np.vdot(grads[k], d[k]) - dir_k) <= 1e-10 * (abs(dir_k) + 1.0)
+    pred = sum(np.vdot(a, b) for a, b in zip(grads, d))
+    return ok and abs(pred - deriv) <= 1e-10 * (abs(deriv) + 1.0)
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3])
+def test_pairs_equal_receiver_on_symmetric_radius_graph(idx):
+    assert pairs_equal_receiver(idx)
+
+
+@pytest.mark.parametrize("idx", [0, 2, 3])
+def test_pairs_backward_matches_directional_derivative(idx):
+    assert pairs_backward_is_derivative(idx)
+
+
+@pytest.mark.parametrize("idx", [0, 3])
+def test_pairs_stored_orientation_does_not_matter(idx):
+    """Storing a pair as (b -> a) with P y instead of (a -> b) with y is the
+    same function: forward and grad_x unchanged, grad_s unchanged, grad_y
+    mapped by P (P is its own inverse)."""
+    lay, x, y, s, g, src, dst, n = random_pairs(idx, seed=9)
+    flip = np.arange(len(src)) % 3 == 1
+    P = variants.parity_sign(lay)
+    src2, dst2 = np.where(flip, dst, src), np.where(flip, src, dst)
+    y2 = np.where(flip[:, None], y * P, y)
+    assert rel_max_err(variants.forward_pairs(lay, x, y2, s, src2, dst2, n),
+                       variants.forward_pairs(lay, x, y, s, src, dst, n)) < 1e-12
+    gx, gy, gs = variants.backward_pairs(lay, x, y, s, g, src, dst, n)
+    gx2, gy2, gs2 = variants.backward_pairs(lay, x, y2, s, g, src2, dst2, n)
+    assert rel_max_err(gx2, gx) < 1e-12 and rel_max_err(gs2, gs) < 1e-12
+    assert rel_max_err(gy2, np.where(flip[:, None], gy * P, gy)) < 1e-12
+
+
+def test_pairs_need_symmetric_scalars():
+    """With scalars that differ between an edge and its reverse, the pair
+    function is not the directed RECEIVER result (the pin above is not vacuous)."""
+    lay, x, y, s, g, src, dst, n = radial_symmetric_case(2)
+    s_dir = np.random.default_rng(1).standard_normal(s.shape)
+    keep = src < dst
+    got = variants.forward_pairs(lay, x, y[keep], s_dir[keep], src[keep], dst[keep], n)
+    assert rel_max_err(got, conv.forward(lay, x, y, s_dir, src, dst, n)) > 1e-2
