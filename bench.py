@@ -60,11 +60,13 @@ def parse():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (counter calibration) and exit")
     ap.add_argument("--mode", default="conv",
-                    choices=("conv", "sender", "jvp", "second", "linear", "radial"),
+                    choices=("conv", "sender", "jvp", "second", "linear", "radial", "pairs"),
                     help="conv: the hot path (default); sender: SENDER graph ordering; "
                          "jvp: fused forward-mode pass; second: second derivatives of the "
                          "training step; linear: output linear; radial: edge scalars from "
-                         "edge lengths in the kernel (gate-points workload) (one line each)")
+                         "edge lengths in the kernel (gate-points workload); pairs: reverse pass "
+                         "with y and s stored once per undirected pair against the directed "
+                         "reverse pass on the same symmetric graph (one line each)")
     return ap.parse_args()
 
 
@@ -520,6 +522,7 @@ def main():
         del x, y, s, g, grads, out, order, order_dev, src, dst, row_ptr
         torch.cuda.empty_cache()
         res["w3_forward"] = bench_forward_workload(3, args)
+        res["pairs_reverse"] = pairs_block(plan, w, inp, res["bwd_ms"], args)
     print(json.dumps(res), flush=True)
 
 
@@ -651,6 +654,9 @@ def bench_mode(args):
     if args.mode == "radial":
         bench_radial(args)
         return
+    if args.mode == "pairs":
+        bench_pairs(args)
+        return
     w = synth.WORKLOADS[args.workload]
     inp = synth.make_inputs(args.workload)
     N, Ec = inp.num_nodes, inp.num_edges
@@ -740,6 +746,121 @@ def bench_mode(args):
     flops = {"forward": forward_flops_per_edge(plan) * Ec, "jvp": jvp_flops_per_edge(plan) * Ec}
     res["roofline"] = roofline(k, ms, by, flops.get(k))
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_mode(args.mode, inp, args.cpu_sample_edges)
+    print(json.dumps(res), flush=True)
+
+
+def pair_bytes(w, N, Ep):
+    """Compulsory bytes of the pair-stored reverse pass: x and g read, grad_x
+    written once; per stored edge y, s, src, dst read and grad_y, grad_s written."""
+    C, nx, ny, no, P = w.channels, w.num_x, (w.lmax + 1) ** 2, w.num_out, w.num_paths
+    return 4 * (2 * N * nx * C + N * no * C + Ep * (2 * ny + 2 * P * C + 2))
+
+
+def pair_inputs(inp):
+    """Pair storage of a workload's symmetric radius graph: the stored edges (sender <
+    receiver, grouped by receiver), their y rows, one seeded N(0,1) row of s per pair,
+    and for each directed edge its pair."""
+    from equivariant_gnn_message_amd import synth
+    w = inp.workload
+    stored, pair_of = synth.pair_index(inp.senders, inp.receivers)
+    s_pair = synth.normal_f32(w.idx, synth.T_S_PAIR, (len(stored), w.num_paths, w.channels))
+    return stored, pair_of, s_pair
+
+
+def time_pairs_reverse(plan, w, inp, stored, s_pair, args):
+    """HIP-event time (ms) of the pair-stored reverse pass on the device copies."""
+    import numpy as np
+    import torch
+
+    from equivariant_gnn_message_amd import e3conv as E
+    N, Ep = inp.num_nodes, len(stored)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    x, g = t(inp.x), t(inp.g)
+    y, s = t(inp.y[stored]), t(s_pair)
+    src, dst = t(inp.senders[stored].astype(np.int32)), t(inp.receivers[stored].astype(np.int32))
+    gx, gy, gs = torch.empty_like(x), torch.empty_like(y), torch.empty_like(s)
+    ms = _timed(lambda: E.e3conv_backward_pairs(plan.handle, x, y, s, src, dst, N, Ep, g, gx, gy, gs),
+                args.steps, args.warmup)
+    del x, g, y, s, src, dst, gx, gy, gs
+    torch.cuda.empty_cache()
+    return ms
+
+
+def pairs_block(plan, w, inp, directed_ms, args):
+    """The pair-stored reverse pass on the training graph (one s row per pair) next to
+    the directed reverse pass of the same graph (its time does not depend on the values)."""
+    stored, _, s_pair = pair_inputs(inp)
+    N, Ec, Ep = inp.num_nodes, inp.num_edges, len(stored)
+    ms = time_pairs_reverse(plan, w, inp, stored, s_pair, args)
+    nbytes = pair_bytes(w, N, Ep)
+    dir_bytes = alg_bytes(w, N, Ec, 4)[1]
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"{w.name}: reverse pass, y and s stored once per undirected pair, N={N}, "
+                        f"{Ep} pairs ({Ec} directed edges)",
+            "ms": ms, "directed_edges_per_s": Ec / (ms * 1e-3), "algorithmic_bytes": nbytes,
+            "hbm_GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS,
+            "directed_reverse_ms": directed_ms, "directed_algorithmic_bytes": dir_bytes,
+            "speedup_vs_directed": directed_ms / ms}
+
+
+def bench_pairs(args):
+    """Reverse pass of the training graph with symmetric scalars: directed storage
+    (every edge its own y and s rows) against pair storage (one row per pair)."""
+    import numpy as np
+    import torch
+
+    from equivariant_gnn_message_amd import e3conv as E
+    from equivariant_gnn_message_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if not w.backward or w.dtype != "f32":
+        raise SystemExit("--mode pairs needs the fp32 training workload (4)")
+    inp = synth.make_inputs(args.workload)
+    N, Ec = inp.num_nodes, inp.num_edges
+    stored, pair_of, s_pair = pair_inputs(inp)
+    Ep = len(stored)
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    # directed: the same graph with s expanded to both directions of each pair
+    x, y, g = t(inp.x), t(inp.y), t(inp.g)
+    s = t(s_pair)[t(pair_of)]
+    src = t(inp.senders)
+    row_ptr = E.e3conv_csr_from_receivers(t(inp.receivers), N)
+    grads = (torch.empty_like(x), torch.empty_like(y), torch.empty_like(s))
+    dir_ms = _timed(lambda: plan.backward(x, y, s, src, row_ptr, g, grads=grads), args.steps, args.warmup)
+    del x, y, g, s, src, row_ptr, grads
+    torch.cuda.empty_cache()
+    pair_ms = time_pairs_reverse(plan, w, inp, stored, s_pair, args)
+    pb, db = pair_bytes(w, N, Ep), alg_bytes(w, N, Ec, 4)[1]
+    res = {"metric": "directed edges/sec of the reverse pass, y and s stored once per undirected pair, "
+                     "1 MI355X",
+           "value": Ec / (pair_ms * 1e-3), "unit": "edges/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": pair_ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"{w.name}: reverse pass on the radius graph N={N} E={Ec} "
+                                  f"({Ep} undirected pairs), one N(0,1) row of s per pair",
+                      "mode": "pairs"},
+           "pairs_ms": pair_ms, "pairs_algorithmic_bytes": pb,
+           "pairs_hbm_GBps": pb / (pair_ms * 1e-3) / 1e9,
+           "directed_ms": dir_ms, "directed_algorithmic_bytes": db,
+           "directed_hbm_GBps": db / (dir_ms * 1e-3) / 1e9,
+           "speedup_vs_directed": dir_ms / pair_ms,
+           "roofline": roofline("conv_bwd_pairs", pair_ms, pb)}
+    res["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import conv, variants
+        lay = conv.make_layout(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+        k = min(args.cpu_sample_edges // 8, Ep)
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            variants.backward_pairs(lay, inp.x, inp.y[stored[:k]], s_pair[:k], inp.g,
+                                    inp.senders[stored[:k]], inp.receivers[stored[:k]], N)
+            dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": 2 * k / dt, "unit": "edges/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {k} pairs ({2 * k} directed edges), pair-stored "
+                                         f"reverse pass, fp64 numpy, {dt:.1f} s"}
     print(json.dumps(res), flush=True)
 
 

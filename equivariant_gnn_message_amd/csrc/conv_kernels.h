@@ -197,6 +197,81 @@ __device__ __forceinline__ void build_k(const float (&yv)[LY::NY], float (&K)[D3
   });
 }
 
+// Orders a wave's LDS accesses around an exchange between its lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Adds a group's partial rows v into dst (NR rows of C floats) with fp32
+// atomics.  Lane li holds channels li*CPL .. li*CPL+CPL-1 of each row; the
+// rows are re-laid through the group's LDS rows xt (NR * C floats) so that
+// lane li adds channels li + c*LPG, and each atomic instruction of the group
+// covers consecutive channels.
+template <int C, int NR, int CPL, int LPG>
+__device__ __forceinline__ void atomic_add_rows(float* dst, const float (&v)[NR][CPL], float* xt,
+                                                int li) {
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    if constexpr (CPL == 4) {
+      *reinterpret_cast<f32x4*>(xt + i * C + li * 4) = f32x4{v[i][0], v[i][1], v[i][2], v[i][3]};
+    } else if constexpr (CPL == 2) {
+      *reinterpret_cast<f32x2*>(xt + i * C + li * 2) = f32x2{v[i][0], v[i][1]};
+    } else {
+      xt[i * C + li] = v[i][0];
+    }
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) unsafeAtomicAdd(dst + i * C + li + c * LPG, xt[i * C + li + c * LPG]);
+  wave_lds_sync();
+}
+
+// Sums the group's per-lane partial edge-feature gradients dyp (NY used of
+// pow2_ceil(NY)) over its LPG lanes and writes the row dst[0 .. NY), or adds
+// it when acc.  Each butterfly step halves the components a lane keeps, so
+// the sum costs NYP - 1 shuffles rather than NY log2(LPG).
+template <int NY, int LPG>
+__device__ __forceinline__ void store_dy(float (&dyp)[pow2_ceil(NY)], float* dst, int li, bool acc) {
+  constexpr int NYP = pow2_ceil(NY);
+  constexpr int STEPS = ilog2(LPG);
+  sfor<0, STEPS>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int d = LPG >> (k + 1);
+    constexpr int n = (NYP >> k) > 1 ? (NYP >> k) : 1;
+    if constexpr (n > 1) {
+      const bool upper = (li & d) != 0;
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) {
+        const float send = upper ? dyp[i] : dyp[i + n / 2];
+        const float keep = upper ? dyp[i + n / 2] : dyp[i];
+        dyp[i] = keep + __shfl_xor(send, d, 64);
+      }
+    } else {
+      dyp[0] += __shfl_xor(dyp[0], d, 64);
+    }
+  });
+  constexpr int NF = (NYP >> STEPS) > 1 ? (NYP >> STEPS) : 1;
+  constexpr int REP = LPG > NYP ? LPG / NYP : 1;
+  if ((li & (REP - 1)) == 0) {
+    int base = 0;
+#pragma unroll
+    for (int k = 0; k < STEPS; ++k) {
+      const int d = LPG >> (k + 1);
+      const int n = (NYP >> k) > 1 ? (NYP >> k) : 1;
+      if (n > 1 && (li & d)) base += n / 2;
+    }
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const int comp = base + j;
+      if (comp < NY) dst[comp] = acc ? dyp[j] + dst[comp] : dyp[j];
+    }
+  }
+}
+
 // ------------------------------------------------------------ forward -------
 
 template <class LY, typename IN, int CPL, int GPR>
@@ -931,7 +1006,6 @@ __global__ void __launch_bounds__(256) conv_bwd(BwdParams prm) {
   static_assert(G % GPR == 0, "groups per receiver must divide groups per wave");
   constexpr int RPW = G / GPR;
   constexpr int NYP = pow2_ceil(NY);
-  constexpr int STEPS = ilog2(LPG);
 
   const float* __restrict__ x = prm.x;
   const float* __restrict__ y = prm.y;
@@ -1072,40 +1146,7 @@ __global__ void __launch_bounds__(256) conv_bwd(BwdParams prm) {
       for (int c = 0; c < CPL; ++c)
         unsafeAtomicAdd(prm.gx + ((size_t)a * NX + i) * C + li + c * LPG, dxp[i][c]);
 
-    // grad_y: reduce the per-lane partials over the group's LPG lanes
-    // (reduce-scatter: each halving step keeps half of the components).
-    sfor<0, STEPS>([&](auto kc) {
-      constexpr int k = decltype(kc)::value;
-      constexpr int d = LPG >> (k + 1);
-      constexpr int n = (NYP >> k) > 1 ? (NYP >> k) : 1;
-      if constexpr (n > 1) {
-        const bool upper = (li & d) != 0;
-#pragma unroll
-        for (int i = 0; i < n / 2; ++i) {
-          const float send = upper ? dyp[i] : dyp[i + n / 2];
-          const float keep = upper ? dyp[i + n / 2] : dyp[i];
-          dyp[i] = keep + __shfl_xor(send, d, 64);
-        }
-      } else {
-        dyp[0] += __shfl_xor(dyp[0], d, 64);
-      }
-    });
-    constexpr int NF = (NYP >> STEPS) > 1 ? (NYP >> STEPS) : 1;   // components left per lane
-    constexpr int REP = LPG > NYP ? LPG / NYP : 1;                  // lanes holding the same ones
-    if ((li & (REP - 1)) == 0) {
-      int base = 0;
-#pragma unroll
-      for (int k = 0; k < STEPS; ++k) {
-        const int d = LPG >> (k + 1);
-        const int n = (NYP >> k) > 1 ? (NYP >> k) : 1;
-        if (n > 1 && (li & d)) base += n / 2;
-      }
-#pragma unroll
-      for (int j = 0; j < NF; ++j) {
-        const int comp = base + j;
-        if (comp < NY) prm.gy[(size_t)e * NY + comp] = dyp[j];
-      }
-    }
+    store_dy<NY, LPG>(dyp, prm.gy + (size_t)e * NY, li, false);
   }
 }
 
@@ -1151,12 +1192,6 @@ __device__ __forceinline__ void load_bwd_edge(BwdBuf<LY, CPL>& buf, const float*
   }
 }
 
-// Orders a wave's LDS accesses around an exchange between its lanes.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // GEN: honour optional outputs (nullptr: not computed) and accumulation flags;
 // the default instantiations assume all three outputs, overwritten.
@@ -1176,7 +1211,6 @@ __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float
                                          float* xt = nullptr, After after = After{}) {
   constexpr int C = LY::C, NX = LY::NX, NY = LY::NY, NP = LY::NP;
   constexpr int NYP = pow2_ceil(NY);
-  constexpr int STEPS = ilog2(LPG);
   float dxp[NX][CPL];
 #pragma unroll
   for (int i = 0; i < NX; ++i)
@@ -1292,27 +1326,7 @@ __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float
 
   if (want_x) {
     if constexpr (Q) {
-      // lane li holds channels li*CPL + c; after the exchange it holds li + c*LPG
-#pragma unroll
-      for (int i = 0; i < NX; ++i) {
-        float v[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) v[c] = dxp[i][c];
-        if constexpr (CPL == 4) {
-          *reinterpret_cast<f32x4*>(xt + i * C + li * 4) = f32x4{v[0], v[1], v[2], v[3]};
-        } else if constexpr (CPL == 2) {
-          *reinterpret_cast<f32x2*>(xt + i * C + li * 2) = f32x2{v[0], v[1]};
-        } else {
-          xt[i * C + li] = v[0];
-        }
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int i = 0; i < NX; ++i)
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-          unsafeAtomicAdd(prm.gx + ((size_t)a * NX + i) * C + li + c * LPG, xt[i * C + li + c * LPG]);
-      wave_lds_sync();
+      atomic_add_rows<C, NX, CPL, LPG>(prm.gx + (size_t)a * NX * C, dxp, xt, li);
     } else {
 #pragma unroll
       for (int i = 0; i < NX; ++i)
@@ -1322,42 +1336,7 @@ __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float
     }
   }
   if (!want_y) return;
-
-  sfor<0, STEPS>([&](auto kc) {
-    constexpr int k = decltype(kc)::value;
-    constexpr int d = LPG >> (k + 1);
-    constexpr int n = (NYP >> k) > 1 ? (NYP >> k) : 1;
-    if constexpr (n > 1) {
-      const bool upper = (li & d) != 0;
-#pragma unroll
-      for (int i = 0; i < n / 2; ++i) {
-        const float send = upper ? dyp[i] : dyp[i + n / 2];
-        const float keep = upper ? dyp[i + n / 2] : dyp[i];
-        dyp[i] = keep + __shfl_xor(send, d, 64);
-      }
-    } else {
-      dyp[0] += __shfl_xor(dyp[0], d, 64);
-    }
-  });
-  constexpr int NF = (NYP >> STEPS) > 1 ? (NYP >> STEPS) : 1;
-  constexpr int REP = LPG > NYP ? LPG / NYP : 1;
-  if ((li & (REP - 1)) == 0) {
-    int base = 0;
-#pragma unroll
-    for (int k = 0; k < STEPS; ++k) {
-      const int d = LPG >> (k + 1);
-      const int n = (NYP >> k) > 1 ? (NYP >> k) : 1;
-      if (n > 1 && (li & d)) base += n / 2;
-    }
-#pragma unroll
-    for (int j = 0; j < NF; ++j) {
-      const int comp = base + j;
-      if (comp < NY) {
-        float* dst = prm.gy + (size_t)e * NY + comp;
-        *dst = (GEN && (prm.flags & kAccumulateY)) ? dyp[j] + *dst : dyp[j];
-      }
-    }
-  }
+  store_dy<NY, LPG>(dyp, prm.gy + (size_t)e * NY, li, GEN && (prm.flags & kAccumulateY));
 }
 
 template <class LY, int CPL, int GPR, bool GEN = false>
@@ -1592,6 +1571,311 @@ __global__ void __launch_bounds__(256) conv_bwd_tile(BwdParams prm) {
   bwd_tile<LY, CPL, GEN>(prm, e0, e1, xt_all[threadIdx.x >> 6][grp], li, grp);
 }
 
+// ------------------------------------------------ pair-stored backward ------
+//
+// On a graph that holds b -> a whenever it holds a -> b, with edge features
+// y_ba = P y_ab (P: (-1)^l on each l block) and scalars s_ba = s_ab, one row
+// of y and s per undirected pair suffices: a stored edge e = (a -> b) stands
+// for itself and for its reverse (b -> a), whose per-path matrix is
+// (-1)^l2 K^p(y[e]).  One pass over the stored edges takes both directions,
+// reading s[e] and writing grad_s[e] once for the two (per path and channel,
+// with w = K^T g[b] / N, w' = (-1)^l2 K^T g[a] / N):
+//   grad_s[e] = <x[a], w> + <x[b], w'>
+//   grad_x[a] += s w,      grad_x[b] += s w'
+//   grad_y[e] = dy(a -> b) + P dy(b -> a)
+// The stored edges come grouped by b (runs of equal dst), so a group keeps
+// g[b], x[b] and the grad_x[b] sum of its run in registers and adds that sum
+// with one set of atomics when the run ends; g[a] and x[a] are gathered per
+// edge and grad_x[a] takes atomics per edge, as in the directed pass.  Any
+// order of the stored edges gives the same result up to the fp32 summation
+// order; grouping only saves atomics.  Tiles of consecutive stored edges, one
+// per wave, as in the edge-tiled pass; a lane holds CPL consecutive channels.
+//
+// Registers: the paths are visited by output block, so the rows of g[a] that
+// one block uses are replaced by the next edge's as soon as that block's paths
+// are done (one buffer of g[a] in flight rather than two), as s is replaced
+// path by path.  1/N is folded into g[b] and x[b] (and the grad_x[b] sum
+// scaled by 1/N when added), so the gathered g[a] needs no scaling.  With one
+// group per wave the edge's y row is wave-uniform and held in scalar registers.
+
+// The j-th path in order of output block (then path index).
+constexpr int path_by_out(const LayoutTables& t, int j) {
+  for (int p = 0; p < t.num_paths; ++p) {
+    int r = 0;
+    for (int q = 0; q < t.num_paths; ++q)
+      if (t.path[q].o3 < t.path[p].o3 || (t.path[q].o3 == t.path[p].o3 && q < p)) ++r;
+    if (r == j) return p;
+  }
+  return -1;
+}
+
+// True if no later path in that order writes the same output block.
+constexpr bool last_into_block(const LayoutTables& t, int j) {
+  return j + 1 >= t.num_paths || t.path[path_by_out(t, j + 1)].o3 != t.path[path_by_out(t, j)].o3;
+}
+
+// A row of N floats at a wave-uniform address, read through the scalar cache.
+template <int N>
+__device__ __forceinline__ void load_row_uniform(const float* p, float (&v)[N]) {
+  typedef const __attribute__((address_space(4))) float cfloat;
+  cfloat* q = (cfloat*)(uintptr_t)p;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = q[i];
+}
+
+template <class LY, int CPL>
+struct PairBuf {
+  float y[LY::NY];
+  float xa[LY::NX][CPL];
+};
+
+template <class LY, int CPL>
+struct PairRun {
+  float gb[LY::NO][CPL];     // g[b] / N
+  float xb[LY::NX][CPL];     // x[b] / N
+  float dxb[LY::NX][CPL];    // N times this group's part of grad_x[b] over the run so far
+};
+
+template <class LY, int CPL, int LPG, class After>
+__device__ __forceinline__ void bwd_pair_edge(const PairBuf<LY, CPL>& buf,
+                                              const float (&ga)[LY::NO][CPL],
+                                              const float (&s)[LY::NP][CPL], PairRun<LY, CPL>& run,
+                                              const BwdParams& prm, int e, int a, int li, float* xt,
+                                              After after) {
+  constexpr int C = LY::C, NX = LY::NX, NY = LY::NY, NP = LY::NP;
+  constexpr int NYP = pow2_ceil(NY);
+  float dxa[NX][CPL];
+#pragma unroll
+  for (int i = 0; i < NX; ++i)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) dxa[i][c] = 0.0f;
+  float dyp[NYP];
+#pragma unroll
+  for (int j = 0; j < NYP; ++j) dyp[j] = 0.0f;
+  float* gsrow = prm.gs + (size_t)e * NP * C + li * CPL;
+
+  sfor<0, NP>([&](auto jc) {
+    constexpr int p = path_by_out(LY::T, decltype(jc)::value);
+    constexpr PathInfo P = LY::T.path[p];
+    constexpr int D1 = 2 * P.l1 + 1, D3 = 2 * P.l3 + 1;
+    constexpr float sg = (P.l2 & 1) ? -1.0f : 1.0f;   // the reverse edge's K is sg K
+    float K[D3][D1];
+    build_k<LY, p, D3, D1>(buf.y, K);
+    float ds[CPL];
+    sfor<0, D1>([&](auto m1c) {
+      constexpr int m1 = decltype(m1c)::value;
+      float w1[CPL], w2[CPL];
+      sfor<0, D3>([&](auto m3c) {
+        constexpr int m3 = decltype(m3c)::value;
+        if constexpr (k_nonzero(LY::T, p, m3, m1)) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            if constexpr (first_m3(LY::T, p, m1) == m3) {
+              w1[c] = K[m3][m1] * run.gb[P.o3 + m3][c];
+              w2[c] = K[m3][m1] * ga[P.o3 + m3][c];
+            } else {
+              w1[c] = __builtin_fmaf(K[m3][m1], run.gb[P.o3 + m3][c], w1[c]);
+              w2[c] = __builtin_fmaf(K[m3][m1], ga[P.o3 + m3][c], w2[c]);
+            }
+          }
+        }
+      });
+      if constexpr (first_m3(LY::T, p, m1) >= 0) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          if constexpr (m1 == 0) {
+            ds[c] = buf.xa[P.o1][c] * w1[c];
+          } else {
+            ds[c] = __builtin_fmaf(buf.xa[P.o1 + m1][c], w1[c], ds[c]);
+          }
+          ds[c] = __builtin_fmaf(sg * run.xb[P.o1 + m1][c], w2[c], ds[c]);
+          dxa[P.o1 + m1][c] = __builtin_fmaf(s[p][c], w1[c], dxa[P.o1 + m1][c]);
+          run.dxb[P.o1 + m1][c] = __builtin_fmaf(sg * s[p][c], w2[c], run.dxb[P.o1 + m1][c]);
+        }
+      } else if constexpr (m1 == 0) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) ds[c] = 0.0f;
+      }
+    });
+    store_row<CPL>(gsrow + p * C, ds, 1.0f);
+
+    // grad_y[o2+m2] += sum_{m1,m3} C[m1,m2,m3] sum_c s (x[a] g[b] + sg x[b] g[a]) / N
+    sfor<0, D1>([&](auto m1c) {
+      constexpr int m1 = decltype(m1c)::value;
+      if constexpr (first_m3(LY::T, p, m1) >= 0) {
+        float u1[CPL], u2[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          u1[c] = s[p][c] * buf.xa[P.o1 + m1][c];
+          u2[c] = sg * s[p][c] * run.xb[P.o1 + m1][c];
+        }
+        sfor<0, D3>([&](auto m3c) {
+          constexpr int m3 = decltype(m3c)::value;
+          if constexpr (k_nonzero(LY::T, p, m3, m1)) {
+            float q = u1[0] * run.gb[P.o3 + m3][0];
+            q = __builtin_fmaf(u2[0], ga[P.o3 + m3][0], q);
+#pragma unroll
+            for (int c = 1; c < CPL; ++c) {
+              q = __builtin_fmaf(u1[c], run.gb[P.o3 + m3][c], q);
+              q = __builtin_fmaf(u2[c], ga[P.o3 + m3][c], q);
+            }
+            sfor<P.nnz_begin, P.nnz_end>([&](auto ec) {
+              constexpr int qi = decltype(ec)::value;
+              constexpr Entry en = LY::T.entry[qi];
+              if constexpr (en.m1 == m1 && en.m3 == m3) {
+                dyp[P.o2 + en.m2] = __builtin_fmaf(LY::CG.v[qi], q, dyp[P.o2 + en.m2]);
+              }
+            });
+          }
+        });
+      }
+    });
+    after(jc);
+  });
+
+  atomic_add_rows<C, NX, CPL, LPG>(prm.gx + (size_t)a * NX * C, dxa, xt, li);
+  store_dy<NY, LPG>(dyp, prm.gy + (size_t)e * NY, li, false);
+}
+
+// One tile: the stored edges [e0, e1); group grp takes e0 + grp, e0 + grp + G, ...
+template <class LY, int CPL>
+__device__ __forceinline__ void bwd_pair_tile(const BwdParams& prm, int e0, int e1, float* xt,
+                                              int li, int grp) {
+  constexpr int C = LY::C, NX = LY::NX, NO = LY::NO, NP = LY::NP;
+  constexpr int LPG = C / CPL;
+  constexpr int G = 64 / LPG;
+  const int last = e1 - 1;
+  const float inv = prm.inv_avg;
+  const int* __restrict__ dst = prm.dst;
+
+  PairRun<LY, CPL> run;
+  int b = -1;                               // node of the current run (none yet)
+  auto flush = [&]() {
+#pragma unroll
+    for (int i = 0; i < NX; ++i)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) run.dxb[i][c] *= inv;
+    atomic_add_rows<C, NX, CPL, LPG>(prm.gx + (size_t)b * NX * C, run.dxb, xt, li);
+  };
+  auto start_run = [&](int nb) {
+    b = nb;
+    const float* grow = prm.g + (size_t)b * NO * C + li * CPL;
+    const float* xrow = prm.x + (size_t)b * NX * C + li * CPL;
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+      load_ch<float, CPL, false>(grow + o * C, run.gb[o]);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) run.gb[o][c] *= inv;
+    }
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      load_ch<float, CPL, false>(xrow + i * C, run.xb[i]);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        run.xb[i][c] *= inv;
+        run.dxb[i][c] = 0.0f;
+      }
+    }
+  };
+  auto load_edge = [&](PairBuf<LY, CPL>& nb, int ec, int a) {
+    if constexpr (G == 1) {
+      load_row_uniform<LY::NY>(prm.y + (size_t)ec * LY::NY, nb.y);
+    } else {
+      load_row<float, LY::NY>(prm.y + (size_t)ec * LY::NY, nb.y);
+    }
+    const float* xrow = prm.x + (size_t)a * NX * C + li * CPL;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) load_ch<float, CPL, false>(xrow + i * C, nb.xa[i]);
+  };
+
+  // s and g[a]: one buffer each, refilled with the next edge's rows as the
+  // paths finish with them; y and x[a]: two buffers.
+  float s[NP][CPL], ga[NO][CPL];
+  PairBuf<LY, CPL> b0, b1;
+  int e = e0 + grp;
+  int ec = e < last ? e : last;
+  int a = prm.src[ec];
+  int bc = dst[ec];
+  load_edge(b0, ec, a);
+  {
+    const float* srow = prm.s + (size_t)ec * NP * C + li * CPL;
+    const float* grow = prm.g + (size_t)a * NO * C + li * CPL;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) load_ch<float, CPL, true>(srow + p * C, s[p]);
+#pragma unroll
+    for (int o = 0; o < NO; ++o) load_ch<float, CPL, false>(grow + o * C, ga[o]);
+  }
+  int en = e + G;
+  int an = prm.src[en < last ? en : last];
+  int bn = dst[en < last ? en : last];
+  auto step = [&](PairBuf<LY, CPL>& cur, PairBuf<LY, CPL>& nxt) {
+    // the next edge's rows (and the indices two edges ahead) are loaded
+    // unconditionally, clamped to the tile's last edge
+    const int en2 = en + G;
+    const int ec2 = en2 < last ? en2 : last;
+    const int an2 = prm.src[ec2];
+    const int bn2 = dst[ec2];
+    const int ecn = en < last ? en : last;
+    load_edge(nxt, ecn, an);
+    const float* snext = prm.s + (size_t)ecn * NP * C + li * CPL;
+    const float* gnext = prm.g + (size_t)an * NO * C + li * CPL;
+    auto reload = [&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int p = path_by_out(LY::T, j);
+      load_ch<float, CPL, true>(snext + p * C, s[p]);
+      if constexpr (last_into_block(LY::T, j)) {
+        constexpr PathInfo P = LY::T.path[p];
+#pragma unroll
+        for (int m3 = 0; m3 < 2 * P.l3 + 1; ++m3)
+          load_ch<float, CPL, false>(gnext + (P.o3 + m3) * C, ga[P.o3 + m3]);
+      }
+    };
+    if (e <= last) {
+      if (bc != b) {
+        if (b >= 0) flush();
+        start_run(bc);
+      }
+      bwd_pair_edge<LY, CPL, LPG>(cur, ga, s, run, prm, e, a, li, xt, reload);
+    } else {
+      sfor<0, NP>(reload);
+    }
+    e = en;
+    a = an;
+    bc = bn;
+    en = en2;
+    an = an2;
+    bn = bn2;
+  };
+  // wave-uniform trip count: steps of G edges until the tile is done
+  for (int k0 = e0; k0 <= last; k0 += 2 * G) {
+    step(b0, b1);
+    if (k0 + G > last) break;
+    step(b1, b0);
+  }
+  if (b >= 0) flush();
+}
+
+// The stored edges are cut into prm.tiles ranges of nearly equal length; wave
+// w runs range w.
+template <class LY, int CPL>
+__global__ void __launch_bounds__(256) conv_bwd_pairs(BwdParams prm) {
+  constexpr int C = LY::C, NX = LY::NX;
+  constexpr int LPG = C / CPL;
+  static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
+  constexpr int G = 64 / LPG;
+  __shared__ float xt_all[4][G][NX * C];
+
+  const int lane = threadIdx.x & 63;
+  const int li = lane % LPG;
+  const int grp = lane / LPG;
+  const long w = logical_wave();
+  if (w >= prm.tiles) return;
+  const int e0 = (int)(w * prm.num_edges / prm.tiles);
+  const int e1 = (int)((w + 1) * prm.num_edges / prm.tiles);
+  if (e0 >= e1) return;
+  bwd_pair_tile<LY, CPL>(prm, e0, e1, xt_all[threadIdx.x >> 6][grp], li, grp);
+}
+
 __global__ void fill_zero(float* __restrict__ p, size_t n) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -1671,6 +1955,25 @@ hipError_t launch_bwd_tile(const BwdParams& prm, hipStream_t st) {
   p.tiles = (int)tiles;
   const long blocks = ((tiles + 3) / 4 + 7) / 8 * 8;   // whole rounds of the 8 XCDs (logical_wave)
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+// Pair-stored reverse pass: grad_x zeroed, then one wave per tile of about T
+// stored edges (prm.num_edges of them, prm.dst their receivers).
+template <class LY, int CPL, int T>
+hipError_t launch_bwd_pairs(const BwdParams& prm, hipStream_t st) {
+  BwdParams p = prm;
+  if (p.num_nodes <= 0) return hipSuccess;
+  const size_t nx = (size_t)p.num_nodes * LY::NX * LY::C;
+  const unsigned zb = (unsigned)((nx + 255) / 256 < 8192 ? (nx + 255) / 256 : 8192);
+  hipLaunchKernelGGL(fill_zero, dim3(zb), dim3(256), 0, st, p.gx, nx);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (p.num_edges <= 0) return hipSuccess;
+  const long tiles = ((long)p.num_edges + T - 1) / T;
+  p.tiles = (int)tiles;
+  const long blocks = ((tiles + 3) / 4 + 7) / 8 * 8;   // whole rounds of the 8 XCDs (logical_wave)
+  hipLaunchKernelGGL((conv_bwd_pairs<LY, CPL>), dim3((unsigned)blocks), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -480,6 +480,27 @@ e3conv_status e3conv_second_derivatives(e3conv_plan_t p, e3conv_dtype dt, const 
                     dg, stream);
 }
 
+e3conv_status e3conv_backward_pairs(e3conv_plan_t p, const float* x, const float* y, const float* s,
+                                    const int32_t* src, const int32_t* dst, int64_t N, int64_t E,
+                                    const float* g, float* gx, float* gy, float* gs, void* stream) {
+  if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+  e3conv_status st = check_sizes(N, E, p->channels, p->num_out > p->num_x ? p->num_out : p->num_x);
+  if (st != E3CONV_OK) return st;
+  if (E > 0 && N == 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "stored edges need nodes");
+  if (N == 0) return ok();
+  if (!g || !gx || (E > 0 && (!x || !y || !s || !src || !dst || !gy || !gs)))
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  if (p->ordering != E3CONV_RECEIVER)
+    return fail(E3CONV_ERR_UNSUPPORTED, "the pair-stored reverse pass takes a RECEIVER plan");
+  if (!p->kk || !p->kk->bwd_pairs_f32)
+    return fail(E3CONV_ERR_UNSUPPORTED, "no compiled pair-stored reverse kernel for this layout");
+  e3c::BwdParams prm{x, y, s, src, nullptr, nullptr, g, gx, gy, gs, (int)N, (int)E, 1.0f / p->avg,
+                     (int)N, 0, 0, dst};
+  const hipError_t err = p->kk->bwd_pairs_f32(prm, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "pair-stored backward launch");
+  return ok();
+}
+
 // ------------------------------------------------------------- linear ---
 
 namespace {

@@ -42,6 +42,7 @@ struct BwdParams {
   int num_real;         // edges into receivers b >= num_real get zero grad_y / grad_s
   int flags;            // kAccumulate*: add into the output instead of overwriting it
   int tiles;            // edge ranges of the edge-tiled kernel (set by its launcher)
+  const int* dst;       // pair-stored pass: (E) receiver of each stored edge, else unused
 };
 
 // BwdParams::flags.  Only the general reverse launchers honour them and
@@ -109,6 +110,7 @@ struct OrderingKernels {
   JvpLauncher jvp_f32;
   JvpLauncher jvp_bf16;
   RadialLauncher radial_f32;    // nullptr: no radial-scalar kernel for this layout
+  BwdLauncher bwd_pairs_f32;    // pair-stored reverse pass, or nullptr
 };
 
 struct KernelSet {

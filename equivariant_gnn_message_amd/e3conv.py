@@ -16,6 +16,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libe3conv.so")
 
 E3CONV_OK = 0
+E3CONV_ERR_INVALID_ARGUMENT, E3CONV_ERR_PARSE, E3CONV_ERR_UNSUPPORTED = 1, 2, 3
+E3CONV_ERR_NO_PATH, E3CONV_ERR_GRAPH = 4, 5
 E3CONV_F32 = 0
 E3CONV_BF16 = 1
 E3CONV_RECEIVER = 0
@@ -39,7 +41,7 @@ EXPORTED = [
     "e3conv_linear", "e3conv_linear_backward", "e3conv_csr_from_receivers",
     "e3conv_validate_graph", "e3conv_validate_graph_async", "e3conv_validate_graph_noalloc",
     "e3conv_receiver_order",
-    "e3conv_stream_reference", "e3conv_second_derivatives",
+    "e3conv_stream_reference", "e3conv_second_derivatives", "e3conv_backward_pairs",
     "e3conv_plan_set_variant",
     "e3conv_plan_num_variants",
     "e3conv_status_string", "e3conv_last_error_detail",
@@ -108,6 +110,7 @@ def load_library(path=LIB_PATH):
         "e3conv_validate_graph": ([P, P, I64, I64, ctypes.c_int], ctypes.c_int),
         "e3conv_validate_graph_async": ([P, P, I64, I64, P, P], ctypes.c_int),
         "e3conv_validate_graph_noalloc": ([P, P, I64, I64, P], ctypes.c_int),
+        "e3conv_backward_pairs": ([P, P, P, P, P, P, I64, I64, P, P, P, P, P], ctypes.c_int),
         "e3conv_second_derivatives": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P, P, P, P,
                                        P, P, P, P, P], ctypes.c_int),
         "e3conv_plan_set_variant": ([P, ctypes.c_int, ctypes.c_int], ctypes.c_int),
@@ -341,6 +344,21 @@ def e3conv_backward_ex(handle, x, y, s, src, row_ptr, num_nodes, num_edges, num_
         handle, E3CONV_F32, _ptr(x), _ptr(y), _ptr(s), _ptr(src), _ptr(row_ptr), _ptr(order),
         int(num_nodes), int(num_edges), int(num_real_nodes), _ptr(grad_out), _ptr(grad_x),
         _ptr(grad_y), _ptr(grad_s), int(flags), _ptr(workspace), wbytes, _stream(stream)))
+
+
+def e3conv_backward_pairs(handle, x, y, s, src, dst, num_nodes, num_pairs, grad_out, grad_x,
+                          grad_y, grad_s, stream=None):
+    """Pair-stored reverse pass: each stored edge (src -> dst) stands for itself and its reverse."""
+    import torch
+    for t, n in ((x, "x"), (y, "y"), (s, "s"), (grad_out, "grad_out"), (grad_x, "grad_x"),
+                 (grad_y, "grad_y"), (grad_s, "grad_s")):
+        _need(t, n, torch.float32)
+    _need(src, "src", torch.int32)
+    _need(dst, "dst", torch.int32)
+    _check(load_library().e3conv_backward_pairs(handle, _ptr(x), _ptr(y), _ptr(s), _ptr(src),
+                                                _ptr(dst), int(num_nodes), int(num_pairs),
+                                                _ptr(grad_out), _ptr(grad_x), _ptr(grad_y),
+                                                _ptr(grad_s), _stream(stream)))
 
 
 def e3conv_linear(handle, channels_out, scale, weights, inp, num_nodes, out, stream=None):

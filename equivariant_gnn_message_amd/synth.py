@@ -81,6 +81,7 @@ WORKLOADS = {
 # tensor ids
 T_GRAPH, T_X, T_DIR, T_S, T_MLP, T_G = 0, 1, 2, 3, 4, 5
 T_DX, T_DY, T_DS = 6, 7, 8   # tangents / second-order cotangents
+T_S_PAIR = 9                  # edge scalars, one row per undirected pair
 
 
 def rng(workload, tensor_id, chunk=0):
@@ -376,6 +377,32 @@ def symmetric_normal(senders, receivers, shape_tail, seed):
     uniq, inv = np.unique(key, return_inverse=True)
     draw = np.random.default_rng(seed).standard_normal((len(uniq),) + tuple(shape_tail))
     return draw[inv]
+
+
+def pair_index(senders, receivers):
+    """Pair storage of a symmetric graph without self loops (it holds b -> a
+    whenever it holds a -> b).
+
+    Returns (stored, pair_of): ``stored`` are the indices of the edges with
+    sender < receiver, in input order (one per undirected pair, so an input
+    sorted by receiver stays grouped by receiver); ``pair_of[e]`` is the
+    position among them of directed edge e's pair.  Raises ValueError if an
+    edge's reverse is missing or an edge is a self loop.
+    """
+    a = np.asarray(senders, dtype=np.int64)
+    b = np.asarray(receivers, dtype=np.int64)
+    stored = np.flatnonzero(a < b)
+    n = int(max(a.max(initial=-1), b.max(initial=-1))) + 1
+    key_stored = a[stored] * n + b[stored]
+    key_all = np.minimum(a, b) * n + np.maximum(a, b)
+    order = np.argsort(key_stored, kind="stable")
+    pos = np.searchsorted(key_stored[order], key_all)
+    pos = np.minimum(pos, max(len(order) - 1, 0))
+    pair_of = order[pos] if len(order) else np.zeros(len(a), np.int64)
+    if len(a) and (len(order) == 0 or not np.array_equal(key_stored[pair_of], key_all)
+                   or np.any(a == b) or 2 * len(stored) != len(a)):
+        raise ValueError("not a symmetric graph without self loops")
+    return stored, pair_of
 
 
 def edge_vectors(pos, senders, receivers):

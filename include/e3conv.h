@@ -286,6 +286,37 @@ e3conv_status e3conv_second_derivatives(e3conv_plan_t plan, e3conv_dtype in_dtyp
                                         const float* cot_s, float* d_x, float* d_y, float* d_s,
                                         float* d_grad_out, void* hip_stream);
 
+/* Pair-stored reverse pass (e3j Convolution page, the note on SENDER
+ * ordering, which assumes a symmetric graph, y_ba = (-1)^l y_ab per l block and
+ * s_ba = s_ab).  Under those assumptions one row of y and s per undirected
+ * pair carries the whole graph: a stored edge e = (a -> b), a = src[e],
+ * b = dst[e], stands for itself, with y[e] and s[e], and for its reverse
+ * (b -> a), with P y[e] (odd-l blocks negated) and s[e].  The forward
+ * function is the RECEIVER convolution (formula above) of those 2 E directed
+ * edges, and this call is its reverse pass for L = <grad_out, out>:
+ *     grad_s[e] = ds(a -> b) + ds(b -> a),
+ *     grad_y[e] = dy(a -> b) + P dy(b -> a),
+ *     grad_x    = the sum over all 2 E directed edges, as in e3conv_backward.
+ * s[e] is read and grad_s[e] written once per pair, which halves the edge
+ * bytes of the directed reverse pass on the same graph.
+ *   x (N, num_x, C), y (E, num_y), s (E, num_paths, C), grad_out (N, num_out,
+ *   C): fp32 device; src, dst: device int32[E] in [0, num_nodes) (out of range
+ *   is undefined behaviour); E = num_pairs;
+ *   grad_x (N, num_x, C): fully overwritten (zeroed, then fp32 atomics, so its
+ *   rounding may vary from run to run); grad_y (E, num_y) and grad_s (E,
+ *   num_paths, C) written once per stored edge.
+ * The stored edges may come in any order with either orientation (a pair
+ * stored as (b -> a) with P y gives the same grad_x and grad_s, and P grad_y);
+ * grouping the edges with equal dst consecutively (e.g. sorted by dst) lets
+ * each run share one set of grad_x[b] atomics.  A stored self loop (a = b)
+ * counts as two edges.  RECEIVER plans only (E3CONV_ERR_UNSUPPORTED
+ * otherwise, or for a layout without this kernel); num_nodes = 0 with
+ * num_pairs = 0 is a no-op; asynchronous on hip_stream. */
+e3conv_status e3conv_backward_pairs(e3conv_plan_t plan, const float* x, const float* y,
+                                    const float* s, const int32_t* src, const int32_t* dst,
+                                    int64_t num_nodes, int64_t num_pairs, const float* grad_out,
+                                    float* grad_x, float* grad_y, float* grad_s, void* hip_stream);
+
 /* Output linear: channel mixing within each output irrep block, the step
  * after the convolution (cuEquivariance page, Flax NNX layers, IrrepsLinear:
  * each block is mixed across its channels by a weight matrix and scaled by

@@ -78,3 +78,23 @@ def test_subgraph16():
     assert np.all(np.diff(dst) >= 0)
     np.testing.assert_array_equal(nodes[src], inp.senders[eids])
     np.testing.assert_array_equal(nodes[dst], inp.receivers[eids])
+
+
+def test_pair_index_of_a_radius_graph():
+    pos = np.random.default_rng(3).uniform(0.0, 3.0, (60, 3))
+    src, dst = synth.radius_graph(pos, 1.2)
+    stored, pair_of = synth.pair_index(src, dst)
+    assert 2 * len(stored) == len(src)
+    assert np.all(src[stored] < dst[stored])
+    assert np.all(np.diff(dst[stored]) >= 0)            # still grouped by receiver
+    # every directed edge maps to the stored edge of its pair, both directions covered
+    assert np.array_equal(np.minimum(src, dst), src[stored][pair_of])
+    assert np.array_equal(np.maximum(src, dst), dst[stored][pair_of])
+    assert np.array_equal(np.bincount(pair_of, minlength=len(stored)), np.full(len(stored), 2))
+
+
+def test_pair_index_rejects_asymmetric_graphs():
+    with pytest.raises(ValueError):
+        synth.pair_index(np.array([0, 1, 2]), np.array([1, 0, 0]))
+    with pytest.raises(ValueError):
+        synth.pair_index(np.array([0, 1, 1]), np.array([1, 0, 1]))     # self loop
