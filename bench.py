@@ -756,15 +756,22 @@ def pair_bytes(w, N, Ep):
     return 4 * (2 * N * nx * C + N * no * C + Ep * (2 * ny + 2 * P * C + 2))
 
 
-def pair_inputs(inp):
-    """Pair storage of a workload's symmetric radius graph: the stored edges (sender <
-    receiver, grouped by receiver), their y rows, one seeded N(0,1) row of s per pair,
-    and for each directed edge its pair."""
+def pair_inputs(inp, cluster=512):
+    """Pair storage of a workload's symmetric radius graph (e3conv_pair_layout: one
+    stored edge per pair, receivers in the locality order, runs of one receiver),
+    one seeded N(0,1) row of s per pair, and for each directed edge its pair."""
+    import numpy as np
+
+    from equivariant_gnn_message_amd import e3conv as E
     from equivariant_gnn_message_amd import synth
     w = inp.workload
-    stored, pair_of = synth.pair_index(inp.senders, inp.receivers)
+    N, Ec = inp.num_nodes, inp.num_edges
+    row_ptr = np.searchsorted(inp.receivers, np.arange(N + 1)).astype(np.int32)
+    t0 = time.perf_counter()
+    stored, pair_of = E.e3conv_pair_layout(row_ptr, inp.senders, N, Ec, cluster)
+    layout_ms = (time.perf_counter() - t0) * 1e3
     s_pair = synth.normal_f32(w.idx, synth.T_S_PAIR, (len(stored), w.num_paths, w.channels))
-    return stored, pair_of, s_pair
+    return stored, pair_of, s_pair, layout_ms
 
 
 def time_pairs_reverse(plan, w, inp, stored, s_pair, args):
@@ -789,7 +796,7 @@ def time_pairs_reverse(plan, w, inp, stored, s_pair, args):
 def pairs_block(plan, w, inp, directed_ms, args):
     """The pair-stored reverse pass on the training graph (one s row per pair) next to
     the directed reverse pass of the same graph (its time does not depend on the values)."""
-    stored, _, s_pair = pair_inputs(inp)
+    stored, _, s_pair, layout_ms = pair_inputs(inp, args.cluster)
     N, Ec, Ep = inp.num_nodes, inp.num_edges, len(stored)
     ms = time_pairs_reverse(plan, w, inp, stored, s_pair, args)
     nbytes = pair_bytes(w, N, Ep)
@@ -800,7 +807,8 @@ def pairs_block(plan, w, inp, directed_ms, args):
             "ms": ms, "directed_edges_per_s": Ec / (ms * 1e-3), "algorithmic_bytes": nbytes,
             "hbm_GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS,
             "directed_reverse_ms": directed_ms, "directed_algorithmic_bytes": dir_bytes,
-            "speedup_vs_directed": directed_ms / ms}
+            "speedup_vs_directed": directed_ms / ms, "pair_layout_ms": layout_ms,
+            "pair_order": f"clustered {args.cluster}"}
 
 
 def bench_pairs(args):
@@ -817,7 +825,7 @@ def bench_pairs(args):
         raise SystemExit("--mode pairs needs the fp32 training workload (4)")
     inp = synth.make_inputs(args.workload)
     N, Ec = inp.num_nodes, inp.num_edges
-    stored, pair_of, s_pair = pair_inputs(inp)
+    stored, pair_of, s_pair, layout_ms = pair_inputs(inp, args.cluster)
     Ep = len(stored)
     plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -844,8 +852,10 @@ def bench_pairs(args):
            "pairs_hbm_GBps": pb / (pair_ms * 1e-3) / 1e9,
            "directed_ms": dir_ms, "directed_algorithmic_bytes": db,
            "directed_hbm_GBps": db / (dir_ms * 1e-3) / 1e9,
-           "speedup_vs_directed": dir_ms / pair_ms,
-           "roofline": roofline("conv_bwd_pairs", pair_ms, pb)}
+           "speedup_vs_directed": dir_ms / pair_ms, "pair_layout_ms": layout_ms,
+           "pair_order": f"clustered {args.cluster}",
+           "roofline": roofline("conv_bwd_pairs", pair_ms, pb,
+                                traffic=traffic_from_profiles("conv_bwd_pairs", args.workload))}
     res["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits

@@ -3,12 +3,14 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <memory>
 #include <new>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "host_core.h"
@@ -622,6 +624,52 @@ e3conv_status e3conv_receiver_order(const int32_t* row_ptr, const int32_t* src, 
   const e3conv_status st = e3conv_validate_graph(src, row_ptr, N, E, 0);
   if (st != E3CONV_OK) return st;
   e3c::receiver_order(row_ptr, src, (int)N, cluster, order);
+  return ok();
+}
+
+e3conv_status e3conv_pair_layout(const int32_t* row_ptr, const int32_t* src, int64_t N, int64_t E,
+                                 int cluster, int32_t* stored, int32_t* pair_of) {
+  if (N < 0 || E < 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "negative size");
+  if (E >= (int64_t)1 << 31 || N >= ((int64_t)1 << 31) - 1)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "sizes must fit int32 indices");
+  if (cluster <= 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "cluster must be positive");
+  if (E % 2 != 0) return fail(E3CONV_ERR_GRAPH, "a symmetric graph has an even number of edges");
+  if (N == 0) return ok();
+  if (!row_ptr || (E > 0 && (!src || !stored || !pair_of)))
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL pointer");
+  const e3conv_status st = e3conv_validate_graph(src, row_ptr, N, E, 0);
+  if (st != E3CONV_OK) return st;
+  std::vector<int> order(N), rank(N);
+  e3c::receiver_order(row_ptr, src, (int)N, cluster, order.data());
+  for (int i = 0; i < (int)N; ++i) rank[order[i]] = i;
+  // one stored edge per pair: the edge into the endpoint that comes first in the order
+  std::unordered_map<int64_t, int> slot;
+  slot.reserve((size_t)E);
+  int k = 0;
+  for (int i = 0; i < (int)N; ++i) {
+    const int b = order[i];
+    for (int e = row_ptr[b]; e < row_ptr[b + 1]; ++e) {
+      const int a = src[e];
+      if (a == b) return fail(E3CONV_ERR_GRAPH, "self loop at edge " + std::to_string(e));
+      if (rank[a] < rank[b]) continue;            // stored as the reverse edge, into a
+      const int64_t key = (int64_t)std::min(a, b) * N + std::max(a, b);
+      if (!slot.emplace(key, k).second)
+        return fail(E3CONV_ERR_GRAPH, "duplicate edge " + std::to_string(e));
+      if (k >= E / 2) return fail(E3CONV_ERR_GRAPH, "graph is not symmetric");
+      stored[k++] = e;
+    }
+  }
+  if (k != E / 2) return fail(E3CONV_ERR_GRAPH, "graph is not symmetric");
+  std::vector<int> seen(k, 0);
+  for (int b = 0; b < (int)N; ++b) {
+    for (int e = row_ptr[b]; e < row_ptr[b + 1]; ++e) {
+      const int a = src[e];
+      const auto it = slot.find((int64_t)std::min(a, b) * N + std::max(a, b));
+      if (it == slot.end() || ++seen[it->second] > 2)
+        return fail(E3CONV_ERR_GRAPH, "graph is not symmetric at edge " + std::to_string(e));
+      pair_of[e] = it->second;
+    }
+  }
   return ok();
 }
 

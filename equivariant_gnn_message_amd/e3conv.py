@@ -41,7 +41,7 @@ EXPORTED = [
     "e3conv_linear", "e3conv_linear_backward", "e3conv_csr_from_receivers",
     "e3conv_validate_graph", "e3conv_validate_graph_async", "e3conv_validate_graph_noalloc",
     "e3conv_receiver_order",
-    "e3conv_stream_reference", "e3conv_second_derivatives", "e3conv_backward_pairs",
+    "e3conv_stream_reference", "e3conv_second_derivatives", "e3conv_backward_pairs", "e3conv_pair_layout",
     "e3conv_plan_set_variant",
     "e3conv_plan_num_variants",
     "e3conv_status_string", "e3conv_last_error_detail",
@@ -111,6 +111,7 @@ def load_library(path=LIB_PATH):
         "e3conv_validate_graph_async": ([P, P, I64, I64, P, P], ctypes.c_int),
         "e3conv_validate_graph_noalloc": ([P, P, I64, I64, P], ctypes.c_int),
         "e3conv_backward_pairs": ([P, P, P, P, P, P, I64, I64, P, P, P, P, P], ctypes.c_int),
+        "e3conv_pair_layout": ([P, P, I64, I64, ctypes.c_int, P, P], ctypes.c_int),
         "e3conv_second_derivatives": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P, P, P, P,
                                        P, P, P, P, P], ctypes.c_int),
         "e3conv_plan_set_variant": ([P, ctypes.c_int, ctypes.c_int], ctypes.c_int),
@@ -406,6 +407,19 @@ def e3conv_receiver_order(row_ptr, src, num_nodes, num_edges, cluster=512):
                                                 int(num_nodes), int(num_edges), int(cluster),
                                                 order.ctypes.data_as(P)))
     return order
+
+
+def e3conv_pair_layout(row_ptr, src, num_nodes, num_edges, cluster=512):
+    """Host-side pair storage of a symmetric graph: (stored, pair_of) as numpy int32."""
+    import numpy as np
+    r = np.ascontiguousarray(np.asarray(row_ptr), dtype=np.int32)
+    s = np.ascontiguousarray(np.asarray(src), dtype=np.int32)
+    stored = np.empty(int(num_edges) // 2, dtype=np.int32)
+    pair_of = np.empty(int(num_edges), dtype=np.int32)
+    _check(load_library().e3conv_pair_layout(r.ctypes.data_as(P), s.ctypes.data_as(P),
+                                             int(num_nodes), int(num_edges), int(cluster),
+                                             stored.ctypes.data_as(P), pair_of.ctypes.data_as(P)))
+    return stored, pair_of
 
 
 def e3conv_validate_graph(src, row_ptr, num_nodes, num_edges):

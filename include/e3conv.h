@@ -366,6 +366,26 @@ e3conv_status e3conv_csr_from_receivers(const int32_t* receivers_sorted, int64_t
 e3conv_status e3conv_receiver_order(const int32_t* row_ptr, const int32_t* src, int64_t num_nodes,
                                     int64_t num_edges, int cluster, int32_t* order);
 
+/* Pair storage for e3conv_backward_pairs (host only, once per graph, like the
+ * receiver order).  From the host receiver CSR (row_ptr, src) of a graph that
+ * holds b -> a whenever it holds a -> b, once each, without self loops (the
+ * radius graphs of the gate-points page are such graphs), it picks one
+ * directed edge per undirected pair and orders the picks: receivers in the
+ * order e3conv_receiver_order(cluster) gives, each pair stored as its edge
+ * into the endpoint that comes first in that order, the stored edges of one
+ * receiver consecutive.  Nearby receivers then follow each other, which keeps
+ * the rows the pair pass gathers in cache.  Writes
+ *   stored[num_edges / 2]  the directed edge of each stored pair (so the pair
+ *                          arrays are y[stored], s[stored], src[stored] and the
+ *                          receivers of those edges);
+ *   pair_of[num_edges]     for every directed edge, the position of its pair
+ *                          in stored (the directed rows of s are s_pair[pair_of]).
+ * E3CONV_ERR_GRAPH if the graph is invalid (as e3conv_validate_graph), not
+ * symmetric, has a repeated edge, a self loop or an odd number of edges. */
+e3conv_status e3conv_pair_layout(const int32_t* row_ptr, const int32_t* src, int64_t num_nodes,
+                                 int64_t num_edges, int cluster, int32_t* stored,
+                                 int32_t* pair_of);
+
 /* Check a graph (the e3j Convolution page, __call__: indices lie in
  * [0, num_nodes); the fused kernels need edges sorted by receiver): row_ptr[0]
  * = 0, row_ptr non-decreasing and within [0, num_edges], row_ptr[num_nodes] =

@@ -194,15 +194,16 @@ def test_pairs_reject_sender_plans_and_null_pointers():
 
 
 def test_pairs_full_training_size_sampled():
-    """The training graph at full size (N = 20000, 298061 pairs) in the launch
-    configuration the benchmark times: sampled grad_s / grad_y rows (each
+    """The training graph at full size (N = 20000, 298061 pairs) in the pair
+    layout and launch configuration the benchmark times: sampled grad_s / grad_y rows (each
     depends on its own edge only) and sampled grad_x rows (every stored edge
     touching the node), plus the trilinear identity <g, out> = <grad_s, s>."""
     import torch
     inp = synth.make_inputs(4)
     w, N = inp.workload, inp.num_nodes
     lay = lay_of(w)
-    stored, _ = synth.pair_index(inp.senders, inp.receivers)
+    row_ptr = np.searchsorted(inp.receivers, np.arange(N + 1)).astype(np.int32)
+    stored, _ = E.e3conv_pair_layout(row_ptr, inp.senders, N, inp.num_edges, 512)
     src, dst = inp.senders[stored], inp.receivers[stored]
     y = inp.y[stored]
     s = synth.normal_f32(w.idx, synth.T_S_PAIR, (len(stored), lay.num_paths, lay.channels))

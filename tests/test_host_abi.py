@@ -302,3 +302,66 @@ def test_radial_argument_errors(lib):
     assert call(mace.handle) == 3        # E3CONV_ERR_UNSUPPORTED: 128 channels
     assert call(sender.handle) == 3      # RECEIVER ordering only
     assert call(gate.handle, N=0, Ecount=0, nr=0) == 0
+
+
+def test_backward_pairs_argument_errors(lib):
+    w = synth.WORKLOADS[2]
+    p = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    ps = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors, ordering=E.E3CONV_SENDER)
+    f = ctypes.c_void_p(0x1000)
+    n = ctypes.c_void_p(0)
+    h = p.handle
+    assert lib.e3conv_backward_pairs(None, f, f, f, f, f, 4, 4, f, f, f, f, None) == 1
+    assert lib.e3conv_backward_pairs(h, f, f, f, f, f, -1, 4, f, f, f, f, None) == 1    # negative size
+    assert lib.e3conv_backward_pairs(h, f, f, f, f, f, 4, 1 << 31, f, f, f, f, None) == 1
+    assert lib.e3conv_backward_pairs(h, f, f, f, f, n, 4, 4, f, f, f, f, None) == 1     # null dst
+    assert lib.e3conv_backward_pairs(h, f, f, f, f, f, 4, 4, f, f, n, f, None) == 1     # null grad_y
+    assert lib.e3conv_backward_pairs(h, f, f, f, f, f, 0, 4, f, f, f, f, None) == 1     # edges, no nodes
+    assert lib.e3conv_backward_pairs(h, n, n, n, n, n, 0, 0, n, n, n, n, None) == 0     # empty: no-op
+    assert lib.e3conv_backward_pairs(ps.handle, f, f, f, f, f, 4, 4, f, f, f, f, None) == 3
+
+
+def _csr(src, dst, n):
+    order = np.lexsort((src, dst))
+    src, dst = np.asarray(src)[order], np.asarray(dst)[order]
+    return np.searchsorted(dst, np.arange(n + 1)).astype(np.int32), src.astype(np.int32), dst
+
+
+@pytest.mark.parametrize("cluster", [1, 16, 512])
+def test_pair_layout_of_radius_graphs(cluster):
+    """One stored edge per pair, both directions mapped to it, the stored edges of a
+    receiver consecutive, receivers in the receiver order, each pair stored as its edge
+    into the endpoint the order visits first; the pair set equals the plain selection."""
+    pos = np.random.default_rng(cluster).uniform(0.0, 4.0, (300, 3))
+    src, dst = synth.radius_graph(pos, 1.0)
+    N, Ec = len(pos), len(src)
+    row_ptr = np.searchsorted(dst, np.arange(N + 1)).astype(np.int32)
+    stored, pair_of = E.e3conv_pair_layout(row_ptr, src, N, Ec, cluster)
+    assert len(stored) * 2 == Ec
+    assert np.array_equal(np.bincount(pair_of, minlength=len(stored)), np.full(len(stored), 2))
+    assert np.array_equal(pair_of[stored], np.arange(len(stored)))
+    lo, hi = np.minimum(src, dst), np.maximum(src, dst)
+    assert np.array_equal(lo[stored][pair_of], lo) and np.array_equal(hi[stored][pair_of], hi)
+    order = E.e3conv_receiver_order(row_ptr, src, N, Ec, cluster)
+    rank = np.empty(N, np.int64)
+    rank[order] = np.arange(N)
+    b, a = dst[stored], src[stored]
+    assert np.all(np.diff(rank[b]) >= 0)                 # receivers in order, runs consecutive
+    assert np.all(rank[a] > rank[b])                     # stored into the earlier endpoint
+    plain, _ = synth.pair_index(src, dst)
+    key = lambda e: set(zip(lo[e].tolist(), hi[e].tolist()))
+    assert key(stored) == key(plain)
+
+
+def test_pair_layout_rejects_graphs_that_are_not_symmetric():
+    def call(src, dst, n):
+        row_ptr, s, _ = _csr(np.array(src), np.array(dst), n)
+        return E.e3conv_pair_layout(row_ptr, s, n, len(s))
+    call([0, 1, 1, 2], [1, 0, 2, 1], 3)                              # symmetric: accepted
+    for src, dst in (([0, 1, 2], [1, 0, 0]),                         # odd edge count
+                     ([0, 1, 0, 1], [1, 0, 2, 2]),                   # reverses missing
+                     ([0, 1, 1, 1], [1, 0, 1, 1]),                   # self loops
+                     ([0, 0, 1, 1], [1, 1, 0, 0])):                  # repeated edges
+        with pytest.raises(E.E3ConvError) as err:
+            call(src, dst, 3)
+        assert err.value.status == E.E3CONV_ERR_GRAPH
