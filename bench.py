@@ -915,6 +915,8 @@ def bench_linear(args):
                         "kernel": "linear_rows (forward): reads in and W, writes out once",
                         "algorithmic_bytes": byt, "fp32_equivalent_TFLOPs": tf_f,
                         "bf16_issued_TFLOPs": 6 * tf_f, "bf16_peak_TFLOPs": PEAK_FP16_MFMA_TFLOPS}}
+    if plan.kernels_fused_linear():
+        res["fused_epilogue"] = fused_linear_block(plan, w, inp, W, args)
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits
         from oracle import conv, linear
@@ -932,6 +934,53 @@ def bench_linear(args):
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
+
+
+def fused_linear_block(plan, w, inp, W, args):
+    """The convolution then the output linear (C_out = C) of a workload: two calls
+    (e3conv_forward, e3conv_linear) against one with the linear in the epilogue
+    (e3conv_forward_linear), same graph, operands, receiver order and weights."""
+    import numpy as np
+    import torch
+
+    from equivariant_gnn_message_amd import e3conv as E
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    N, Ec, C, NO = inp.num_nodes, inp.num_edges, w.channels, w.num_out
+    x, y, s, src = dev(inp.x), dev(inp.y), dev(inp.s), dev(inp.senders)
+    row_ptr = E.e3conv_csr_from_receivers(dev(inp.receivers), N)
+    order = torch.from_numpy(E.e3conv_receiver_order(row_ptr.cpu().numpy(), inp.senders, N, Ec,
+                                                     args.cluster)).cuda()
+    m = torch.empty((N, NO, C), dtype=torch.float32, device="cuda")
+    o_sep, o_fus = torch.empty_like(m), torch.empty_like(m)
+
+    def separate():
+        plan.forward(x, y, s, src, row_ptr, out=m, order=order)
+        plan.linear(m, W, C, out=o_sep)
+
+    fused = lambda: E.e3conv_forward_linear(plan.handle, x, y, s, src, row_ptr, N, Ec, 1.0, W, o_fus,
+                                            order=order)
+    sep_ms = _timed(separate, args.steps, args.warmup)
+    conv_ms = _timed(lambda: plan.forward(x, y, s, src, row_ptr, out=m, order=order), args.steps,
+                     args.warmup)
+    fus_ms = _timed(fused, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    diff = float((o_sep - o_fus).abs().max() / o_sep.pow(2).mean().sqrt())
+    b_in = 2 if w.dtype == "bf16" else 4
+    fwd_bytes = alg_bytes(w, N, Ec, b_in)[0]
+    fused_bytes = fwd_bytes + 4 * W.numel()
+    return {"workload": f"{w.name}: forward, then the output linear, N={N} E={Ec}, {w.irreps_out}, "
+                        f"C_out = C, {'bf16' if w.dtype == 'bf16' else 'fp32'} operands",
+            "separate_ms": sep_ms, "forward_only_ms": conv_ms, "fused_ms": fus_ms,
+            "speedup_vs_separate": sep_ms / fus_ms,
+            "fused_algorithmic_bytes": fused_bytes,
+            "fused_hbm_GBps": fused_bytes / (fus_ms * 1e-3) / 1e9,
+            "separate_algorithmic_bytes": fused_bytes + 2 * 4 * N * NO * C,
+            "max_abs_diff_over_rms_fused_vs_separate": diff}
 
 
 def bench_radial(args):

@@ -272,6 +272,47 @@ __device__ __forceinline__ void store_dy(float (&dyp)[pow2_ceil(NY)], float* dst
   }
 }
 
+template <int CPL>
+__device__ __forceinline__ void store_row(float* dst, const float (&v)[CPL], float scale) {
+  if constexpr (CPL == 4) {
+    f32x4 w = {v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale};
+    __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(dst));
+  } else if constexpr (CPL == 2) {
+    f32x2 w = {v[0] * scale, v[1] * scale};
+    __builtin_nontemporal_store(w, reinterpret_cast<f32x2*>(dst));
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) __builtin_nontemporal_store(v[c] * scale, dst + c);
+  }
+}
+
+// A lane's CPL consecutive floats in LDS (its own channels: no exchange).
+template <int CPL>
+__device__ __forceinline__ void lds_store_ch(float* p, const float (&v)[CPL], float scale) {
+  if constexpr (CPL == 4) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale};
+  } else if constexpr (CPL == 2) {
+    *reinterpret_cast<f32x2*>(p) = f32x2{v[0] * scale, v[1] * scale};
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) p[c] = v[c] * scale;
+  }
+}
+
+template <int CPL>
+__device__ __forceinline__ void lds_load_ch(const float* p, float (&v)[CPL]) {
+  if constexpr (CPL == 4) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(p);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  } else if constexpr (CPL == 2) {
+    const f32x2 t = *reinterpret_cast<const f32x2*>(p);
+    v[0] = t.x; v[1] = t.y;
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) v[c] = p[c];
+  }
+}
+
 // ------------------------------------------------------------ forward -------
 
 template <class LY, typename IN, int CPL, int GPR>
@@ -380,6 +421,83 @@ __global__ void __launch_bounds__(256) conv_fwd(FwdParams prm) {
       }
     }
   }
+}
+
+// ------------------------------------------------ fused output linear ------
+
+// Output blocks of a block code.
+constexpr int num_blocks(uint32_t code) {
+  int n = 0;
+  for (int l = 0; l <= kMaxL; ++l) n += block_parity(code, l) != 0;
+  return n;
+}
+
+// The output channels v0 .. v0+VL-1 of every component of receiver b from its
+// summed row (LDS) and the weights (LDS).
+template <class LY, int VL>
+__device__ __forceinline__ void lin_rows(const float* w, const float* row, const FwdParams& prm,
+                                         int b, int v0) {
+  constexpr int C = LY::C, NO = LY::NO;
+  float res[NO][VL];
+#pragma unroll
+  for (int o = 0; o < NO; ++o)
+#pragma unroll
+    for (int c = 0; c < VL; ++c) res[o][c] = 0.0f;
+  int k = 0;
+  sfor<0, kMaxL + 1>([&](auto lc) {
+    constexpr int l = decltype(lc)::value;
+    if constexpr (block_parity(LY::OCODE, l) != 0) {
+      constexpr int ob = code_offset(LY::OCODE, l);
+      const float* wk = w + k * C * C + v0;
+#pragma unroll 2
+      for (int u = 0; u < C; u += 4) {
+        float wv[4][VL];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lds_load_ch<VL>(wk + (u + q) * C, wv[q]);
+#pragma unroll
+        for (int m = 0; m < 2 * l + 1; ++m) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(row + (ob + m) * C + u);
+#pragma unroll
+          for (int c = 0; c < VL; ++c) {
+            res[ob + m][c] = __builtin_fmaf(a.x, wv[0][c], res[ob + m][c]);
+            res[ob + m][c] = __builtin_fmaf(a.y, wv[1][c], res[ob + m][c]);
+            res[ob + m][c] = __builtin_fmaf(a.z, wv[2][c], res[ob + m][c]);
+            res[ob + m][c] = __builtin_fmaf(a.w, wv[3][c], res[ob + m][c]);
+          }
+        }
+      }
+      ++k;
+    }
+  });
+  float* orow = prm.out + (size_t)b * NO * C + v0;
+#pragma unroll
+  for (int o = 0; o < NO; ++o) store_row<VL>(orow + (size_t)o * C, res[o], prm.lin_alpha);
+}
+
+// Fused output linear (the step after the convolution: each output irrep
+// block mixed over its channels by a C x C weight matrix, scaled by
+// scale / sqrt(C)).  The receiver's summed row goes through the wave's LDS
+// row; then the GPR * LPG lanes of the receiver each produce C / (GPR * LPG)
+// output channels of every component,
+//   out[b, o, v] = lin_alpha * sum_u row[o, u] W_k(o)[u, v]
+// (lin_alpha = scale / sqrt(C) / N), W staged in LDS once per work-group.
+template <class LY, int CPL, int GPR>
+__device__ __forceinline__ void lin_epilogue(const float (&acc)[LY::NO][CPL], const float* w,
+                                             float* row, const FwdParams& prm, int b, bool valid,
+                                             int li, int gi) {
+  constexpr int C = LY::C, NO = LY::NO;
+  constexpr int LPG = C / CPL;
+  constexpr int EL = LPG * GPR;                 // lanes of one receiver
+  constexpr int VL = C / EL > 0 ? C / EL : 1;   // output channels per lane
+  static_assert(C % 4 == 0, "rows are read four channels at a time");
+  if (gi == 0) {
+#pragma unroll
+    for (int o = 0; o < NO; ++o) lds_store_ch<CPL>(row + o * C + li * CPL, acc[o], 1.0f);
+  }
+  wave_lds_sync();
+  const int v0 = (gi * LPG + li) * VL;
+  if (valid && v0 < C) lin_rows<LY, VL>(w, row, prm, b, v0);
+  wave_lds_sync();   // the row is rewritten for the wave's next receiver
 }
 
 // ------------------------------------------------- pipelined forward --------
@@ -545,13 +663,13 @@ __device__ __forceinline__ void edge_accumulate(const EdgeBuf<LY, IN, CPL>& buf,
 // conditional load, merged into the loop variable, makes the compiler wait
 // for every load in flight, the next edge's rows included). Which form is
 // faster depends on the layout.
-template <class LY, typename IN, int CPL, int GPR, bool UL = false>
-__global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm) {
+// The receivers of wave slot ws (RPW of them): one per GPR groups.
+template <class LY, typename IN, int CPL, int GPR, bool UL, bool LIN>
+__device__ __forceinline__ void fwd_pipe_receivers(const FwdParams& prm, int ws, const float* lin_w,
+                                                   float* lin_row) {
   constexpr int C = LY::C, NO = LY::NO;
   constexpr int LPG = C / CPL;
-  static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
   constexpr int G = 64 / LPG;
-  static_assert(G % GPR == 0, "groups per receiver must divide groups per wave");
   constexpr int RPW = G / GPR;
 
   const IN* __restrict__ x = static_cast<const IN*>(prm.x);
@@ -565,7 +683,7 @@ __global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm) {
   const int grp = lane / LPG;
   const int gi = grp % GPR;
   const int slot = grp / GPR;
-  const int bl = logical_wave() * RPW + slot;
+  const int bl = ws * RPW + slot;
   const bool valid = bl < prm.num_nodes;
   const int b = valid ? (prm.order ? prm.order[bl] : bl) : 0;
   const int c0 = li * CPL;
@@ -625,6 +743,10 @@ __global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm) {
         for (int d = LPG; d < LPG * GPR; d <<= 1) acc[o][c] += __shfl_xor(acc[o][c], d, 64);
   }
 
+  if constexpr (LIN) {
+    lin_epilogue<LY, CPL, GPR>(acc, lin_w, lin_row + slot * NO * C, prm, b, valid, li, gi);
+    return;
+  }
   if (valid) {
     float* orow = prm.out + (size_t)b * NO * C + c0;
 #pragma unroll
@@ -646,6 +768,35 @@ __global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm) {
   }
 }
 
+// LIN: the output linear fused into the epilogue.  Its weights (NB blocks of
+// C x C) are staged in LDS once per work-group, so the work-groups loop over
+// contiguous ranges of wave slots rather than taking one each.
+template <class LY, typename IN, int CPL, int GPR, bool UL = false, bool LIN = false>
+__global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm) {
+  constexpr int C = LY::C, NO = LY::NO;
+  constexpr int LPG = C / CPL;
+  static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
+  constexpr int G = 64 / LPG;
+  static_assert(G % GPR == 0, "groups per receiver must divide groups per wave");
+  constexpr int RPW = G / GPR;
+  if constexpr (!LIN) {
+    fwd_pipe_receivers<LY, IN, CPL, GPR, UL, false>(prm, logical_wave(), nullptr, nullptr);
+  } else {
+    constexpr int NB = num_blocks(LY::OCODE);
+    __shared__ float lin_w[NB * C * C];
+    __shared__ float lin_row[4][RPW * NO * C];    // one row per receiver slot of each wave
+    for (int i = threadIdx.x; i < NB * C * C; i += blockDim.x) lin_w[i] = prm.lin_w[i];
+    __syncthreads();
+    const int waves = (int)gridDim.x * 4;
+    const int slots = (prm.num_nodes + RPW - 1) / RPW;
+    const int per = (slots + waves - 1) / waves;
+    const int w0 = logical_wave() * per;
+    const int w1 = w0 + per < slots ? w0 + per : slots;
+    for (int ws = w0; ws < w1; ++ws)
+      fwd_pipe_receivers<LY, IN, CPL, GPR, UL, true>(prm, ws, lin_w, lin_row[threadIdx.x >> 6]);
+  }
+}
+
 // ------------------------------------------------------ forward-mode (JVP) --
 //
 // The convolution is trilinear in (x, y, s), so its derivative along a
@@ -654,20 +805,6 @@ __global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm) {
 // One pass reads both the primal and the tangent operands, builds K from y
 // and from dy, and accumulates the primal output (stored when out != NULL)
 // and the tangent output together.
-
-template <int CPL>
-__device__ __forceinline__ void store_row(float* dst, const float (&v)[CPL], float scale) {
-  if constexpr (CPL == 4) {
-    f32x4 w = {v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale};
-    __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(dst));
-  } else if constexpr (CPL == 2) {
-    f32x2 w = {v[0] * scale, v[1] * scale};
-    __builtin_nontemporal_store(w, reinterpret_cast<f32x2*>(dst));
-  } else {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) __builtin_nontemporal_store(v[c] * scale, dst + c);
-  }
-}
 
 template <class LY, typename IN, int CPL, int GPR>
 __global__ void __launch_bounds__(256) conv_jvp(JvpParams prm) {
@@ -1628,33 +1765,6 @@ __device__ __forceinline__ void load_row_uniform(const float* p, float (&v)[N]) 
   for (int i = 0; i < N; ++i) v[i] = q[i];
 }
 
-// A lane's CPL consecutive floats in LDS (its own channels: no exchange).
-template <int CPL>
-__device__ __forceinline__ void lds_store_ch(float* p, const float (&v)[CPL], float scale) {
-  if constexpr (CPL == 4) {
-    *reinterpret_cast<f32x4*>(p) = f32x4{v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale};
-  } else if constexpr (CPL == 2) {
-    *reinterpret_cast<f32x2*>(p) = f32x2{v[0] * scale, v[1] * scale};
-  } else {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) p[c] = v[c] * scale;
-  }
-}
-
-template <int CPL>
-__device__ __forceinline__ void lds_load_ch(const float* p, float (&v)[CPL]) {
-  if constexpr (CPL == 4) {
-    const f32x4 t = *reinterpret_cast<const f32x4*>(p);
-    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-  } else if constexpr (CPL == 2) {
-    const f32x2 t = *reinterpret_cast<const f32x2*>(p);
-    v[0] = t.x; v[1] = t.y;
-  } else {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) v[c] = p[c];
-  }
-}
-
 template <class LY, int CPL>
 struct PairBuf {
   float y[LY::NY];
@@ -1932,13 +2042,17 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <class LY, typename IN, int CPL, int GPR, bool UL = false>
+// LIN: the output linear fused into the epilogue (p.lin_w, p.lin_alpha).
+template <class LY, typename IN, int CPL, int GPR, bool UL = false, bool LIN = false>
 hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t st) {
   constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
   if (p.num_nodes <= 0) return hipSuccess;
   const long waves = (p.num_nodes + RPW - 1) / RPW;
   const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
-  hipLaunchKernelGGL((conv_fwd_pipe<LY, IN, CPL, GPR, UL>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  // the fused linear's work-groups loop over receivers: at most 1024 of them,
+  // each staging the weights once
+  const long grid = LIN && blocks > 1024 ? 1024 : blocks;
+  hipLaunchKernelGGL((conv_fwd_pipe<LY, IN, CPL, GPR, UL, LIN>), dim3((unsigned)grid), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

@@ -345,6 +345,29 @@ e3conv_status e3conv_forward_masked(e3conv_plan_t p, e3conv_dtype dt, const void
   return ok();
 }
 
+e3conv_status e3conv_forward_linear(e3conv_plan_t p, e3conv_dtype dt, const void* x, const void* y,
+                                    const void* s, const int32_t* src, const int32_t* row_ptr,
+                                    const int32_t* order, int64_t N, int64_t E, float scale,
+                                    const float* weights, float* out, void* stream) {
+  if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (dt != E3CONV_F32 && dt != E3CONV_BF16) return fail(E3CONV_ERR_INVALID_ARGUMENT, "bad dtype");
+  e3conv_status st = check_sizes(N, E, p->channels, p->num_out > p->num_x ? p->num_out : p->num_x);
+  if (st != E3CONV_OK) return st;
+  if (!std::isfinite(scale)) return fail(E3CONV_ERR_INVALID_ARGUMENT, "scale must be finite");
+  const e3c::FwdLauncher L = !p->kk ? nullptr : (dt == E3CONV_F32 ? p->kk->fwd_lin_f32 : p->kk->fwd_lin_bf16);
+  if (!L)
+    return fail(E3CONV_ERR_UNSUPPORTED,
+                "no fused output-linear kernel for this layout (call e3conv_forward, then e3conv_linear)");
+  if (N == 0) return ok();
+  if (!out || !row_ptr || !weights || (E > 0 && (!x || !y || !s || !src)))
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  e3c::FwdParams prm{x, y, s, src, row_ptr, order, out, (int)N, (int)E, 1.0f / p->avg, (int)N, weights,
+                     (float)(scale / std::sqrt((double)p->channels) / p->avg)};
+  const hipError_t err = L(prm, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "forward-linear launch");
+  return ok();
+}
+
 e3conv_status e3conv_forward_radial(e3conv_plan_t p, const float* x, const float* y, const float* r,
                                     const float* w1, const float* w2, int32_t num_basis,
                                     int32_t hidden, float r_max, float sigma, const int32_t* src,

@@ -23,6 +23,8 @@ struct FwdParams {
   int num_edges;
   float inv_avg;
   int num_real;         // receivers b >= num_real are padding: zero rows, no messages
+  const float* lin_w;   // fused output linear: (blocks, C, C) weights, or unused
+  float lin_alpha;      // its factor scale / sqrt(C) / N
 };
 
 struct BwdParams {
@@ -111,6 +113,8 @@ struct OrderingKernels {
   JvpLauncher jvp_bf16;
   RadialLauncher radial_f32;    // nullptr: no radial-scalar kernel for this layout
   BwdLauncher bwd_pairs_f32;    // pair-stored reverse pass, or nullptr
+  FwdLauncher fwd_lin_f32;      // forward with the output linear fused, or nullptr
+  FwdLauncher fwd_lin_bf16;
 };
 
 struct KernelSet {

@@ -41,7 +41,7 @@ EXPORTED = [
     "e3conv_linear", "e3conv_linear_backward", "e3conv_csr_from_receivers",
     "e3conv_validate_graph", "e3conv_validate_graph_async", "e3conv_validate_graph_noalloc",
     "e3conv_receiver_order",
-    "e3conv_stream_reference", "e3conv_second_derivatives", "e3conv_backward_pairs", "e3conv_pair_layout",
+    "e3conv_stream_reference", "e3conv_second_derivatives", "e3conv_backward_pairs", "e3conv_pair_layout", "e3conv_forward_linear",
     "e3conv_plan_set_variant",
     "e3conv_plan_num_variants",
     "e3conv_status_string", "e3conv_last_error_detail",
@@ -112,6 +112,8 @@ def load_library(path=LIB_PATH):
         "e3conv_validate_graph_noalloc": ([P, P, I64, I64, P], ctypes.c_int),
         "e3conv_backward_pairs": ([P, P, P, P, P, P, I64, I64, P, P, P, P, P], ctypes.c_int),
         "e3conv_pair_layout": ([P, P, I64, I64, ctypes.c_int, P, P], ctypes.c_int),
+        "e3conv_forward_linear": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, ctypes.c_float, P, P, P],
+                                  ctypes.c_int),
         "e3conv_second_derivatives": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P, P, P, P,
                                        P, P, P, P, P], ctypes.c_int),
         "e3conv_plan_set_variant": ([P, ctypes.c_int, ctypes.c_int], ctypes.c_int),
@@ -362,6 +364,23 @@ def e3conv_backward_pairs(handle, x, y, s, src, dst, num_nodes, num_pairs, grad_
                                                 _ptr(grad_s), _stream(stream)))
 
 
+def e3conv_forward_linear(handle, x, y, s, src, row_ptr, num_nodes, num_edges, scale, weights, out,
+                          order=None, stream=None):
+    """The convolution with the output linear (C_out = C) fused into its epilogue."""
+    import torch
+    dt = _dtype_code(x)
+    for t, n in ((x, "x"), (y, "y"), (s, "s")):
+        _need(t, n, x.dtype)
+    _need(weights, "weights", torch.float32)
+    _need(out, "out", torch.float32)
+    _check_graph_args(src, row_ptr, order)
+    _check(load_library().e3conv_forward_linear(handle, dt, _ptr(x), _ptr(y), _ptr(s), _ptr(src),
+                                                _ptr(row_ptr), _ptr(order), int(num_nodes),
+                                                int(num_edges), float(scale), _ptr(weights), _ptr(out),
+                                                _stream(stream)))
+    return out
+
+
 def e3conv_linear(handle, channels_out, scale, weights, inp, num_nodes, out, stream=None):
     import torch
     for t, n in ((weights, "weights"), (inp, "in"), (out, "out")):
@@ -532,6 +551,12 @@ class Plan:
 
     def num_out_blocks(self):
         return len({(p["l3"], p["p3"]) for p in self.paths()})
+
+    def kernels_fused_linear(self, dtype=E3CONV_F32):
+        """True if this plan has the forward with the output linear in its epilogue
+        (asked with an empty graph: num_nodes = 0 is a no-op where it is compiled)."""
+        return load_library().e3conv_forward_linear(self.handle, dtype, None, None, None, None, None,
+                                                    None, 0, 0, 1.0, None, None, None) == E3CONV_OK
 
     def linear(self, inp, weights, channels_out, scale=1.0, out=None, stream=None):
         """Output linear (channel mixing per output irrep block); in (N, num_out, C)."""

@@ -337,6 +337,25 @@ e3conv_status e3conv_linear(e3conv_plan_t plan, int channels_out, float scale,
                             const float* weights, const float* in, int64_t num_nodes, float* out,
                             void* hip_stream);
 
+/* The convolution with the output linear fused into its epilogue: out =
+ * e3conv_linear(plan, C, scale, weights, e3conv_forward(...)) with
+ * channels_out = C, in one pass (cuEquivariance page, Flax NNX layers,
+ * IrrepsLinear, applied to the convolution's output).  Each receiver's row is
+ * mixed per output irrep block by the C x C weight block while still on chip,
+ * so the convolution's own output never reaches memory.  Arguments as
+ * e3conv_forward (x, y, s in in_dtype; out fp32 (num_nodes, num_out, C),
+ * fully overwritten) plus scale (finite) and weights (device float[
+ * num_out_blocks * C * C], blocks in the plan's output order, then u, then v,
+ * as e3conv_linear).  Compiled for RECEIVER plans of up to 64 channels, whose
+ * weight blocks fit one work-group's LDS (at most 64 KiB); other plans give
+ * E3CONV_ERR_UNSUPPORTED (use e3conv_forward, then e3conv_linear).  fp32
+ * products on the vector ALU; asynchronous on hip_stream. */
+e3conv_status e3conv_forward_linear(e3conv_plan_t plan, e3conv_dtype in_dtype, const void* x,
+                                    const void* y, const void* s, const int32_t* src,
+                                    const int32_t* row_ptr, const int32_t* order,
+                                    int64_t num_nodes, int64_t num_edges, float scale,
+                                    const float* weights, float* out, void* hip_stream);
+
 /* Reverse pass of e3conv_linear for L = <grad_out, out>:
  *   grad_in[b, i, u]   = scale / sqrt(C) * sum_v weights[k, u, v] grad_out[b, i, v]
  *   grad_weights[k, u, v] = scale / sqrt(C) * sum_{b, i in block k} in[b, i, u] grad_out[b, i, v]

@@ -73,3 +73,83 @@ def test_conv_then_linear():
     err = rel_err(out.cpu().numpy(), ref)
     say(f"[conv -> linear] N={inp.num_nodes} max|err|/RMS {err:.3e}")
     assert err <= 1e-5
+
+
+def _bf16_dev(a):
+    import torch
+    return torch.from_numpy(synth.bf16_bits(np.asarray(a, np.float32)).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("idx,kw,bf16", [(0, {}, False), (1, {"num_graphs": 6}, False),
+                                         (3, {"num_nodes": 501}, True), (3, {"num_nodes": 301}, False),
+                                         (0, {}, True), (1, {"num_graphs": 2}, True)],
+                         ids=["tiny", "gate", "big-bf16", "big-f32", "tiny-bf16", "gate-bf16"])
+def test_forward_linear_fused_parity(idx, kw, bf16):
+    """e3conv_forward_linear against oracle.linear(oracle.conv(...)) on the layouts of
+    up to 64 channels, and against the two separate calls on the device."""
+    import torch
+    inp = synth.make_inputs(idx, **kw)
+    w = inp.workload
+    lay = conv.make_layout(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    x, y, s = inp.as_f32("x"), inp.as_f32("y"), inp.as_f32("s")
+    if bf16:        # the values the kernel reads
+        x, y, s = (synth.bf16_to_f32(synth.bf16_bits(a.astype(np.float32))).reshape(a.shape) for a in (x, y, s))
+    rng = np.random.default_rng(idx + 70)
+    W = rng.standard_normal((plan.num_out_blocks(), w.channels, w.channels)).astype(np.float32)
+    scale = 0.7
+    N, Ec = inp.num_nodes, inp.num_edges
+    ref = linear.linear(lay, W, scale, conv.forward(lay, x, y, s, inp.senders, inp.receivers, N))
+    dev = _bf16_dev if bf16 else cuda
+    dx, dy, ds = dev(x), dev(y), dev(s)
+    src = icuda(inp.senders)
+    row_ptr = E.e3conv_csr_from_receivers(icuda(inp.receivers), N)
+    out = torch.full((N, lay.num_out, w.channels), 3.0, device="cuda")
+    E.e3conv_forward_linear(plan.handle, dx, dy, ds, src, row_ptr, N, Ec, scale, cuda(W), out)
+    sep = plan.linear(plan.forward(dx, dy, ds, src, row_ptr), cuda(W), w.channels, scale)
+    torch.cuda.synchronize()
+    err, err_sep = rel_err(out.cpu().numpy(), ref), rel_err(sep.cpu().numpy(), ref)
+    say(f"[forward+linear fused] {w.name} bf16={bf16} N={N} E={Ec} max|err|/RMS {err:.3e} "
+        f"(separate calls {err_sep:.3e})")
+    assert err <= 1e-5 and err_sep <= 1e-5
+
+
+def test_forward_linear_edge_cases():
+    """Receivers without edges, a graph without edges, a receiver order, and the
+    128-channel layout (not compiled: the separate calls serve it)."""
+    import torch
+    w = synth.WORKLOADS[1]
+    lay = conv.make_layout(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    rng = np.random.default_rng(3)
+    N, Ec = 90, 400
+    dst = np.sort(rng.integers(0, 60, Ec))            # receivers 60..89 take no edges
+    src = rng.integers(0, N, Ec)
+    x = rng.standard_normal((N, lay.num_x, w.channels)).astype(np.float32)
+    y = synth.spherical_harmonics(w.lmax, rng.standard_normal((Ec, 3))).astype(np.float32)
+    s = rng.standard_normal((Ec, lay.num_paths, w.channels)).astype(np.float32)
+    W = rng.standard_normal((plan.num_out_blocks(), w.channels, w.channels)).astype(np.float32)
+    ref = linear.linear(lay, W, 1.3, conv.forward(lay, x, y, s, src, dst, N))
+    row_ptr = E.e3conv_csr_from_receivers(icuda(dst), N)
+    order = icuda(rng.permutation(N))
+    out = torch.full((N, lay.num_out, w.channels), 3.0, device="cuda")
+    E.e3conv_forward_linear(plan.handle, cuda(x), cuda(y), cuda(s), icuda(src), row_ptr, N, Ec, 1.3,
+                            cuda(W), out, order=order)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert rel_err(got, ref) <= 1e-5 and np.all(got[60:] == 0.0)
+    # no edges at all: zero rows
+    e0 = torch.zeros(0, dtype=torch.int32, device="cuda")
+    out0 = torch.full((N, lay.num_out, w.channels), 3.0, device="cuda")
+    E.e3conv_forward_linear(plan.handle, cuda(x), torch.zeros(0, lay.num_y, device="cuda"),
+                            torch.zeros(0, lay.num_paths, w.channels, device="cuda"), e0,
+                            E.e3conv_csr_from_receivers(e0, N), N, 0, 1.0, cuda(W), out0)
+    torch.cuda.synchronize()
+    assert float(out0.abs().max()) == 0.0
+    w2 = synth.WORKLOADS[2]
+    big = E.Plan(w2.irreps_in, w2.lmax, w2.irreps_out, w2.avg_num_neighbors)
+    with pytest.raises(E.E3ConvError) as err:
+        E.e3conv_forward_linear(big.handle, cuda(np.zeros((2, 4, 128))), cuda(np.zeros((1, 16))),
+                                cuda(np.zeros((1, 10, 128))), icuda([0]), icuda([0, 1, 1]), 2, 1, 1.0,
+                                cuda(np.zeros((4, 128, 128))), torch.empty(2, 16, 128, device="cuda"))
+    assert err.value.status == E.E3CONV_ERR_UNSUPPORTED
