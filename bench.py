@@ -523,6 +523,13 @@ def main():
         torch.cuda.empty_cache()
         res["w3_forward"] = bench_forward_workload(3, args)
         res["pairs_reverse"] = pairs_block(plan, w, inp, res["bwd_ms"], args)
+        # the small configurations' forwards (latency-bound: far from either roof)
+        res["w0_forward"] = bench_forward_workload(0, args)
+        res["w1_forward"] = bench_forward_workload(1, args)
+        res["bar_60pct_hbm"] = {
+            "w2_forward": res["w2_forward"]["hbm_frac"] >= 0.6,
+            "w3_forward": res["w3_forward"]["hbm_frac"] >= 0.6,
+            "w4_step": res["step_hbm_frac"] >= 0.6}
     print(json.dumps(res), flush=True)
 
 

@@ -371,12 +371,14 @@ def test_forward_linear_argument_errors(lib):
     f = ctypes.c_void_p(0x1000)
     n = ctypes.c_void_p(0)
     w = synth.WORKLOADS[1]
-    h = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors).handle
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)   # kept alive: owns h
+    h = plan.handle
     assert lib.e3conv_forward_linear(None, 0, f, f, f, f, f, None, 4, 4, 1.0, f, f, None) == 1
     assert lib.e3conv_forward_linear(h, 3, f, f, f, f, f, None, 4, 4, 1.0, f, f, None) == 1     # dtype
     assert lib.e3conv_forward_linear(h, 0, f, f, f, f, f, None, 4, 4, float("inf"), f, f, None) == 1
     assert lib.e3conv_forward_linear(h, 0, f, f, f, f, f, None, 4, 4, 1.0, n, f, None) == 1     # weights
     assert lib.e3conv_forward_linear(h, 0, n, n, n, n, n, None, 0, 0, 1.0, n, n, None) == 0     # no-op
     w2 = synth.WORKLOADS[2]                                                                      # 128 ch.
-    h2 = E.Plan(w2.irreps_in, w2.lmax, w2.irreps_out, w2.avg_num_neighbors).handle
+    plan2 = E.Plan(w2.irreps_in, w2.lmax, w2.irreps_out, w2.avg_num_neighbors)
+    h2 = plan2.handle
     assert lib.e3conv_forward_linear(h2, 0, f, f, f, f, f, None, 4, 4, 1.0, f, f, None) == 3
