@@ -657,7 +657,7 @@ e3conv_status e3conv_pair_layout(const int32_t* row_ptr, const int32_t* src, int
     return fail(E3CONV_ERR_INVALID_ARGUMENT, "sizes must fit int32 indices");
   if (cluster <= 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "cluster must be positive");
   if (E % 2 != 0) return fail(E3CONV_ERR_GRAPH, "a symmetric graph has an even number of edges");
-  if (N == 0) return ok();
+  if (N == 0) return E == 0 ? ok() : fail(E3CONV_ERR_GRAPH, "edges without nodes");
   if (!row_ptr || (E > 0 && (!src || !stored || !pair_of)))
     return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL pointer");
   const e3conv_status st = e3conv_validate_graph(src, row_ptr, N, E, 0);

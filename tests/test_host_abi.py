@@ -358,6 +358,10 @@ def test_pair_layout_rejects_graphs_that_are_not_symmetric():
         row_ptr, s, _ = _csr(np.array(src), np.array(dst), n)
         return E.e3conv_pair_layout(row_ptr, s, n, len(s))
     call([0, 1, 1, 2], [1, 0, 2, 1], 3)                              # symmetric: accepted
+    stored, pair_of = E.e3conv_pair_layout(np.zeros(1, np.int32), np.zeros(0, np.int32), 0, 0)
+    assert len(stored) == 0 and len(pair_of) == 0                    # empty graph
+    with pytest.raises(E.E3ConvError):
+        E.e3conv_pair_layout(np.zeros(1, np.int32), np.zeros(2, np.int32), 0, 2)   # edges, no nodes
     for src, dst in (([0, 1, 2], [1, 0, 0]),                         # odd edge count
                      ([0, 1, 0, 1], [1, 0, 2, 2]),                   # reverses missing
                      ([0, 1, 1, 1], [1, 0, 1, 1]),                   # self loops
