@@ -522,7 +522,7 @@ def main():
         del x, y, s, g, grads, out, order, order_dev, src, dst, row_ptr
         torch.cuda.empty_cache()
         res["w3_forward"] = bench_forward_workload(3, args)
-        res["pairs_reverse"] = pairs_block(plan, w, inp, res["bwd_ms"], args)
+        res["pairs_reverse"] = pairs_block(plan, w, inp, res["fwd_ms"], res["bwd_ms"], args)
         # the small configurations' forwards (latency-bound: far from either roof)
         res["w0_forward"] = bench_forward_workload(0, args)
         res["w1_forward"] = bench_forward_workload(1, args)
@@ -781,31 +781,39 @@ def pair_inputs(inp, cluster=512):
     return stored, pair_of, s_pair, layout_ms
 
 
-def time_pairs_reverse(plan, w, inp, stored, s_pair, args):
-    """HIP-event time (ms) of the pair-stored reverse pass on the device copies."""
+def time_pairs(plan, w, inp, stored, pmap, s_pair, args):
+    """HIP-event times (ms) of the pair-stored forward (directed receiver CSR, receiver
+    order, rows through the pair map) and of the pair-stored reverse pass."""
     import numpy as np
     import torch
 
     from equivariant_gnn_message_amd import e3conv as E
-    N, Ep = inp.num_nodes, len(stored)
+    N, Ec, Ep = inp.num_nodes, inp.num_edges, len(stored)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     x, g = t(inp.x), t(inp.g)
     y, s = t(inp.y[stored]), t(s_pair)
     src, dst = t(inp.senders[stored].astype(np.int32)), t(inp.receivers[stored].astype(np.int32))
+    dsrc, d_map = t(inp.senders.astype(np.int32)), t(pmap.astype(np.int32))
+    row_ptr = E.e3conv_csr_from_receivers(t(inp.receivers.astype(np.int32)), N)
+    order = t(E.e3conv_receiver_order(row_ptr.cpu().numpy(), inp.senders, N, Ec, args.cluster))
+    out = torch.empty((N, w.num_out, w.channels), dtype=torch.float32, device="cuda")
     gx, gy, gs = torch.empty_like(x), torch.empty_like(y), torch.empty_like(s)
-    ms = _timed(lambda: E.e3conv_backward_pairs(plan.handle, x, y, s, src, dst, N, Ep, g, gx, gy, gs),
-                args.steps, args.warmup)
-    del x, g, y, s, src, dst, gx, gy, gs
+    fwd_ms = _timed(lambda: E.e3conv_forward_pairs(plan.handle, x, y, s, dsrc, row_ptr, d_map, N, Ec, Ep,
+                                                   out, order=order), args.steps, args.warmup)
+    bwd_ms = _timed(lambda: E.e3conv_backward_pairs(plan.handle, x, y, s, src, dst, N, Ep, g, gx, gy, gs),
+                    args.steps, args.warmup)
+    del x, g, y, s, src, dst, dsrc, d_map, row_ptr, order, out, gx, gy, gs
     torch.cuda.empty_cache()
-    return ms
+    return fwd_ms, bwd_ms
 
 
-def pairs_block(plan, w, inp, directed_ms, args):
-    """The pair-stored reverse pass on the training graph (one s row per pair) next to
-    the directed reverse pass of the same graph (its time does not depend on the values)."""
-    stored, _, s_pair, layout_ms = pair_inputs(inp, args.cluster)
+def pairs_block(plan, w, inp, directed_fwd_ms, directed_ms, args):
+    """The pair-stored forward and reverse pass on the training graph (one y and s row per
+    pair) next to the directed passes of the same graph (their times do not depend on the
+    values)."""
+    stored, pmap, s_pair, layout_ms = pair_inputs(inp, args.cluster)
     N, Ec, Ep = inp.num_nodes, inp.num_edges, len(stored)
-    ms = time_pairs_reverse(plan, w, inp, stored, s_pair, args)
+    fwd_ms, ms = time_pairs(plan, w, inp, stored, pmap, s_pair, args)
     nbytes = pair_bytes(w, N, Ep)
     dir_bytes = alg_bytes(w, N, Ec, 4)[1]
     gbps = nbytes / (ms * 1e-3) / 1e9
@@ -815,7 +823,10 @@ def pairs_block(plan, w, inp, directed_ms, args):
             "hbm_GBps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS,
             "directed_reverse_ms": directed_ms, "directed_algorithmic_bytes": dir_bytes,
             "speedup_vs_directed": directed_ms / ms, "pair_layout_ms": layout_ms,
-            "pair_order": f"clustered {args.cluster}"}
+            "pair_order": f"clustered {args.cluster}",
+            "forward_ms": fwd_ms, "directed_forward_ms": directed_fwd_ms,
+            "step_ms": fwd_ms + ms, "directed_step_ms": directed_fwd_ms + directed_ms,
+            "step_speedup_vs_directed": (directed_fwd_ms + directed_ms) / (fwd_ms + ms)}
 
 
 def bench_pairs(args):
@@ -838,14 +849,18 @@ def bench_pairs(args):
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     # directed: the same graph with s expanded to both directions of each pair
     x, y, g = t(inp.x), t(inp.y), t(inp.g)
-    s = t(s_pair)[t(pair_of)]
+    s = t(s_pair)[t(np.where(pair_of >= 0, pair_of, ~pair_of))]
     src = t(inp.senders)
     row_ptr = E.e3conv_csr_from_receivers(t(inp.receivers), N)
     grads = (torch.empty_like(x), torch.empty_like(y), torch.empty_like(s))
+    order = t(E.e3conv_receiver_order(row_ptr.cpu().numpy(), inp.senders, N, Ec, args.cluster))
+    out = torch.empty((N, w.num_out, w.channels), dtype=torch.float32, device="cuda")
+    dir_fwd_ms = _timed(lambda: plan.forward(x, y, s, src, row_ptr, out=out, order=order), args.steps,
+                        args.warmup)
     dir_ms = _timed(lambda: plan.backward(x, y, s, src, row_ptr, g, grads=grads), args.steps, args.warmup)
-    del x, y, g, s, src, row_ptr, grads
+    del x, y, g, s, src, row_ptr, grads, order, out
     torch.cuda.empty_cache()
-    pair_ms = time_pairs_reverse(plan, w, inp, stored, s_pair, args)
+    pair_fwd_ms, pair_ms = time_pairs(plan, w, inp, stored, pair_of, s_pair, args)
     pb, db = pair_bytes(w, N, Ep), alg_bytes(w, N, Ec, 4)[1]
     res = {"metric": "directed edges/sec of the reverse pass, y and s stored once per undirected pair, "
                      "1 MI355X",
@@ -861,6 +876,9 @@ def bench_pairs(args):
            "directed_hbm_GBps": db / (dir_ms * 1e-3) / 1e9,
            "speedup_vs_directed": dir_ms / pair_ms, "pair_layout_ms": layout_ms,
            "pair_order": f"clustered {args.cluster}",
+           "pairs_forward_ms": pair_fwd_ms, "directed_forward_ms": dir_fwd_ms,
+           "pairs_step_ms": pair_fwd_ms + pair_ms, "directed_step_ms": dir_fwd_ms + dir_ms,
+           "step_speedup_vs_directed": (dir_fwd_ms + dir_ms) / (pair_fwd_ms + pair_ms),
            "roofline": roofline("conv_bwd_pairs", pair_ms, pb,
                                 traffic=traffic_from_profiles("conv_bwd_pairs", args.workload))}
     res["cpu_baseline"] = None

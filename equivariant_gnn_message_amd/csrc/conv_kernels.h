@@ -582,6 +582,7 @@ struct EdgeBuf {
   RawVec<IN, LY::NY> y;
   RawVec<IN, CPL> x[LY::NX];
   RawVec<IN, CPL> s[LY::NP];
+  float ysg;              // pair-stored rows: -1 when the edge is its pair's reverse (P y)
 };
 
 template <class LY, typename IN, int CPL>
@@ -598,13 +599,30 @@ __device__ __forceinline__ void load_edge(EdgeBuf<LY, IN, CPL>& buf, const IN* _
   for (int i = 0; i < NX; ++i) load_raw<IN, CPL, false>(xrow + i * C, buf.x[i]);
 }
 
+// Pair-stored edge data (PR): the edge's y and s rows are its pair's, read at
+// row |p| of the pair arrays, with the odd-l blocks of y negated when the
+// edge is the reverse of the stored one (p < 0: ~p is the pair).
 template <class LY, typename IN, int CPL>
+__device__ __forceinline__ void load_edge_pair(EdgeBuf<LY, IN, CPL>& buf, const IN* __restrict__ x,
+                                               const IN* __restrict__ y, const IN* __restrict__ s,
+                                               int p, int a, int c0) {
+  load_edge<LY, IN, CPL>(buf, x, y, s, p >= 0 ? p : ~p, a, c0);
+  buf.ysg = p >= 0 ? 1.0f : -1.0f;
+}
+
+template <class LY, typename IN, int CPL, bool PR = false>
 __device__ __forceinline__ void edge_accumulate(const EdgeBuf<LY, IN, CPL>& buf,
                                                 float (&acc)[LY::NO][CPL]) {
   constexpr int NY = LY::NY, NP = LY::NP;
   float yv[NY];
 #pragma unroll
   for (int j = 0; j < NY; ++j) yv[j] = buf.y.get(j);
+  if constexpr (PR) {
+#pragma unroll
+    for (int l = 1; l * l < NY; l += 2)
+#pragma unroll
+      for (int j = l * l; j < (l + 1) * (l + 1); ++j) yv[j] *= buf.ysg;
+  }
   sfor<0, NP>([&](auto pc) {
     constexpr int p = decltype(pc)::value;
     constexpr PathInfo P = LY::T.path[p];
@@ -664,7 +682,7 @@ __device__ __forceinline__ void edge_accumulate(const EdgeBuf<LY, IN, CPL>& buf,
 // for every load in flight, the next edge's rows included). Which form is
 // faster depends on the layout.
 // The receivers of wave slot ws (RPW of them): one per GPR groups.
-template <class LY, typename IN, int CPL, int GPR, bool UL, bool LIN>
+template <class LY, typename IN, int CPL, int GPR, bool UL, bool LIN, bool PR>
 __device__ __forceinline__ void fwd_pipe_receivers(const FwdParams& prm, int ws, const float* lin_w,
                                                    float* lin_row) {
   constexpr int C = LY::C, NO = LY::NO;
@@ -700,38 +718,55 @@ __device__ __forceinline__ void fwd_pipe_receivers(const FwdParams& prm, int ws,
     end = b < prm.num_real ? row_ptr[b + 1] : beg;   // padding receivers: no messages
   }
 
+  // PR: the pair map entry of an edge is fetched with its sender index
+  const int* __restrict__ emap = prm.emap;
+  auto pmap = [&](int ee) { return PR ? emap[ee] : 0; };
+  auto ld = [&](EdgeBuf<LY, IN, CPL>& buf, int ee, int a, int pm) {
+    if constexpr (PR) {
+      load_edge_pair<LY, IN, CPL>(buf, x, y, s, pm, a, c0);
+    } else {
+      load_edge<LY, IN, CPL>(buf, x, y, s, ee, a, c0);
+    }
+  };
   EdgeBuf<LY, IN, CPL> b0, b1;
   int e = beg + gi;
-  if (e < end) load_edge<LY, IN, CPL>(b0, x, y, s, e, src[e], c0);
+  if (e < end) ld(b0, e, src[e], pmap(e));
   int en = e + GPR;
   int an = en < end ? src[en] : 0;
+  int pn = en < end ? pmap(en) : 0;
   while (e < end) {
     int en2 = en + GPR;
-    int an2;
+    int an2, pn2;
     if constexpr (UL) {
       an2 = src[en2 < end ? en2 : end - 1];
-      load_edge<LY, IN, CPL>(b1, x, y, s, en < end ? en : end - 1, an, c0);
+      pn2 = pmap(en2 < end ? en2 : end - 1);
+      ld(b1, en < end ? en : end - 1, an, pn);
     } else {
-      if (en < end) load_edge<LY, IN, CPL>(b1, x, y, s, en, an, c0);
+      if (en < end) ld(b1, en, an, pn);
       an2 = en2 < end ? src[en2] : 0;
+      pn2 = en2 < end ? pmap(en2) : 0;
     }
-    edge_accumulate<LY, IN, CPL>(b0, acc);
+    edge_accumulate<LY, IN, CPL, PR>(b0, acc);
     e = en;
     en = en2;
     an = an2;
+    pn = pn2;
     if (e >= end) break;
     en2 = en + GPR;
     if constexpr (UL) {
       an2 = src[en2 < end ? en2 : end - 1];
-      load_edge<LY, IN, CPL>(b0, x, y, s, en < end ? en : end - 1, an, c0);
+      pn2 = pmap(en2 < end ? en2 : end - 1);
+      ld(b0, en < end ? en : end - 1, an, pn);
     } else {
-      if (en < end) load_edge<LY, IN, CPL>(b0, x, y, s, en, an, c0);
+      if (en < end) ld(b0, en, an, pn);
       an2 = en2 < end ? src[en2] : 0;
+      pn2 = en2 < end ? pmap(en2) : 0;
     }
-    edge_accumulate<LY, IN, CPL>(b1, acc);
+    edge_accumulate<LY, IN, CPL, PR>(b1, acc);
     e = en;
     en = en2;
     an = an2;
+    pn = pn2;
   }
 
   if constexpr (GPR > 1) {
@@ -771,8 +806,9 @@ __device__ __forceinline__ void fwd_pipe_receivers(const FwdParams& prm, int ws,
 // LIN: the output linear fused into the epilogue.  Its weights (NB blocks of
 // C x C) are staged in LDS once per work-group, so the work-groups loop over
 // contiguous ranges of wave slots rather than taking one each.
-template <class LY, typename IN, int CPL, int GPR, bool UL = false, bool LIN = false>
-__global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm) {
+template <class LY, typename IN, int CPL, int GPR, bool UL = false, bool LIN = false, bool PR = false>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PR ? 2 : 1)))
+conv_fwd_pipe(FwdParams prm) {
   constexpr int C = LY::C, NO = LY::NO;
   constexpr int LPG = C / CPL;
   static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
@@ -780,7 +816,7 @@ __global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm) {
   static_assert(G % GPR == 0, "groups per receiver must divide groups per wave");
   constexpr int RPW = G / GPR;
   if constexpr (!LIN) {
-    fwd_pipe_receivers<LY, IN, CPL, GPR, UL, false>(prm, logical_wave(), nullptr, nullptr);
+    fwd_pipe_receivers<LY, IN, CPL, GPR, UL, false, PR>(prm, logical_wave(), nullptr, nullptr);
   } else {
     constexpr int NB = num_blocks(LY::OCODE);
     __shared__ float lin_w[NB * C * C];
@@ -793,7 +829,7 @@ __global__ void __launch_bounds__(256) conv_fwd_pipe(FwdParams prm) {
     const int w0 = logical_wave() * per;
     const int w1 = w0 + per < slots ? w0 + per : slots;
     for (int ws = w0; ws < w1; ++ws)
-      fwd_pipe_receivers<LY, IN, CPL, GPR, UL, true>(prm, ws, lin_w, lin_row[threadIdx.x >> 6]);
+      fwd_pipe_receivers<LY, IN, CPL, GPR, UL, true, PR>(prm, ws, lin_w, lin_row[threadIdx.x >> 6]);
   }
 }
 
@@ -2043,7 +2079,8 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t st) {
 }
 
 // LIN: the output linear fused into the epilogue (p.lin_w, p.lin_alpha).
-template <class LY, typename IN, int CPL, int GPR, bool UL = false, bool LIN = false>
+// PR: y and s read from pair-stored rows through p.emap.
+template <class LY, typename IN, int CPL, int GPR, bool UL = false, bool LIN = false, bool PR = false>
 hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t st) {
   constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
   if (p.num_nodes <= 0) return hipSuccess;
@@ -2052,7 +2089,8 @@ hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t st) {
   // the fused linear's work-groups loop over receivers: at most 1024 of them,
   // each staging the weights once
   const long grid = LIN && blocks > 1024 ? 1024 : blocks;
-  hipLaunchKernelGGL((conv_fwd_pipe<LY, IN, CPL, GPR, UL, LIN>), dim3((unsigned)grid), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((conv_fwd_pipe<LY, IN, CPL, GPR, UL, LIN, PR>), dim3((unsigned)grid), dim3(256), 0, st,
+                     p);
   return hipGetLastError();
 }
 

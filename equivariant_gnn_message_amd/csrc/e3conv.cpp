@@ -368,6 +368,28 @@ e3conv_status e3conv_forward_linear(e3conv_plan_t p, e3conv_dtype dt, const void
   return ok();
 }
 
+e3conv_status e3conv_forward_pairs(e3conv_plan_t p, const float* x, const float* y, const float* s,
+                                   const int32_t* src, const int32_t* row_ptr, const int32_t* pair_of,
+                                   const int32_t* order, int64_t N, int64_t E, int64_t num_pairs,
+                                   float* out, void* stream) {
+  if (!p) return fail(E3CONV_ERR_INVALID_ARGUMENT, "plan is NULL");
+  e3conv_status st = check_sizes(N, E, p->channels, p->num_out > p->num_x ? p->num_out : p->num_x);
+  if (st != E3CONV_OK) return st;
+  if (num_pairs < 0 || num_pairs > E) return fail(E3CONV_ERR_INVALID_ARGUMENT, "num_pairs out of range");
+  if (p->ordering != E3CONV_RECEIVER)
+    return fail(E3CONV_ERR_UNSUPPORTED, "the pair-stored forward takes a RECEIVER plan");
+  if (!p->kk || !p->kk->fwd_pairs_f32)
+    return fail(E3CONV_ERR_UNSUPPORTED, "no compiled pair-stored forward for this layout");
+  if (N == 0) return ok();
+  if (!out || !row_ptr || (E > 0 && (!x || !y || !s || !src || !pair_of)))
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+  e3c::FwdParams prm{x, y, s, src, row_ptr, order, out, (int)N, (int)E, 1.0f / p->avg, (int)N, nullptr,
+                     0.0f, pair_of};
+  const hipError_t err = p->kk->fwd_pairs_f32(prm, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "pair-stored forward launch");
+  return ok();
+}
+
 e3conv_status e3conv_forward_radial(e3conv_plan_t p, const float* x, const float* y, const float* r,
                                     const float* w1, const float* w2, int32_t num_basis,
                                     int32_t hidden, float r_max, float sigma, const int32_t* src,
@@ -690,7 +712,7 @@ e3conv_status e3conv_pair_layout(const int32_t* row_ptr, const int32_t* src, int
       const auto it = slot.find((int64_t)std::min(a, b) * N + std::max(a, b));
       if (it == slot.end() || ++seen[it->second] > 2)
         return fail(E3CONV_ERR_GRAPH, "graph is not symmetric at edge " + std::to_string(e));
-      pair_of[e] = it->second;
+      pair_of[e] = stored[it->second] == e ? it->second : ~it->second;
     }
   }
   return ok();

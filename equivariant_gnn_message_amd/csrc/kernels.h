@@ -25,6 +25,7 @@ struct FwdParams {
   int num_real;         // receivers b >= num_real are padding: zero rows, no messages
   const float* lin_w;   // fused output linear: (blocks, C, C) weights, or unused
   float lin_alpha;      // its factor scale / sqrt(C) / N
+  const int* emap;      // pair-stored rows: (E) pair of each edge, ~pair when reversed; or unused
 };
 
 struct BwdParams {
@@ -115,6 +116,7 @@ struct OrderingKernels {
   BwdLauncher bwd_pairs_f32;    // pair-stored reverse pass, or nullptr
   FwdLauncher fwd_lin_f32;      // forward with the output linear fused, or nullptr
   FwdLauncher fwd_lin_bf16;
+  FwdLauncher fwd_pairs_f32;    // forward reading pair-stored y and s, or nullptr
 };
 
 struct KernelSet {

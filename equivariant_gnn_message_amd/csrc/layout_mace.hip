@@ -33,7 +33,7 @@ const KernelSet* kernels_mace() {
     L::C, L::XCODE, L::L, L::OCODE, &kTables, kCG.v,
     {kF32, E3C_N(kF32), kBF16, E3C_N(kBF16), kBwd, E3C_N(kBwd), launch_bwd_pipe<L, 2, 1, true>,
      launch_jvp_pipe<L, float, 2, 1, false>, launch_jvp_pipe<L, bf16_bits, 2, 1, true>, nullptr,
-     launch_bwd_pairs<L, 2, 16>},
+     launch_bwd_pairs<L, 2, 16>, nullptr, nullptr, launch_fwd_pipe<L, float, 2, 1, false, false, true>},
     {kSenderF32, 1, kSenderBF16, 1, kSenderBwd, 1, launch_bwd_pipe<LS, 2, 1, true>,
      launch_jvp_pipe<LS, float, 2, 1, false>, launch_jvp_pipe<LS, bf16_bits, 2, 1, true>},
   };

@@ -31,7 +31,7 @@ const KernelSet* kernels_tiny() {
     {kF32, E3C_N(kF32), kBF16, E3C_N(kBF16), kBwd, E3C_N(kBwd), launch_bwd_pipe<L, 2, 4, true>,
      launch_jvp<L, float, 2, 4>, launch_jvp<L, bf16_bits, 2, 4>, nullptr,
      launch_bwd_pairs<L, 2, 16>, launch_fwd_pipe<L, float, 4, 4, false, true>,
-     launch_fwd_pipe<L, bf16_bits, 4, 4, false, true>},
+     launch_fwd_pipe<L, bf16_bits, 4, 4, false, true>, launch_fwd_pipe<L, float, 4, 4, false, false, true>},
     {kSenderF32, 1, kSenderBF16, 1, kSenderBwd, 1, launch_bwd_pipe<LS, 2, 4, true>,
      launch_jvp<LS, float, 2, 4>, launch_jvp<LS, bf16_bits, 2, 4>},
   };

@@ -41,7 +41,7 @@ EXPORTED = [
     "e3conv_linear", "e3conv_linear_backward", "e3conv_csr_from_receivers",
     "e3conv_validate_graph", "e3conv_validate_graph_async", "e3conv_validate_graph_noalloc",
     "e3conv_receiver_order",
-    "e3conv_stream_reference", "e3conv_second_derivatives", "e3conv_backward_pairs", "e3conv_pair_layout", "e3conv_forward_linear",
+    "e3conv_stream_reference", "e3conv_second_derivatives", "e3conv_backward_pairs", "e3conv_pair_layout", "e3conv_forward_linear", "e3conv_forward_pairs",
     "e3conv_plan_set_variant",
     "e3conv_plan_num_variants",
     "e3conv_status_string", "e3conv_last_error_detail",
@@ -112,6 +112,7 @@ def load_library(path=LIB_PATH):
         "e3conv_validate_graph_noalloc": ([P, P, I64, I64, P], ctypes.c_int),
         "e3conv_backward_pairs": ([P, P, P, P, P, P, I64, I64, P, P, P, P, P], ctypes.c_int),
         "e3conv_pair_layout": ([P, P, I64, I64, ctypes.c_int, P, P], ctypes.c_int),
+        "e3conv_forward_pairs": ([P, P, P, P, P, P, P, P, I64, I64, I64, P, P], ctypes.c_int),
         "e3conv_forward_linear": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, ctypes.c_float, P, P, P],
                                   ctypes.c_int),
         "e3conv_second_derivatives": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P, P, P, P,
@@ -349,6 +350,21 @@ def e3conv_backward_ex(handle, x, y, s, src, row_ptr, num_nodes, num_edges, num_
         _ptr(grad_y), _ptr(grad_s), int(flags), _ptr(workspace), wbytes, _stream(stream)))
 
 
+def e3conv_forward_pairs(handle, x, y, s, src, row_ptr, pair_of, num_nodes, num_edges, num_pairs, out,
+                         order=None, stream=None):
+    """Forward over the directed receiver CSR with y and s read from pair-stored rows."""
+    import torch
+    for t, n in ((x, "x"), (y, "y"), (s, "s"), (out, "out")):
+        _need(t, n, torch.float32)
+    _need(pair_of, "pair_of", torch.int32)
+    _check_graph_args(src, row_ptr, order)
+    _check(load_library().e3conv_forward_pairs(handle, _ptr(x), _ptr(y), _ptr(s), _ptr(src),
+                                               _ptr(row_ptr), _ptr(pair_of), _ptr(order), int(num_nodes),
+                                               int(num_edges), int(num_pairs), _ptr(out),
+                                               _stream(stream)))
+    return out
+
+
 def e3conv_backward_pairs(handle, x, y, s, src, dst, num_nodes, num_pairs, grad_out, grad_x,
                           grad_y, grad_s, stream=None):
     """Pair-stored reverse pass: each stored edge (src -> dst) stands for itself and its reverse."""
@@ -429,7 +445,8 @@ def e3conv_receiver_order(row_ptr, src, num_nodes, num_edges, cluster=512):
 
 
 def e3conv_pair_layout(row_ptr, src, num_nodes, num_edges, cluster=512):
-    """Host-side pair storage of a symmetric graph: (stored, pair_of) as numpy int32."""
+    """Host-side pair storage of a symmetric graph: (stored, pair_of) as numpy int32; pair_of[e]
+    is the pair of directed edge e, or ~pair when e is the reverse of the stored edge."""
     import numpy as np
     r = np.ascontiguousarray(np.asarray(row_ptr), dtype=np.int32)
     s = np.ascontiguousarray(np.asarray(src), dtype=np.int32)

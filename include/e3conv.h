@@ -385,6 +385,25 @@ e3conv_status e3conv_csr_from_receivers(const int32_t* receivers_sorted, int64_t
 e3conv_status e3conv_receiver_order(const int32_t* row_ptr, const int32_t* src, int64_t num_nodes,
                                     int64_t num_edges, int cluster, int32_t* order);
 
+/* Forward of pair-stored edge data: the function whose reverse pass is
+ * e3conv_backward_pairs (e3j Convolution page, the note on SENDER ordering:
+ * symmetric graph, y_ba = (-1)^l y_ab, s_ba = s_ab).  The messages are summed
+ * over the directed receiver CSR (src, row_ptr, order, num_edges = 2 *
+ * num_pairs, exactly as e3conv_forward), but each edge reads its y and s rows
+ * from the pair arrays: row k = pair_of[e] if that is >= 0, else row ~k with
+ * the odd-l blocks of y negated (the edge is the reverse of the stored one).
+ * y (num_pairs, num_y) and s (num_pairs, num_paths, C) hold one row per pair;
+ * pair_of is device int32[num_edges] in [-num_pairs, num_pairs) (out of range
+ * is undefined behaviour), as e3conv_pair_layout writes it.  Every s row is
+ * read twice (once per direction), so the bytes equal e3conv_forward's; the
+ * edge data takes half the memory.  x and out as e3conv_forward (fp32).
+ * RECEIVER plans; E3CONV_ERR_UNSUPPORTED for a layout without this kernel. */
+e3conv_status e3conv_forward_pairs(e3conv_plan_t plan, const float* x, const float* y, const float* s,
+                                   const int32_t* src, const int32_t* row_ptr,
+                                   const int32_t* pair_of, const int32_t* order, int64_t num_nodes,
+                                   int64_t num_edges, int64_t num_pairs, float* out,
+                                   void* hip_stream);
+
 /* Pair storage for e3conv_backward_pairs (host only, once per graph, like the
  * receiver order).  From the host receiver CSR (row_ptr, src) of a graph that
  * holds b -> a whenever it holds a -> b, once each, without self loops (the
@@ -397,8 +416,11 @@ e3conv_status e3conv_receiver_order(const int32_t* row_ptr, const int32_t* src, 
  *   stored[num_edges / 2]  the directed edge of each stored pair (so the pair
  *                          arrays are y[stored], s[stored], src[stored] and the
  *                          receivers of those edges);
- *   pair_of[num_edges]     for every directed edge, the position of its pair
- *                          in stored (the directed rows of s are s_pair[pair_of]).
+ *   pair_of[num_edges]     for every directed edge e, the position k of its pair
+ *                          in stored if e is the stored edge, else ~k = -k - 1
+ *                          (e is the stored edge's reverse); the directed rows
+ *                          of s are s_pair[k], those of y are y_pair[k] and
+ *                          P y_pair[k] (the map e3conv_forward_pairs takes).
  * E3CONV_ERR_GRAPH if the graph is invalid (as e3conv_validate_graph), not
  * symmetric, has a repeated edge, a self loop or an odd number of edges. */
 e3conv_status e3conv_pair_layout(const int32_t* row_ptr, const int32_t* src, int64_t num_nodes,

@@ -236,3 +236,86 @@ def test_pairs_full_training_size_sampled():
     val = float(np.vdot(gs.astype(np.float64), s.astype(np.float64)))
     say(f"  <g,out> {L:.6e} vs <grad_s,s> {val:.6e}")
     assert abs(val - L) <= 1e-5 * abs(L)
+
+
+# ------------------------------------------------------- pair-stored forward -----
+
+def pair_layout(inp):
+    """e3conv_pair_layout of a workload's radius graph: stored edges and the signed map."""
+    N, Ec = inp.num_nodes, inp.num_edges
+    row_ptr = np.searchsorted(inp.receivers, np.arange(N + 1)).astype(np.int32)
+    return E.e3conv_pair_layout(row_ptr, inp.senders, N, Ec, 64)
+
+
+def run_forward_pairs(w, x, y_p, s_p, inp, pmap, order=None):
+    import torch
+    plan = plan_of(w)
+    N, Ec = inp.num_nodes, inp.num_edges
+    d_dst = dev(inp.receivers, np.int32)
+    row_ptr = E.e3conv_csr_from_receivers(d_dst, N)
+    out = torch.full((N, plan.num_out, plan.channels), 5.0, device="cuda")
+    E.e3conv_forward_pairs(plan.handle, dev(x), dev(y_p), dev(s_p), dev(inp.senders, np.int32), row_ptr,
+                           dev(pmap, np.int32), N, Ec, len(y_p), out,
+                           order=None if order is None else dev(order, np.int32))
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), plan, row_ptr
+
+
+@pytest.mark.parametrize("idx,kw", [(1, {"num_graphs": 3}), (2, {"num_nodes": 601}),
+                                    (3, {"num_nodes": 401})], ids=["w1-gate", "w2-n601", "w3-n401"])
+def test_forward_pairs_parity(idx, kw):
+    """Against oracle.variants.forward_pairs, and bitwise against the directed forward of the
+    expanded rows (s_pair[k], and y_pair[k] with the odd-l blocks negated for reverses)."""
+    import torch
+    inp = synth.make_inputs(idx, with_cotangent=True, **kw)
+    w = inp.workload
+    x, y = inp.as_f32("x"), inp.as_f32("y")
+    stored, pmap = pair_layout(inp)
+    k = np.where(pmap >= 0, pmap, ~pmap)
+    y_p = y[stored]
+    if idx == 1:
+        s_p = inp.as_f32("s")[stored]
+    else:
+        s_p = synth.normal_f32(w.idx, synth.T_S_PAIR, (len(stored),) + inp.s.shape[1:])
+    N = inp.num_nodes
+    say(f"[forward pairs] workload {idx} N={N} pairs={len(stored)}")
+    got, plan, row_ptr = run_forward_pairs(w, x, y_p, s_p, inp, pmap)
+    ref = variants.forward_pairs(lay_of(w), x, y_p, s_p, inp.senders[stored], inp.receivers[stored], N)
+    err = rel_err(got, ref)
+    say(f"  max|err|/RMS {err:.3e}")
+    assert err <= TOL
+    P = variants.parity_sign(lay_of(w)).astype(np.float32)
+    y_dir = np.where((pmap >= 0)[:, None], y_p[k], y_p[k] * P)
+    dirc = plan.forward(dev(x), dev(y_dir), dev(s_p[k]), dev(inp.senders, np.int32), row_ptr)
+    torch.cuda.synchronize()
+    assert np.array_equal(got, dirc.cpu().numpy())
+
+
+def test_forward_pairs_order_and_full_size():
+    """The training graph at full size with the receiver order the benchmark uses:
+    bitwise equal to the directed forward of the expanded rows, sampled rows against
+    the oracle."""
+    import torch
+    inp = synth.make_inputs(4)
+    w, N = inp.workload, inp.num_nodes
+    stored, pmap = pair_layout(inp)
+    k = np.where(pmap >= 0, pmap, ~pmap)
+    y_p = inp.y[stored]
+    s_p = synth.normal_f32(w.idx, synth.T_S_PAIR, (len(stored), w.num_paths, w.channels))
+    row_ptr_h = np.searchsorted(inp.receivers, np.arange(N + 1)).astype(np.int32)
+    order = E.e3conv_receiver_order(row_ptr_h, inp.senders, N, inp.num_edges, 512)
+    say(f"[forward pairs full size] N={N} pairs={len(stored)}")
+    got, plan, row_ptr = run_forward_pairs(w, inp.x, y_p, s_p, inp, pmap, order=order)
+    P = variants.parity_sign(lay_of(w)).astype(np.float32)
+    y_dir = np.where((pmap >= 0)[:, None], y_p[k], y_p[k] * P)
+    dirc = plan.forward(dev(inp.x), dev(y_dir), dev(s_p[k]), dev(inp.senders, np.int32), row_ptr,
+                        order=dev(order, np.int32))
+    torch.cuda.synchronize()
+    assert np.array_equal(got, dirc.cpu().numpy())
+    rows = np.sort(np.random.default_rng(2).choice(N, size=64, replace=False))
+    sel = np.flatnonzero(np.isin(inp.receivers[stored], rows) | np.isin(inp.senders[stored], rows))
+    ref = variants.forward_pairs(lay_of(w), inp.x, y_p[sel], s_p[sel], inp.senders[stored][sel],
+                                 inp.receivers[stored][sel], N)
+    err = rel_err(got[rows], ref[rows])
+    say(f"  sampled rows max|err|/RMS {err:.3e}")
+    assert err <= TOL

@@ -336,12 +336,16 @@ def test_pair_layout_of_radius_graphs(cluster):
     src, dst = synth.radius_graph(pos, 1.0)
     N, Ec = len(pos), len(src)
     row_ptr = np.searchsorted(dst, np.arange(N + 1)).astype(np.int32)
-    stored, pair_of = E.e3conv_pair_layout(row_ptr, src, N, Ec, cluster)
+    stored, pmap = E.e3conv_pair_layout(row_ptr, src, N, Ec, cluster)
+    pair_of = np.where(pmap >= 0, pmap, ~pmap)
     assert len(stored) * 2 == Ec
     assert np.array_equal(np.bincount(pair_of, minlength=len(stored)), np.full(len(stored), 2))
-    assert np.array_equal(pair_of[stored], np.arange(len(stored)))
+    assert np.array_equal(pmap[stored], np.arange(len(stored)))      # stored edges: non-negative
+    assert np.count_nonzero(pmap < 0) == len(stored)                # their reverses: ~pair
     lo, hi = np.minimum(src, dst), np.maximum(src, dst)
     assert np.array_equal(lo[stored][pair_of], lo) and np.array_equal(hi[stored][pair_of], hi)
+    rev = pmap < 0
+    assert np.array_equal(src[rev], dst[stored][pair_of[rev]])      # a reverse runs the other way
     order = E.e3conv_receiver_order(row_ptr, src, N, Ec, cluster)
     rank = np.empty(N, np.int64)
     rank[order] = np.arange(N)
@@ -386,3 +390,17 @@ def test_forward_linear_argument_errors(lib):
     plan2 = E.Plan(w2.irreps_in, w2.lmax, w2.irreps_out, w2.avg_num_neighbors)
     h2 = plan2.handle
     assert lib.e3conv_forward_linear(h2, 0, f, f, f, f, f, None, 4, 4, 1.0, f, f, None) == 3
+
+
+def test_forward_pairs_argument_errors(lib):
+    f = ctypes.c_void_p(0x1000)
+    n = ctypes.c_void_p(0)
+    w = synth.WORKLOADS[2]
+    plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    splan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors, ordering=E.E3CONV_SENDER)
+    h = plan.handle
+    assert lib.e3conv_forward_pairs(None, f, f, f, f, f, f, None, 4, 4, 2, f, None) == 1
+    assert lib.e3conv_forward_pairs(h, f, f, f, f, f, f, None, 4, 4, 5, f, None) == 1     # pairs > edges
+    assert lib.e3conv_forward_pairs(h, f, f, f, f, f, n, None, 4, 4, 2, f, None) == 1     # null map
+    assert lib.e3conv_forward_pairs(h, n, n, n, n, n, n, None, 0, 0, 0, n, None) == 0     # no-op
+    assert lib.e3conv_forward_pairs(splan.handle, f, f, f, f, f, f, None, 4, 4, 2, f, None) == 3
