@@ -449,6 +449,19 @@ def main():
     wall = time.perf_counter() - t1
 
     ms_per_step = wall / args.steps * 1e3
+    graph_ms = None
+    if w.backward and not args.no_extra:
+        # the same step captured once in a HIP graph and replayed (no launch gaps)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(False)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(False)
+        graph_ms = _timed(graph.replay, args.steps, args.warmup)
+        del graph
     fwd_times = [a.elapsed_time(b) for a, b in fwd_ev]
     fwd_ms = float(np.mean(fwd_times))
     b_in = 2 if w.dtype == "bf16" else 4
@@ -484,6 +497,9 @@ def main():
         "variants": [args.fwd_variant, args.bwd_variant],
         "fwd_ms_stats": time_stats(fwd_times),
     }
+    if graph_ms is not None:
+        res["graph_step_ms"] = graph_ms
+        res["graph_step_hbm_frac"] = (fwd_bytes + bwd_bytes) / (graph_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS
     if N * w.num_out * w.channels * 4 < (64 << 20):
         # small problems fit the 256 MB MALL: also report cold-cache forwards
         res["fwd_ms_cold"] = cold_forward_ms(lambda: plan.forward(x, y, s, src, row_ptr, out=out,
