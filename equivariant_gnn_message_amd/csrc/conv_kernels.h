@@ -474,9 +474,9 @@ __device__ __forceinline__ void lin_rows(const float* w, const float* row, const
   for (int o = 0; o < NO; ++o) store_row<VL>(orow + (size_t)o * C, res[o], prm.lin_alpha);
 }
 
-// Fused output linear (the step after the convolution: each output irrep
-// block mixed over its channels by a C x C weight matrix, scaled by
-// scale / sqrt(C)).  The receiver's summed row goes through the wave's LDS
+// Fused output linear (the step after the convolution, cuEquivariance page,
+// Flax NNX layers, IrrepsLinear: each output irrep block mixed over its
+// channels by a C x C weight matrix, scaled by scale / sqrt(C)).  The receiver's summed row goes through the wave's LDS
 // row; then the GPR * LPG lanes of the receiver each produce C / (GPR * LPG)
 // output channels of every component,
 //   out[b, o, v] = lin_alpha * sum_u row[o, u] W_k(o)[u, v]
@@ -599,9 +599,10 @@ __device__ __forceinline__ void load_edge(EdgeBuf<LY, IN, CPL>& buf, const IN* _
   for (int i = 0; i < NX; ++i) load_raw<IN, CPL, false>(xrow + i * C, buf.x[i]);
 }
 
-// Pair-stored edge data (PR): the edge's y and s rows are its pair's, read at
-// row |p| of the pair arrays, with the odd-l blocks of y negated when the
-// edge is the reverse of the stored one (p < 0: ~p is the pair).
+// Pair-stored edge data (PR; the symmetry of the e3j Convolution page's note
+// on SENDER ordering): the edge's y and s rows are its pair's, read at row
+// |p| of the pair arrays, with the odd-l blocks of y negated when the edge is
+// the reverse of the stored one (p < 0: ~p is the pair).
 template <class LY, typename IN, int CPL>
 __device__ __forceinline__ void load_edge_pair(EdgeBuf<LY, IN, CPL>& buf, const IN* __restrict__ x,
                                                const IN* __restrict__ y, const IN* __restrict__ s,
@@ -1747,7 +1748,8 @@ __global__ void __launch_bounds__(256) conv_bwd_tile(BwdParams prm) {
 // ------------------------------------------------ pair-stored backward ------
 //
 // On a graph that holds b -> a whenever it holds a -> b, with edge features
-// y_ba = P y_ab (P: (-1)^l on each l block) and scalars s_ba = s_ab, one row
+// y_ba = P y_ab (P: (-1)^l on each l block) and scalars s_ba = s_ab (the
+// assumptions of the e3j Convolution page's note on SENDER ordering), one row
 // of y and s per undirected pair suffices: a stored edge e = (a -> b) stands
 // for itself and for its reverse (b -> a), whose per-path matrix is
 // (-1)^l2 K^p(y[e]).  One pass over the stored edges takes both directions,
