@@ -327,6 +327,37 @@ def cpu_baseline(inp, with_backward, workers):
     return base, res
 
 
+def oracle_forward_threads(inp, threads):
+    """The oracle's forward over the whole workload: receiver-aligned ranges run on a thread
+    pool (numpy releases the interpreter lock in its array loops); bf16 operands decoded per
+    range.  Returns (out fp64, seconds)."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+
+    from oracle import conv
+    from equivariant_gnn_message_amd import synth
+    w = inp.workload
+    lay = conv.make_layout(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    N = inp.num_nodes
+    ptr = np.searchsorted(inp.receivers, np.arange(N + 1))
+    x = inp.as_f32("x")
+    dec = (lambda a: synth.bf16_to_f32(a).reshape(a.shape)) if w.dtype == "bf16" else (lambda a: a)
+    out = np.empty((N, w.num_out, w.channels))
+    parts = max(1, 8 * threads)
+
+    def run(k):
+        b0, b1 = N * k // parts, N * (k + 1) // parts
+        e0, e1 = int(ptr[b0]), int(ptr[b1])
+        out[b0:b1] = conv.forward(lay, x, dec(inp.y[e0:e1]), dec(inp.s[e0:e1]), inp.senders[e0:e1],
+                                  inp.receivers[e0:e1] - b0, b1 - b0)
+
+    t0 = time.perf_counter()
+    with threadpool_limits(1), ThreadPoolExecutor(threads) as ex:
+        list(ex.map(run, range(parts)))
+    return out, time.perf_counter() - t0
+
+
 def parity_full(got, ref):
     """max|got - ref| / RMS(ref) over whole tensors (chunked to bound host memory)."""
     import numpy as np
@@ -537,11 +568,11 @@ def main():
         res["w2_forward"] = forward_block(plan, w, fwd_times, fwd_bytes, N, Ecount)
         del x, y, s, g, grads, out, order, order_dev, src, dst, row_ptr
         torch.cuda.empty_cache()
-        res["w3_forward"] = bench_forward_workload(3, args)
+        res["w3_forward"] = bench_forward_workload(3, args, parity=not args.no_cpu_baseline)
         res["pairs_reverse"] = pairs_block(plan, w, inp, res["fwd_ms"], res["bwd_ms"], args)
         # the small configurations' forwards (latency-bound: far from either roof)
-        res["w0_forward"] = bench_forward_workload(0, args)
-        res["w1_forward"] = bench_forward_workload(1, args)
+        res["w0_forward"] = bench_forward_workload(0, args, parity=not args.no_cpu_baseline)
+        res["w1_forward"] = bench_forward_workload(1, args, parity=not args.no_cpu_baseline)
         res["bar_60pct_hbm"] = {
             "w2_forward": res["w2_forward"]["hbm_frac"] >= 0.6,
             "w3_forward": res["w3_forward"]["hbm_frac"] >= 0.6,
@@ -573,7 +604,7 @@ def forward_block(plan, w, times, nbytes, N, Ecount):
             "bound": "alu" if flops / PEAK_FP32_VALU_TFLOPS / 1e12 > nbytes / PEAK_HBM_GBPS / 1e9 else "hbm"}
 
 
-def bench_forward_workload(idx, args):
+def bench_forward_workload(idx, args, parity=False):
     """Forward of workload idx (full size, default kernel, clustered receiver order), timed
     per call with HIP events on the launch stream."""
     import numpy as np
@@ -597,7 +628,8 @@ def bench_forward_workload(idx, args):
     row_ptr = E.e3conv_csr_from_receivers(t(inp.receivers), N)
     order = torch.from_numpy(E.e3conv_receiver_order(row_ptr.cpu().numpy(), inp.senders, N, Ec,
                                                      args.cluster)).cuda()
-    del inp
+    if not parity:
+        del inp
     plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
     out = torch.empty((N, w.num_out, w.channels), dtype=torch.float32, device="cuda")
     for _ in range(args.warmup):
@@ -613,8 +645,21 @@ def bench_forward_workload(idx, args):
     torch.cuda.synchronize()
     times = [a.elapsed_time(b) for a, b in ev]
     blk = forward_block(plan, w, times, alg_bytes(w, N, Ec, b_in)[0], N, Ec)
-    del x, y, s, src, row_ptr, order, out
-    torch.cuda.empty_cache()
+    if parity:
+        # every output element against the oracle (fp64, over the host cores)
+        got = out.cpu().numpy()
+        del x, y, s, src, row_ptr, order, out
+        torch.cuda.empty_cache()
+        threads = host_cores()
+        ref, secs = oracle_forward_threads(inp, threads)
+        err = parity_full(got, ref)
+        tol = 2e-2 if w.dtype == "bf16" else 1e-5
+        blk["parity_full"] = {"max_abs_err_over_rms": err, "tolerance": tol, "pass": err <= tol,
+                              "oracle_s": secs, "oracle_threads": threads}
+        del got, ref
+    else:
+        del x, y, s, src, row_ptr, order, out
+        torch.cuda.empty_cache()
     return blk
 
 
