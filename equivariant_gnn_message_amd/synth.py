@@ -145,15 +145,20 @@ def normal_bf16(workload, tensor_id, shape):
 # ------------------------------------------------------ spherical harmonics ---
 
 def spherical_harmonics(lmax, vec):
-    """Real spherical harmonics l = 0..lmax (lmax <= 3) of the directions ``vec``.
+    """Real spherical harmonics l = 0..lmax of the directions ``vec``.
 
     Component normalisation (|Y^l(v)|^2 = 2l+1), m = -l..l, z polar axis, so
     l=1 is sqrt(3) (y, z, x).  Textbook closed forms of the orthonormal real
-    harmonics times sqrt(4 pi).  Vectors are normalised first.  Returns
-    (n, (lmax+1)^2) float64.
+    harmonics times sqrt(4 pi) for l <= 3; the associated Legendre recursion
+    (``sh_by_recursion``) from l = 4 on.  Vectors are normalised first.
+    Returns (n, (lmax+1)^2) float64.
     """
-    if not 0 <= lmax <= 3:
-        raise ValueError("closed forms cover lmax <= 3")
+    if lmax < 0:
+        raise ValueError("lmax must be non-negative")
+    if lmax > 3:
+        low = spherical_harmonics(3, vec)
+        high = sh_by_recursion(lmax, vec)[..., 16:]
+        return np.concatenate([low, high], axis=-1)
     v = np.asarray(vec, dtype=np.float64)
     v = v / np.linalg.norm(v, axis=-1, keepdims=True)
     x, y, z = v[..., 0], v[..., 1], v[..., 2]
@@ -174,6 +179,38 @@ def spherical_harmonics(lmax, vec):
                  d * (5 * z ** 3 - 3 * z), c * x * (5 * z * z - 1),
                  b / 2 * (x * x - y * y) * z, a * (x * x - 3 * y * y) * x]
     return np.stack(cols, axis=-1)
+
+
+def sh_by_recursion(lmax, vec):
+    """The same harmonics for any lmax from the associated Legendre recursion.
+
+    Y_l^m = sqrt(2l+1) sqrt((l-|m|)! / (l+|m|)!) Q_l^|m|(z) A_m(x, y), with
+    Q_l^m the polynomial part of P_l^m (no Condon-Shortley phase):
+    Q_m^m = (2m-1)!!, Q_{m+1}^m = (2m+1) z Q_m^m,
+    (l-m) Q_l^m = (2l-1) z Q_{l-1}^m - (l+m-1) Q_{l-2}^m;
+    and A_0 = 1, A_m = sqrt(2) Re (x + i y)^m, A_-m = sqrt(2) Im (x + i y)^m.
+    """
+    v = np.asarray(vec, dtype=np.float64)
+    v = v / np.linalg.norm(v, axis=-1, keepdims=True)
+    x, y, z = v[..., 0], v[..., 1], v[..., 2]
+    w = x + 1j * y
+    out = np.empty(v.shape[:-1] + ((lmax + 1) ** 2,))
+    for m in range(lmax + 1):
+        q_prev = None
+        q = np.full(z.shape, float(np.prod(np.arange(2 * m - 1, 0, -2, dtype=np.float64))))
+        a = w ** m
+        for l in range(m, lmax + 1):
+            if l == m + 1:
+                q_prev, q = q, (2 * m + 1) * z * q
+            elif l > m + 1:
+                q_prev, q = q, ((2 * l - 1) * z * q - (l + m - 1) * q_prev) / (l - m)
+            norm = math.sqrt((2 * l + 1) * math.factorial(l - m) / math.factorial(l + m))
+            if m == 0:
+                out[..., l * l + l] = norm * q
+            else:
+                out[..., l * l + l + m] = math.sqrt(2.0) * norm * q * a.real
+                out[..., l * l + l - m] = math.sqrt(2.0) * norm * q * a.imag
+    return out
 
 
 # ------------------------------------------------------------------ graphs ---

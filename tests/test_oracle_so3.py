@@ -222,6 +222,46 @@ def test_sh_equivariant_under_oracle_D():
             np.testing.assert_allclose(YR[:, sl], Y[:, sl] @ so3.wigner_D(l, axis, ang).T, atol=1e-12)
 
 
+def test_sh_recursion_equals_closed_forms():
+    """The associated-Legendre recursion reproduces the hand-written l <= 3 forms."""
+    v = np.random.default_rng(6).standard_normal((40, 3))
+    np.testing.assert_allclose(synth.sh_by_recursion(3, v), synth.spherical_harmonics(3, v), atol=1e-14)
+
+
+@pytest.mark.parametrize("lmax", [6, 8])
+def test_sh_high_l_addition_parity_norm(lmax):
+    """Up to l = 8: the addition theorem against scipy's Legendre polynomials, parity
+    (-1)^l under v -> -v, and the component norm 2l+1."""
+    rng = np.random.default_rng(lmax)
+    u = rng.standard_normal((60, 3))
+    v = rng.standard_normal((60, 3))
+    Yu = synth.spherical_harmonics(lmax, u)
+    Yv = synth.spherical_harmonics(lmax, v)
+    Ym = synth.spherical_harmonics(lmax, -v)
+    assert Yu.shape == (60, (lmax + 1) ** 2)
+    cos = np.sum(u * v, 1) / np.linalg.norm(u, axis=1) / np.linalg.norm(v, axis=1)
+    for l in range(lmax + 1):
+        sl = slice(l * l, (l + 1) ** 2)
+        np.testing.assert_allclose(np.sum(Yu[:, sl] * Yv[:, sl], 1), (2 * l + 1) * eval_legendre(l, cos),
+                                   atol=1e-10)
+        np.testing.assert_allclose(Ym[:, sl], (-1) ** l * Yv[:, sl], atol=1e-12)
+        np.testing.assert_allclose(np.sum(Yv[:, sl] ** 2, 1), 2 * l + 1, atol=1e-10)
+
+
+def test_sh_high_l_equivariant_under_oracle_D():
+    """Y(R v) = D(R) Y(v) for l = 4..6 with the oracle's Wigner D (the basis and the m
+    order of the recursion agree with the oracle's real basis)."""
+    rng = np.random.default_rng(9)
+    v = rng.standard_normal((8, 3))
+    axis, ang = random_rotation(rng)
+    R = so3.rotation_matrix(axis, ang)
+    Y = synth.spherical_harmonics(6, v)
+    YR = synth.spherical_harmonics(6, v @ R.T)
+    for l in range(4, 7):
+        sl = slice(l * l, (l + 1) ** 2)
+        np.testing.assert_allclose(YR[:, sl], Y[:, sl] @ so3.wigner_D(l, axis, ang).T, atol=1e-10)
+
+
 def test_sh_shapes():
     v = np.ones((2, 3))
     Y = synth.spherical_harmonics(2, v)
