@@ -568,7 +568,9 @@ def main():
         res["w2_forward"] = forward_block(plan, w, fwd_times, fwd_bytes, N, Ecount)
         del x, y, s, g, grads, out, order, order_dev, src, dst, row_ptr
         torch.cuda.empty_cache()
-        res["w3_forward"] = bench_forward_workload(3, args, parity=not args.no_cpu_baseline)
+        # beside the default kernel: the matrix-core form (bf16 operands, variant 6)
+        res["w3_forward"] = bench_forward_workload(3, args, parity=not args.no_cpu_baseline,
+                                                   variants=((6, "matrix_core_variant"),))
         res["pairs_reverse"] = pairs_block(plan, w, inp, res["fwd_ms"], res["bwd_ms"], args)
         # the small configurations' forwards (latency-bound: far from either roof)
         res["w0_forward"] = bench_forward_workload(0, args, parity=not args.no_cpu_baseline)
@@ -604,9 +606,11 @@ def forward_block(plan, w, times, nbytes, N, Ecount):
             "bound": "alu" if flops / PEAK_FP32_VALU_TFLOPS / 1e12 > nbytes / PEAK_HBM_GBPS / 1e9 else "hbm"}
 
 
-def bench_forward_workload(idx, args, parity=False):
+def bench_forward_workload(idx, args, parity=False, variants=()):
     """Forward of workload idx (full size, default kernel, clustered receiver order), timed
-    per call with HIP events on the launch stream."""
+    per call with HIP events on the launch stream.  variants: (index, key) pairs of other
+    forward variants timed the same way, each reported under its key with its own parity
+    against the same oracle output."""
     import numpy as np
     import torch
 
@@ -632,31 +636,50 @@ def bench_forward_workload(idx, args, parity=False):
         del inp
     plan = E.Plan(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
     out = torch.empty((N, w.num_out, w.channels), dtype=torch.float32, device="cuda")
-    for _ in range(args.warmup):
-        plan.forward(x, y, s, src, row_ptr, out=out, order=order)
-    torch.cuda.synchronize()
-    ev = []
-    for _ in range(args.steps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        plan.forward(x, y, s, src, row_ptr, out=out, order=order)
-        b.record()
-        ev.append((a, b))
-    torch.cuda.synchronize()
-    times = [a.elapsed_time(b) for a, b in ev]
-    blk = forward_block(plan, w, times, alg_bytes(w, N, Ec, b_in)[0], N, Ec)
+
+    def timed():
+        for _ in range(args.warmup):
+            plan.forward(x, y, s, src, row_ptr, out=out, order=order)
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(args.steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            plan.forward(x, y, s, src, row_ptr, out=out, order=order)
+            b.record()
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    nbytes = alg_bytes(w, N, Ec, b_in)[0]
+    blk = forward_block(plan, w, timed(), nbytes, N, Ec)
+    outs = {None: out.cpu().numpy()} if parity else {}
+    nf, _ = plan.num_variants(E.E3CONV_BF16 if w.dtype == "bf16" else E.E3CONV_F32)
+    for v, key in variants:
+        if v >= nf:
+            continue
+        plan.set_variant(v, 0)
+        blk[key] = forward_block(plan, w, timed(), nbytes, N, Ec)
+        blk[key]["variant"] = v
+        if parity:
+            outs[key] = out.cpu().numpy()
+    plan.set_variant(0, 0)
     if parity:
         # every output element against the oracle (fp64, over the host cores)
-        got = out.cpu().numpy()
         del x, y, s, src, row_ptr, order, out
         torch.cuda.empty_cache()
         threads = host_cores()
         ref, secs = oracle_forward_threads(inp, threads)
-        err = parity_full(got, ref)
         tol = 2e-2 if w.dtype == "bf16" else 1e-5
-        blk["parity_full"] = {"max_abs_err_over_rms": err, "tolerance": tol, "pass": err <= tol,
-                              "oracle_s": secs, "oracle_threads": threads}
-        del got, ref
+        for key, got in outs.items():
+            err = parity_full(got, ref)
+            par = {"max_abs_err_over_rms": err, "tolerance": tol, "pass": err <= tol}
+            if key is None:
+                par.update(oracle_s=secs, oracle_threads=threads)
+                blk["parity_full"] = par
+            else:
+                blk[key]["parity_full"] = par
+        del outs, ref
     else:
         del x, y, s, src, row_ptr, order, out
         torch.cuda.empty_cache()

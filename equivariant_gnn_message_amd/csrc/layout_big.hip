@@ -1,5 +1,6 @@
 // Kernels of the layout 64x(0e+1o+2e), lmax 3 -> 64x(0e+1o+2e+3o).
 #include "conv_kernels.h"
+#include "conv_mfma.h"
 
 namespace e3c {
 namespace {
@@ -15,7 +16,8 @@ constexpr CGValues<L::NNZ> kCG = L::CG;
 const FwdLauncher kF32[] = {launch_fwd_pipe<L, float, 2, 2>, launch_fwd<L, float, 4, 4>, launch_fwd_pipe<L, float, 4, 4>};
 const FwdLauncher kBF16[] = {launch_fwd_pipe<L, bf16_bits, 2, 2, true>, launch_fwd<L, bf16_bits, 4, 4>,
                              launch_fwd_pipe<L, bf16_bits, 4, 4>, launch_fwd_pipe<L, bf16_bits, 4, 2>,
-                             launch_fwd_pipe<L, bf16_bits, 2, 1>, launch_fwd_pipe<L, bf16_bits, 2, 2>};
+                             launch_fwd_pipe<L, bf16_bits, 2, 1>, launch_fwd_pipe<L, bf16_bits, 2, 2>,
+                             launch_fwd_mfma<L, false>, launch_fwd_mfma<L, true>};
 const BwdLauncher kBwd[] = {launch_bwd<L, 2, 2>, launch_bwd_pipe<L, 2, 2>};
 
 const FwdLauncher kSenderF32[] = {launch_fwd_pipe<LS, float, 2, 2>};

@@ -9,6 +9,12 @@ kernel that rounded any intermediate (K, a product, a partial sum) to bf16
 (2^-9) would be off by ~1e-2 RMS and fail it.  Every compiled bf16 variant of
 the layout runs, in both graph orderings, with padding receivers and with
 receivers that have no edges.
+
+The exception is the matrix-core form (RECEIVER variants 6 and 7): its
+operands are bf16 by design (u = s x rounded once; K rounded once, or split
+into two bf16 parts in variant 7), so it is held to the 2e-2 bar of bf16
+storage, and to at least 2e-3 (it must show the rounding it is built on, so
+that a silent fall back to the fp32 arithmetic would be noticed).
 """
 
 import numpy as np
@@ -23,6 +29,9 @@ from ._gpu import rel_err, say
 pytestmark = pytest.mark.gpu
 
 TIGHT = 2e-4
+BF16_BAR = 2e-2
+MATRIX_CORE = (6, 7)        # RECEIVER bf16 variants of this layout on the matrix cores
+N_RECEIVER_BF16 = 8         # variants compiled for the layout (a change of the list fails here)
 
 
 def lay_of(w):
@@ -46,6 +55,9 @@ def run_all_variants(plan, x, y, s, src, row_ptr, ref, label, **kw):
     import torch
     nf, _ = plan.num_variants(E.E3CONV_BF16)
     assert nf >= 1
+    receiver = plan.ordering == E.E3CONV_RECEIVER
+    if receiver:
+        assert nf == N_RECEIVER_BF16, nf
     outs = []
     for v in range(nf):
         plan.set_variant(v, 0)
@@ -54,7 +66,12 @@ def run_all_variants(plan, x, y, s, src, row_ptr, ref, label, **kw):
         torch.cuda.synchronize()
         err = rel_err(out.cpu().numpy(), ref)
         say(f"  max|err|/RMS = {err:.3e}")
-        assert err <= TIGHT, (v, err)
+        if receiver and v in MATRIX_CORE:
+            assert err <= BF16_BAR, (v, err)
+            if np.abs(ref).max() > 0:
+                assert err >= 2e-3, (v, err)
+        else:
+            assert err <= TIGHT, (v, err)
         outs.append(out)
     plan.set_variant(0, 0)
     return outs
