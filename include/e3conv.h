@@ -477,8 +477,14 @@ e3conv_status e3conv_validate_graph_noalloc(const int32_t* src, const int32_t* r
 e3conv_status e3conv_stream_reference(const void* src, void* dst, size_t bytes, void* hip_stream);
 
 /* Tuning: select a kernel variant for this plan (0 = default).  Variants
- * differ only in how lanes map to channels and edges; all compute the same
- * result.  Returns E3CONV_ERR_UNSUPPORTED for an unknown variant.  Plans are
+ * differ in how lanes map to channels and edges and compute the same result
+ * to fp32 rounding, with one exception: for 64x(0e+1o+2e), SH lmax 3 ->
+ * 64x(0e+1o+2e+3o) with bf16 operands, RECEIVER forward variants 6 and 7 run
+ * the product on bf16 matrix instructions and round s x (and K, the edge's CG
+ * matrix from y; variant 7 keeps K as two bf16 parts) to bf16, an error of at
+ * most about 2^-7 of sum |C||y||s||x| per output element.  A variant index
+ * beyond the list of an ordering or dtype selects its default.  Returns
+ * E3CONV_ERR_UNSUPPORTED for a variant beyond every list.  Plans are
  * otherwise immutable; set variants before sharing a plan across threads. */
 e3conv_status e3conv_plan_set_variant(e3conv_plan_t plan, int forward_variant, int backward_variant);
 
