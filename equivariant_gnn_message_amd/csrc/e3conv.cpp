@@ -672,6 +672,33 @@ e3conv_status e3conv_receiver_order(const int32_t* row_ptr, const int32_t* src, 
   return ok();
 }
 
+e3conv_status e3conv_relabel_nodes(const int32_t* row_ptr, const int32_t* src, int64_t N, int64_t E,
+                                   int cluster, int32_t* node_new, int32_t* edge_perm) {
+  if (N < 0 || E < 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "negative size");
+  if (E >= (int64_t)1 << 31 || N >= ((int64_t)1 << 31) - 1)
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "sizes must fit int32 indices");
+  if (cluster <= 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "cluster must be positive");
+  if (N == 0) return E == 0 ? ok() : fail(E3CONV_ERR_GRAPH, "edges without nodes");
+  if (!row_ptr || !node_new || (E > 0 && (!src || !edge_perm)))
+    return fail(E3CONV_ERR_INVALID_ARGUMENT, "NULL pointer");
+  const e3conv_status st = e3conv_validate_graph(src, row_ptr, N, E, 0);
+  if (st != E3CONV_OK) return st;
+  std::vector<int> order((size_t)N);
+  e3c::receiver_order(row_ptr, src, (int)N, cluster, order.data());
+  for (int i = 0; i < (int)N; ++i) node_new[order[i]] = i;
+  // new receiver b' = node_new[b] takes the edges of old receiver order[b'], in
+  // new-receiver order; within one receiver, stable by new sender
+  int64_t k = 0;
+  for (int nb = 0; nb < (int)N; ++nb) {
+    const int b = order[nb];
+    const int64_t k0 = k;
+    for (int e = row_ptr[b]; e < row_ptr[b + 1]; ++e) edge_perm[k++] = e;
+    std::stable_sort(edge_perm + k0, edge_perm + k,
+                     [&](int32_t a, int32_t c) { return node_new[src[a]] < node_new[src[c]]; });
+  }
+  return ok();
+}
+
 e3conv_status e3conv_pair_layout(const int32_t* row_ptr, const int32_t* src, int64_t N, int64_t E,
                                  int cluster, int32_t* stored, int32_t* pair_of) {
   if (N < 0 || E < 0) return fail(E3CONV_ERR_INVALID_ARGUMENT, "negative size");

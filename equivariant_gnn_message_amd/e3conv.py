@@ -41,6 +41,7 @@ EXPORTED = [
     "e3conv_linear", "e3conv_linear_backward", "e3conv_csr_from_receivers",
     "e3conv_validate_graph", "e3conv_validate_graph_async", "e3conv_validate_graph_noalloc",
     "e3conv_receiver_order",
+    "e3conv_relabel_nodes",
     "e3conv_stream_reference", "e3conv_second_derivatives", "e3conv_backward_pairs", "e3conv_pair_layout", "e3conv_forward_linear", "e3conv_forward_pairs",
     "e3conv_plan_set_variant",
     "e3conv_plan_num_variants",
@@ -102,6 +103,7 @@ def load_library(path=LIB_PATH):
         "e3conv_backward_ex": ([P, ctypes.c_int, P, P, P, P, P, P, I64, I64, I64, P, P, P, P,
                                 ctypes.c_uint, P, ctypes.c_size_t, P], ctypes.c_int),
         "e3conv_receiver_order": ([P, P, I64, I64, ctypes.c_int, P], ctypes.c_int),
+        "e3conv_relabel_nodes": ([P, P, I64, I64, ctypes.c_int, P, P], ctypes.c_int),
         "e3conv_linear": ([P, ctypes.c_int, ctypes.c_float, P, P, I64, P, P], ctypes.c_int),
         "e3conv_linear_backward": ([P, ctypes.c_int, ctypes.c_float, P, P, I64, P, P, P, P],
                                    ctypes.c_int),
@@ -442,6 +444,20 @@ def e3conv_receiver_order(row_ptr, src, num_nodes, num_edges, cluster=512):
                                                 int(num_nodes), int(num_edges), int(cluster),
                                                 order.ctypes.data_as(P)))
     return order
+
+
+def e3conv_relabel_nodes(row_ptr, src, num_nodes, num_edges, cluster=512):
+    """Host-side node relabeling in receiver-cluster order: (node_new, edge_perm) as numpy
+    int32 (new id of each old node; old index of each edge of the relabeled graph)."""
+    import numpy as np
+    r = np.ascontiguousarray(np.asarray(row_ptr), dtype=np.int32)
+    s = np.ascontiguousarray(np.asarray(src), dtype=np.int32)
+    node_new = np.empty(int(num_nodes), dtype=np.int32)
+    edge_perm = np.empty(int(num_edges), dtype=np.int32)
+    _check(load_library().e3conv_relabel_nodes(r.ctypes.data_as(P), s.ctypes.data_as(P),
+                                               int(num_nodes), int(num_edges), int(cluster),
+                                               node_new.ctypes.data_as(P), edge_perm.ctypes.data_as(P)))
+    return node_new, edge_perm
 
 
 def e3conv_pair_layout(row_ptr, src, num_nodes, num_edges, cluster=512):

@@ -385,6 +385,26 @@ e3conv_status e3conv_csr_from_receivers(const int32_t* receivers_sorted, int64_t
 e3conv_status e3conv_receiver_order(const int32_t* row_ptr, const int32_t* src, int64_t num_nodes,
                                     int64_t num_edges, int cluster, int32_t* order);
 
+/* Node relabeling for locality (host only; once per graph).  The convolution
+ * commutes with renaming the nodes (the page's formula sums over the edges into
+ * each receiver, whatever the node ids): relabeled inputs give the relabeled
+ * output.  This call renames node v to its rank in the order
+ * e3conv_receiver_order(cluster) gives, so that index order is that processing
+ * order: consecutive receivers share senders and their rows of s, y and out
+ * sit next to each other in memory.  Outputs (host, caller-owned):
+ *   node_new[num_nodes]  new id of old node v (a permutation);
+ *   edge_perm[num_edges] old index of the k-th edge of the relabeled graph,
+ *                        whose edges are sorted by new receiver, then by new
+ *                        sender, then by old index.
+ * The relabeled graph is src'[k] = node_new[src[edge_perm[k]]], dst'[k] =
+ * node_new[dst[edge_perm[k]]]; its edge rows are y[edge_perm[k]] and
+ * s[edge_perm[k]]; node rows move as x'[node_new[v]] = x[v], and the output
+ * comes back as out[v] = out'[node_new[v]].  Validates the graph first
+ * (E3CONV_ERR_GRAPH); cluster > 0. */
+e3conv_status e3conv_relabel_nodes(const int32_t* row_ptr, const int32_t* src, int64_t num_nodes,
+                                   int64_t num_edges, int cluster, int32_t* node_new,
+                                   int32_t* edge_perm);
+
 /* Forward of pair-stored edge data: the function whose reverse pass is
  * e3conv_backward_pairs (e3j Convolution page, the note on SENDER ordering:
  * symmetric graph, y_ba = (-1)^l y_ab, s_ba = s_ab).  The messages are summed

@@ -245,6 +245,48 @@ def test_receiver_order_clusters_are_connected():
         assert np.any(pos[nbrs] < pos[v])    # the radius graph is symmetric
 
 
+@pytest.mark.parametrize("cluster", [1, 64, 512])
+def test_relabel_nodes(cluster):
+    """Node ids renamed to their rank in the receiver order; the relabeled edges are the
+    same directed edges, sorted by new receiver then new sender; and the oracle's
+    output of the relabeled graph is the relabeled output (the sum does not see ids)."""
+    from oracle import conv
+    inp = synth.make_inputs(0)
+    N, Ec = inp.num_nodes, inp.num_edges
+    row_ptr = np.searchsorted(inp.receivers, np.arange(N + 1)).astype(np.int32)
+    node_new, edge_perm = E.e3conv_relabel_nodes(row_ptr, inp.senders, N, Ec, cluster)
+    order = E.e3conv_receiver_order(row_ptr, inp.senders, N, Ec, cluster)
+    assert np.array_equal(node_new[order], np.arange(N))
+    assert np.array_equal(np.sort(edge_perm), np.arange(Ec))
+    s2, d2 = node_new[inp.senders[edge_perm]], node_new[inp.receivers[edge_perm]]
+    key = d2.astype(np.int64) * N + s2
+    assert np.all(np.diff(key) >= 0)
+    old = np.sort(node_new[inp.receivers].astype(np.int64) * N + node_new[inp.senders])
+    assert np.array_equal(np.sort(key), old)
+    w = inp.workload
+    lay = conv.make_layout(w.irreps_in, w.lmax, w.irreps_out, w.avg_num_neighbors)
+    x, y, s = inp.as_f32("x"), inp.as_f32("y"), inp.as_f32("s")
+    ref = conv.forward(lay, x, y, s, inp.senders, inp.receivers, N)
+    x2 = np.empty_like(x)
+    x2[node_new] = x
+    got = conv.forward(lay, x2, y[edge_perm], s[edge_perm], s2, d2, N)
+    np.testing.assert_allclose(got[node_new], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_relabel_nodes_edge_cases():
+    node_new, edge_perm = E.e3conv_relabel_nodes(np.zeros(4, np.int32), np.zeros(0, np.int32), 3, 0, 8)
+    assert np.array_equal(np.sort(node_new), np.arange(3)) and len(edge_perm) == 0
+    with pytest.raises(E.E3ConvError) as ei:
+        E.e3conv_relabel_nodes(np.array([0, 2, 1], np.int32), np.array([0, 1], np.int32), 2, 2, 8)
+    assert ei.value.status == 5
+    with pytest.raises(E.E3ConvError) as ei:
+        E.e3conv_relabel_nodes(np.array([0, 1], np.int32), np.array([0], np.int32), 1, 1, 0)
+    assert ei.value.status == 1
+    with pytest.raises(E.E3ConvError) as ei:
+        E.e3conv_relabel_nodes(np.array([0, 1], np.int32), np.array([3], np.int32), 1, 1, 8)
+    assert ei.value.status == 5
+
+
 def test_ordered_plans(lib):
     w = synth.WORKLOADS[2]
     h = ctypes.c_void_p()
