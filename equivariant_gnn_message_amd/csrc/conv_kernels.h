@@ -180,19 +180,104 @@ __device__ __forceinline__ void load_row(const IN* p, float (&v)[N]) {
 
 // ----------------------------------------------------- shared edge math -----
 
-// K^p[m3][m1] = sum_m2 C^p[m1,m2,m3] y[o2+m2] over the compile-time pattern.
+// Entries of one path's K^p that are equal up to sign.  Within a path many
+// entries K[m3][m1] = sum_m2 C[m1,m2,m3] y[m2] have the same terms (the same
+// m2, coefficients of equal magnitude) up to one common sign; the table below
+// finds them at compile time from the coefficient values.  Each entry is
+// mapped to the first entry (in the order of the entry list) with the same
+// terms up to sign; only those representatives are computed, and the others
+// are their copies or negations, which the compiler folds into the source
+// modifiers of the instructions that use them.
+struct KRefTable {
+  int8_t rm3[kMaxNnz];   // representative of the K entry of CG entry q
+  int8_t rm1[kMaxNnz];
+  int8_t sgn[kMaxNnz];   // +1 or -1
+};
+
+// True if the K entries of CG entries qa and qb (same path) have the same
+// terms up to one common sign, returned in sgn.
+constexpr bool k_terms_match(const LayoutTables& t, const float* v, int p, int qa, int qb, int& sgn) {
+  const int a3 = t.entry[qa].m3, a1 = t.entry[qa].m1, b3 = t.entry[qb].m3, b1 = t.entry[qb].m1;
+  int na = 0, nb = 0;
+  sgn = 0;
+  for (int q = t.path[p].nnz_begin; q < t.path[p].nnz_end; ++q) {
+    if (t.entry[q].m3 == b3 && t.entry[q].m1 == b1) ++nb;
+    if (t.entry[q].m3 != a3 || t.entry[q].m1 != a1) continue;
+    ++na;
+    int r = -1;
+    for (int q2 = t.path[p].nnz_begin; q2 < t.path[p].nnz_end; ++q2)
+      if (t.entry[q2].m3 == b3 && t.entry[q2].m1 == b1 && t.entry[q2].m2 == t.entry[q].m2) r = q2;
+    if (r < 0) return false;
+    const float va = v[q], vb = v[r];
+    const float aa = va < 0.0f ? -va : va, ab = vb < 0.0f ? -vb : vb;
+    if (aa == 0.0f && ab == 0.0f) continue;
+    const float d = aa > ab ? aa - ab : ab - aa;
+    if (aa == 0.0f || ab == 0.0f || d > 1e-6f * aa) return false;
+    const int s = (va < 0.0f) != (vb < 0.0f) ? -1 : 1;
+    if (sgn == 0) sgn = s;
+    if (sgn != s) return false;
+  }
+  if (sgn == 0) sgn = 1;
+  return na == nb;
+}
+
+template <class LY>
+constexpr KRefTable make_kref() {
+  KRefTable r{};
+  const LayoutTables& t = LY::T;
+  for (int p = 0; p < t.num_paths; ++p)
+    for (int q = t.path[p].nnz_begin; q < t.path[p].nnz_end; ++q) {
+      r.rm3[q] = t.entry[q].m3;
+      r.rm1[q] = t.entry[q].m1;
+      r.sgn[q] = 1;
+      for (int q2 = t.path[p].nnz_begin; q2 < q; ++q2) {
+        if (!first_term(t, p, q2)) continue;
+        if (t.entry[q2].m3 == t.entry[q].m3 && t.entry[q2].m1 == t.entry[q].m1) break;
+        int sg = 0;
+        if (k_terms_match(t, LY::CG.v, p, q, q2, sg)) {
+          r.rm3[q] = t.entry[q2].m3;
+          r.rm1[q] = t.entry[q2].m1;
+          r.sgn[q] = (int8_t)sg;
+          break;
+        }
+      }
+    }
+  return r;
+}
+
+template <class LY>
+struct KRefs {
+  static constexpr KRefTable R = make_kref<LY>();
+};
+
+// K^p[m3][m1] = sum_m2 C^p[m1,m2,m3] y[o2+m2] over the compile-time pattern,
+// each class of entries equal up to sign computed once.
 template <class LY, int p, int D3, int D1>
 __device__ __forceinline__ void build_k(const float (&yv)[LY::NY], float (&K)[D3][D1]) {
   constexpr PathInfo P = LY::T.path[p];
   sfor<P.nnz_begin, P.nnz_end>([&](auto qc) {
     constexpr int q = decltype(qc)::value;
     constexpr Entry en = LY::T.entry[q];
-    constexpr float c = LY::CG.v[q];
-    const float yy = yv[P.o2 + en.m2];
-    if constexpr (first_term(LY::T, p, q)) {
-      K[en.m3][en.m1] = c * yy;
-    } else {
-      K[en.m3][en.m1] = __builtin_fmaf(c, yy, K[en.m3][en.m1]);
+    if constexpr (KRefs<LY>::R.rm3[q] == en.m3 && KRefs<LY>::R.rm1[q] == en.m1) {
+      constexpr float c = LY::CG.v[q];
+      const float yy = yv[P.o2 + en.m2];
+      if constexpr (first_term(LY::T, p, q)) {
+        K[en.m3][en.m1] = c * yy;
+      } else {
+        K[en.m3][en.m1] = __builtin_fmaf(c, yy, K[en.m3][en.m1]);
+      }
+    }
+  });
+  sfor<P.nnz_begin, P.nnz_end>([&](auto qc) {
+    constexpr int q = decltype(qc)::value;
+    constexpr Entry en = LY::T.entry[q];
+    constexpr int r3 = KRefs<LY>::R.rm3[q], r1 = KRefs<LY>::R.rm1[q];
+    if constexpr (first_term(LY::T, p, q) && !(r3 == en.m3 && r1 == en.m1)) {
+      if constexpr (KRefs<LY>::R.sgn[q] > 0) {
+        K[en.m3][en.m1] = K[r3][r1];
+      } else {
+        K[en.m3][en.m1] = -K[r3][r1];
+      }
     }
   });
 }
@@ -1337,33 +1422,23 @@ struct BwdBuf {
   float s[LY::NP][CPL];
 };
 
-// Q: the lane holds channels li*CPL .. li*CPL+CPL-1 (one vector access per
-// row); otherwise channels li, li+LPG, ... (one 4-byte access per channel).
-template <class LY, int CPL, int LPG, bool Q = false>
+// The lane holds channels li, li+LPG, ... (one 4-byte access per channel).
+template <class LY, int CPL, int LPG>
 __device__ __forceinline__ void load_bwd_edge(BwdBuf<LY, CPL>& buf, const float* __restrict__ x,
                                               const float* __restrict__ y,
                                               const float* __restrict__ s, int e, int a, int li) {
   constexpr int C = LY::C, NX = LY::NX, NY = LY::NY, NP = LY::NP;
   load_row<float, NY>(y + (size_t)e * NY, buf.y);
-  if constexpr (Q) {
-    const float* xrow = x + (size_t)a * NX * C + li * CPL;
+  const float* xrow = x + (size_t)a * NX * C + li;
 #pragma unroll
-    for (int i = 0; i < NX; ++i) load_ch<float, CPL, false>(xrow + i * C, buf.x[i]);
-    const float* srow = s + (size_t)e * NP * C + li * CPL;
+  for (int i = 0; i < NX; ++i)
 #pragma unroll
-    for (int p = 0; p < NP; ++p) load_ch<float, CPL, true>(srow + p * C, buf.s[p]);
-  } else {
-    const float* xrow = x + (size_t)a * NX * C + li;
+    for (int c = 0; c < CPL; ++c) buf.x[i][c] = xrow[i * C + c * LPG];
+  const float* srow = s + (size_t)e * NP * C + li;
 #pragma unroll
-    for (int i = 0; i < NX; ++i)
+  for (int p = 0; p < NP; ++p)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) buf.x[i][c] = xrow[i * C + c * LPG];
-    const float* srow = s + (size_t)e * NP * C + li;
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) buf.s[p][c] = __builtin_nontemporal_load(srow + p * C + c * LPG);
-  }
+    for (int c = 0; c < CPL; ++c) buf.s[p][c] = __builtin_nontemporal_load(srow + p * C + c * LPG);
 }
 
 
@@ -1652,6 +1727,17 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& prm, long e0, int e1, 
 
   if ((int)e0 < e_lim) {
     int e = (int)e0 + grp;
+    BwdBuf<LY, CPL> b0, b1;
+    {
+      // the first edge's y and s rows do not depend on the receiver search:
+      // in flight while it runs (measured on MI355X: -0.7 % on the training
+      // graph)
+      const int ef = e < e_lim - 1 ? e : e_lim - 1;
+      load_row<float, LY::NY>(prm.y + (size_t)ef * LY::NY, b0.y);
+      const float* sf = prm.s + (size_t)ef * LY::NP * C + li * CPL;
+#pragma unroll
+      for (int p = 0; p < LY::NP; ++p) load_ch<float, CPL, true>(sf + p * C, b0.s[p]);
+    }
     int b = find_receiver(prm.row_ptr, prm.num_nodes, prm.num_edges, (int)e0);
     while (prm.row_ptr[b + 1] <= (e < e_lim ? e : e_lim - 1)) ++b;   // this group's first edge
     int bend = prm.row_ptr[b + 1];
@@ -1671,9 +1757,10 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& prm, long e0, int e1, 
     // s rows: one buffer, s[p] replaced by the next edge's row as soon as path
     // p is done with it, which keeps a whole edge of s in flight at the cost
     // of one row of registers.
-    BwdBuf<LY, CPL> b0, b1;
     int a = prm.src[e < last ? e : last];
-    load_bwd_edge<LY, CPL, LPG, true>(b0, prm.x, prm.y, prm.s, e < last ? e : last, a, li);
+#pragma unroll
+    for (int i = 0; i < NX; ++i)
+      load_ch<float, CPL, false>(prm.x + ((size_t)a * NX + i) * C + li * CPL, b0.x[i]);
     int en = e + G;
     int an = prm.src[en < last ? en : last];
     auto step = [&](BwdBuf<LY, CPL>& cur, BwdBuf<LY, CPL>& nxt) {
@@ -2061,11 +2148,6 @@ conv_bwd_pairs(BwdParams prm) {
                          gb_all[threadIdx.x >> 6][grp] + li * CPL, li, grp);
 }
 
-__global__ void fill_zero(float* __restrict__ p, size_t n) {
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (; i < n; i += stride) p[i] = 0.0f;
-}
 
 // ------------------------------------------------------------- launchers ----
 
@@ -2100,10 +2182,7 @@ template <class LY, int CPL, int GPR>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t st) {
   constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
   if (p.num_nodes <= 0) return hipSuccess;
-  const size_t nx = (size_t)p.num_nodes * LY::NX * LY::C;
-  const unsigned zb = (unsigned)((nx + 255) / 256 < 8192 ? (nx + 255) / 256 : 8192);
-  hipLaunchKernelGGL(fill_zero, dim3(zb), dim3(256), 0, st, p.gx, nx);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch_fill_zero(p.gx, (size_t)p.num_nodes * LY::NX * LY::C, st);
   if (err != hipSuccess) return err;
   const long waves = (p.num_nodes + RPW - 1) / RPW;
   const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
@@ -2116,10 +2195,7 @@ hipError_t launch_bwd_pipe(const BwdParams& p, hipStream_t st) {
   constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
   if (p.num_nodes <= 0) return hipSuccess;
   if (p.gx && !(p.flags & kAccumulateX)) {
-    const size_t nx = (size_t)p.num_nodes * LY::NX * LY::C;
-    const unsigned zb = (unsigned)((nx + 255) / 256 < 8192 ? (nx + 255) / 256 : 8192);
-    hipLaunchKernelGGL(fill_zero, dim3(zb), dim3(256), 0, st, p.gx, nx);
-    const hipError_t err = hipGetLastError();
+    const hipError_t err = launch_fill_zero(p.gx, (size_t)p.num_nodes * LY::NX * LY::C, st);
     if (err != hipSuccess) return err;
   }
   const long waves = (p.num_nodes + RPW - 1) / RPW;
@@ -2134,10 +2210,7 @@ hipError_t launch_bwd_tile(const BwdParams& prm, hipStream_t st) {
   BwdParams p = prm;
   if (p.num_nodes <= 0) return hipSuccess;
   if (p.gx && !(p.flags & kAccumulateX)) {
-    const size_t nx = (size_t)p.num_nodes * LY::NX * LY::C;
-    const unsigned zb = (unsigned)((nx + 255) / 256 < 8192 ? (nx + 255) / 256 : 8192);
-    hipLaunchKernelGGL(fill_zero, dim3(zb), dim3(256), 0, st, p.gx, nx);
-    const hipError_t err = hipGetLastError();
+    const hipError_t err = launch_fill_zero(p.gx, (size_t)p.num_nodes * LY::NX * LY::C, st);
     if (err != hipSuccess) return err;
   }
   if (p.num_edges <= 0) return hipSuccess;
@@ -2155,10 +2228,7 @@ template <class LY, int CPL, int T>
 hipError_t launch_bwd_pairs(const BwdParams& prm, hipStream_t st) {
   BwdParams p = prm;
   if (p.num_nodes <= 0) return hipSuccess;
-  const size_t nx = (size_t)p.num_nodes * LY::NX * LY::C;
-  const unsigned zb = (unsigned)((nx + 255) / 256 < 8192 ? (nx + 255) / 256 : 8192);
-  hipLaunchKernelGGL(fill_zero, dim3(zb), dim3(256), 0, st, p.gx, nx);
-  const hipError_t err = hipGetLastError();
+  const hipError_t err = launch_fill_zero(p.gx, (size_t)p.num_nodes * LY::NX * LY::C, st);
   if (err != hipSuccess) return err;
   if (p.num_edges <= 0) return hipSuccess;
   const long tiles = ((long)p.num_edges + T - 1) / T;

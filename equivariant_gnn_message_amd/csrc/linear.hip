@@ -420,9 +420,20 @@ __global__ void __launch_bounds__(64 * RW) linear_rows(LinearGemm g, int tiles_t
   }
 }
 
-__global__ void linear_fill_zero(float* __restrict__ p, size_t n) {
+// Zeroes p[0, n): 16-byte stores from the first 16-byte boundary on, single
+// floats for the head before it and the tail after the last whole vector.
+__global__ void fill_zero(float* __restrict__ p, size_t n) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
+  const size_t lead = ((16 - (reinterpret_cast<size_t>(p) & 15)) & 15) / sizeof(float);
+  const size_t head = lead < n ? lead : n;
+  if (tid < head) p[tid] = 0.0f;
+  f32x4* q = reinterpret_cast<f32x4*>(p + head);
+  const size_t nq = (n - head) / 4;
+  for (size_t i = tid; i < nq; i += stride) q[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const size_t t0 = head + nq * 4;
+  if (tid < n - t0) p[t0 + tid] = 0.0f;
 }
 
 }  // namespace
@@ -459,8 +470,9 @@ hipError_t launch_linear_rows(const LinearGemm& g, hipStream_t stream) {
 
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  const size_t blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
-  hipLaunchKernelGGL(linear_fill_zero, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+  const size_t vecs = (n + 3) / 4;
+  const size_t blocks = (vecs + 255) / 256 < 8192 ? (vecs + 255) / 256 : 8192;
+  hipLaunchKernelGGL(fill_zero, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
   return hipGetLastError();
 }
 
