@@ -4,9 +4,10 @@ The definitions (gate-points page, radial embedding and fully connected
 network; reading R11) fix closed-form values: the cutoff is 1 at r = 0, 1/2
 at r_max / 2 and 0 at r_max; each Gaussian is 1 at its center and e^-1 one
 sigma away; silu(z) - silu(-z) = z for every z; the network is linear in its
-last weight matrix.  The oracle's scalars must also agree with the input
-generator's independently written recipe for the gate-points workload, and
-its vectorised route with pure-Python loops.
+last weight matrix; its vectorised route must agree with pure-Python loops.
+Those are the pins.  A further consistency check (not a pin: both sides are
+this project's code) compares the oracle's scalars with the ones the input
+generator stores for the gate-points workload.
 """
 
 import math
@@ -76,7 +77,8 @@ def gate_layout(C=None):
 
 
 def test_scalars_match_the_workload_recipe():
-    """The gate-points workload's s was generated by the input recipe's own code."""
+    """Consistency, not a pin: the gate-points workload's stored s (written by the
+    input generator's own code) equals the oracle's scalars of the same inputs."""
     inp = synth.make_inputs(1, num_graphs=3)
     r, w1, w2 = synth.radial_inputs(inp)
     w1d, w2d = synth.radial_mlp_weights(w2.shape[1])
