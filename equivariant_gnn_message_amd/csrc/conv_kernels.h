@@ -86,12 +86,13 @@ constexpr int ilog2(int v) {
 // 8 XCDs (8 L2 caches); remapping so that XCD k runs a contiguous range of
 // logical blocks keeps receivers that are processed together (neighbours in
 // the receiver order) on one L2, where their shared senders' rows are reused.
-// The grid is a multiple of 8 work-groups of 4 waves.
+// The grid is a multiple of 8 work-groups of WPB waves.
+template <int WPB = 4>
 __device__ __forceinline__ int logical_wave() {
   const int per_xcd = (int)(gridDim.x >> 3);
   const int bid = (int)blockIdx.x;
   const int lb = (bid & 7) * per_xcd + (bid >> 3);
-  return __builtin_amdgcn_readfirstlane(lb * 4 + (int)(threadIdx.x >> 6));
+  return __builtin_amdgcn_readfirstlane(lb * WPB + (WPB > 1 ? (int)(threadIdx.x >> 6) : 0));
 }
 
 // --------------------------------------------------------------- loads ------
@@ -892,8 +893,9 @@ __device__ __forceinline__ void fwd_pipe_receivers(const FwdParams& prm, int ws,
 // LIN: the output linear fused into the epilogue.  Its weights (NB blocks of
 // C x C) are staged in LDS once per work-group, so the work-groups loop over
 // contiguous ranges of wave slots rather than taking one each.
-template <class LY, typename IN, int CPL, int GPR, bool UL = false, bool LIN = false, bool PR = false>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PR ? 2 : 1)))
+template <class LY, typename IN, int CPL, int GPR, bool UL = false, bool LIN = false, bool PR = false,
+          int WPB = 4>
+__global__ void __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(PR ? 2 : 1)))
 conv_fwd_pipe(FwdParams prm) {
   constexpr int C = LY::C, NO = LY::NO;
   constexpr int LPG = C / CPL;
@@ -902,7 +904,7 @@ conv_fwd_pipe(FwdParams prm) {
   static_assert(G % GPR == 0, "groups per receiver must divide groups per wave");
   constexpr int RPW = G / GPR;
   if constexpr (!LIN) {
-    fwd_pipe_receivers<LY, IN, CPL, GPR, UL, false, PR>(prm, logical_wave(), nullptr, nullptr);
+    fwd_pipe_receivers<LY, IN, CPL, GPR, UL, false, PR>(prm, logical_wave<WPB>(), nullptr, nullptr);
   } else {
     constexpr int NB = num_blocks(LY::OCODE);
     __shared__ float lin_w[NB * C * C];
@@ -1813,23 +1815,23 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& prm, long e0, int e1, 
 
 // The edges are cut into prm.tiles ranges of nearly equal length (differing by
 // at most one edge); wave w runs range w.
-template <class LY, int CPL, bool GEN = false>
-__global__ void __launch_bounds__(256) conv_bwd_tile(BwdParams prm) {
+template <class LY, int CPL, bool GEN = false, int WPB = 4>
+__global__ void __launch_bounds__(64 * WPB) conv_bwd_tile(BwdParams prm) {
   constexpr int C = LY::C, NX = LY::NX;
   constexpr int LPG = C / CPL;
   static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
   constexpr int G = 64 / LPG;
-  __shared__ float xt_all[4][G][NX * C];
+  __shared__ float xt_all[WPB][G][NX * C];
 
   const int lane = threadIdx.x & 63;
   const int li = lane % LPG;
   const int grp = lane / LPG;
-  const long w = logical_wave();
+  const long w = logical_wave<WPB>();
   if (w >= prm.tiles) return;
   const long e0 = w * prm.num_edges / prm.tiles;
   const int e1 = (int)((w + 1) * prm.num_edges / prm.tiles);
   if (e0 >= e1) return;
-  bwd_tile<LY, CPL, GEN>(prm, e0, e1, xt_all[threadIdx.x >> 6][grp], li, grp);
+  bwd_tile<LY, CPL, GEN>(prm, e0, e1, xt_all[WPB > 1 ? threadIdx.x >> 6 : 0][grp], li, grp);
 }
 
 // ------------------------------------------------ pair-stored backward ------
@@ -2164,17 +2166,19 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t st) {
 
 // LIN: the output linear fused into the epilogue (p.lin_w, p.lin_alpha).
 // PR: y and s read from pair-stored rows through p.emap.
-template <class LY, typename IN, int CPL, int GPR, bool UL = false, bool LIN = false, bool PR = false>
+template <class LY, typename IN, int CPL, int GPR, bool UL = false, bool LIN = false, bool PR = false,
+          int WPB = 4>
 hipError_t launch_fwd_pipe(const FwdParams& p, hipStream_t st) {
   constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
+  static_assert(WPB == 4 || !LIN, "the fused linear runs work-groups of four waves");
   if (p.num_nodes <= 0) return hipSuccess;
   const long waves = (p.num_nodes + RPW - 1) / RPW;
-  const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
+  const long blocks = ((waves + WPB - 1) / WPB + 7) / 8 * 8;
   // the fused linear's work-groups loop over receivers: at most 1024 of them,
   // each staging the weights once
   const long grid = LIN && blocks > 1024 ? 1024 : blocks;
-  hipLaunchKernelGGL((conv_fwd_pipe<LY, IN, CPL, GPR, UL, LIN, PR>), dim3((unsigned)grid), dim3(256), 0, st,
-                     p);
+  hipLaunchKernelGGL((conv_fwd_pipe<LY, IN, CPL, GPR, UL, LIN, PR, WPB>), dim3((unsigned)grid), dim3(64 * WPB),
+                     0, st, p);
   return hipGetLastError();
 }
 
@@ -2205,7 +2209,7 @@ hipError_t launch_bwd_pipe(const BwdParams& p, hipStream_t st) {
 }
 
 // One wave per tile of about T edges.
-template <class LY, int CPL, int T, bool GEN = false>
+template <class LY, int CPL, int T, bool GEN = false, int WPB = 4>
 hipError_t launch_bwd_tile(const BwdParams& prm, hipStream_t st) {
   BwdParams p = prm;
   if (p.num_nodes <= 0) return hipSuccess;
@@ -2214,11 +2218,11 @@ hipError_t launch_bwd_tile(const BwdParams& prm, hipStream_t st) {
     if (err != hipSuccess) return err;
   }
   if (p.num_edges <= 0) return hipSuccess;
-  const auto kernel = conv_bwd_tile<LY, CPL, GEN>;
+  const auto kernel = conv_bwd_tile<LY, CPL, GEN, WPB>;
   const long tiles = ((long)p.num_edges + T - 1) / T;
   p.tiles = (int)tiles;
-  const long blocks = ((tiles + 3) / 4 + 7) / 8 * 8;   // whole rounds of the 8 XCDs (logical_wave)
-  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, st, p);
+  const long blocks = ((tiles + WPB - 1) / WPB + 7) / 8 * 8;   // whole rounds of the 8 XCDs (logical_wave)
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * WPB), 0, st, p);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ pytestmark = pytest.mark.gpu
 TIGHT = 2e-4
 BF16_BAR = 2e-2
 MATRIX_CORE = (6, 7)        # RECEIVER bf16 variants of this layout on the matrix cores
-N_RECEIVER_BF16 = 8         # variants compiled for the layout (a change of the list fails here)
+N_RECEIVER_BF16 = 9         # variants compiled for the layout (a change of the list fails here)
 
 
 def lay_of(w):
