@@ -1106,8 +1106,8 @@ __device__ __forceinline__ void jvp_accumulate(const JvpBuf<LY, IN, CPL>& buf, f
 
 // PX: the sender rows (x, dx) are prefetched with the rest; without it they
 // are loaded just before their edge is accumulated (fewer registers).
-template <class LY, typename IN, int CPL, int GPR, bool PX>
-__global__ void __launch_bounds__(256) conv_jvp_pipe(JvpParams prm) {
+template <class LY, typename IN, int CPL, int GPR, bool PX, int WPB = 4>
+__global__ void __launch_bounds__(64 * WPB) conv_jvp_pipe(JvpParams prm) {
   constexpr int C = LY::C, NO = LY::NO;
   constexpr int LPG = C / CPL;
   static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
@@ -1129,7 +1129,7 @@ __global__ void __launch_bounds__(256) conv_jvp_pipe(JvpParams prm) {
   const int grp = lane / LPG;
   const int gi = grp % GPR;
   const int slot = grp / GPR;
-  const int bl = logical_wave() * RPW + slot;
+  const int bl = logical_wave<WPB>() * RPW + slot;
   const bool valid = bl < prm.num_nodes;
   const int b = valid ? (prm.order ? prm.order[bl] : bl) : 0;
   const int c0 = li * CPL;
@@ -1590,8 +1590,8 @@ __device__ __forceinline__ void bwd_edge(const BwdBuf<LY, CPL>& buf, const float
   store_dy<NY, LPG>(dyp, prm.gy + (size_t)e * NY, li, GEN && (prm.flags & kAccumulateY));
 }
 
-template <class LY, int CPL, int GPR, bool GEN = false>
-__global__ void __launch_bounds__(256) conv_bwd_pipe(BwdParams prm) {
+template <class LY, int CPL, int GPR, bool GEN = false, int WPB = 4>
+__global__ void __launch_bounds__(64 * WPB) conv_bwd_pipe(BwdParams prm) {
   constexpr int C = LY::C, NO = LY::NO;
   constexpr int LPG = C / CPL;
   static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
@@ -1609,7 +1609,7 @@ __global__ void __launch_bounds__(256) conv_bwd_pipe(BwdParams prm) {
   const int grp = lane / LPG;
   const int gi = grp % GPR;
   const int slot = grp / GPR;
-  const int bl = logical_wave() * RPW + slot;
+  const int bl = logical_wave<WPB>() * RPW + slot;
   if (bl >= prm.num_nodes) return;   // whole slots only: no cross-lane work follows an early exit
   const int b = prm.order ? prm.order[bl] : bl;
 
@@ -2128,26 +2128,26 @@ __device__ __forceinline__ void bwd_pair_tile(const BwdParams& prm, int e0, int 
 
 // The stored edges are cut into prm.tiles ranges of nearly equal length; wave
 // w runs range w.
-template <class LY, int CPL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <class LY, int CPL, int WPB = 4>
+__global__ void __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(2)))
 conv_bwd_pairs(BwdParams prm) {
   constexpr int C = LY::C, NX = LY::NX;
   constexpr int LPG = C / CPL;
   static_assert(C % CPL == 0 && 64 % LPG == 0, "a group must tile a wave");
   constexpr int G = 64 / LPG;
-  __shared__ float xt_all[4][G][NX * C];
-  __shared__ float gb_all[4][G][LY::NO * C];
+  __shared__ float xt_all[WPB][G][NX * C];
+  __shared__ float gb_all[WPB][G][LY::NO * C];
 
   const int lane = threadIdx.x & 63;
   const int li = lane % LPG;
   const int grp = lane / LPG;
-  const long w = logical_wave();
+  const long w = logical_wave<WPB>();
   if (w >= prm.tiles) return;
   const int e0 = (int)(w * prm.num_edges / prm.tiles);
   const int e1 = (int)((w + 1) * prm.num_edges / prm.tiles);
   if (e0 >= e1) return;
-  bwd_pair_tile<LY, CPL>(prm, e0, e1, xt_all[threadIdx.x >> 6][grp],
-                         gb_all[threadIdx.x >> 6][grp] + li * CPL, li, grp);
+  bwd_pair_tile<LY, CPL>(prm, e0, e1, xt_all[WPB > 1 ? threadIdx.x >> 6 : 0][grp],
+                         gb_all[WPB > 1 ? threadIdx.x >> 6 : 0][grp] + li * CPL, li, grp);
 }
 
 
@@ -2194,7 +2194,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <class LY, int CPL, int GPR, bool GEN = false>
+template <class LY, int CPL, int GPR, bool GEN = false, int WPB = 4>
 hipError_t launch_bwd_pipe(const BwdParams& p, hipStream_t st) {
   constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
   if (p.num_nodes <= 0) return hipSuccess;
@@ -2203,8 +2203,8 @@ hipError_t launch_bwd_pipe(const BwdParams& p, hipStream_t st) {
     if (err != hipSuccess) return err;
   }
   const long waves = (p.num_nodes + RPW - 1) / RPW;
-  const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
-  hipLaunchKernelGGL((conv_bwd_pipe<LY, CPL, GPR, GEN>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  const long blocks = ((waves + WPB - 1) / WPB + 7) / 8 * 8;
+  hipLaunchKernelGGL((conv_bwd_pipe<LY, CPL, GPR, GEN, WPB>), dim3((unsigned)blocks), dim3(64 * WPB), 0, st, p);
   return hipGetLastError();
 }
 
@@ -2228,7 +2228,7 @@ hipError_t launch_bwd_tile(const BwdParams& prm, hipStream_t st) {
 
 // Pair-stored reverse pass: grad_x zeroed, then one wave per tile of about T
 // stored edges (prm.num_edges of them, prm.dst their receivers).
-template <class LY, int CPL, int T>
+template <class LY, int CPL, int T, int WPB = 4>
 hipError_t launch_bwd_pairs(const BwdParams& prm, hipStream_t st) {
   BwdParams p = prm;
   if (p.num_nodes <= 0) return hipSuccess;
@@ -2237,18 +2237,18 @@ hipError_t launch_bwd_pairs(const BwdParams& prm, hipStream_t st) {
   if (p.num_edges <= 0) return hipSuccess;
   const long tiles = ((long)p.num_edges + T - 1) / T;
   p.tiles = (int)tiles;
-  const long blocks = ((tiles + 3) / 4 + 7) / 8 * 8;   // whole rounds of the 8 XCDs (logical_wave)
-  hipLaunchKernelGGL((conv_bwd_pairs<LY, CPL>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  const long blocks = ((tiles + WPB - 1) / WPB + 7) / 8 * 8;   // whole rounds of the 8 XCDs (logical_wave)
+  hipLaunchKernelGGL((conv_bwd_pairs<LY, CPL, WPB>), dim3((unsigned)blocks), dim3(64 * WPB), 0, st, p);
   return hipGetLastError();
 }
 
-template <class LY, typename IN, int CPL, int GPR, bool PX>
+template <class LY, typename IN, int CPL, int GPR, bool PX, int WPB = 4>
 hipError_t launch_jvp_pipe(const JvpParams& p, hipStream_t st) {
   constexpr int RPW = (64 / (LY::C / CPL)) / GPR;
   if (p.num_nodes <= 0) return hipSuccess;
   const long waves = (p.num_nodes + RPW - 1) / RPW;
-  const long blocks = ((waves + 3) / 4 + 7) / 8 * 8;
-  hipLaunchKernelGGL((conv_jvp_pipe<LY, IN, CPL, GPR, PX>), dim3((unsigned)blocks), dim3(256), 0, st, p);
+  const long blocks = ((waves + WPB - 1) / WPB + 7) / 8 * 8;
+  hipLaunchKernelGGL((conv_jvp_pipe<LY, IN, CPL, GPR, PX, WPB>), dim3((unsigned)blocks), dim3(64 * WPB), 0, st, p);
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ const KernelSet* kernels_big() {
   static const KernelSet k = {
     L::C, L::XCODE, L::L, L::OCODE, &kTables, kCG.v,
     {kF32, E3C_N(kF32), kBF16, E3C_N(kBF16), kBwd, E3C_N(kBwd), launch_bwd_pipe<L, 2, 2, true>,
-     launch_jvp<L, float, 2, 2>, launch_jvp_pipe<L, bf16_bits, 2, 2, false>, nullptr,
+     launch_jvp<L, float, 2, 2>, launch_jvp_pipe<L, bf16_bits, 2, 2, false, 1>, nullptr,
      launch_bwd_pairs<L, 1, 16>, launch_fwd_pipe<L, float, 2, 2, false, true>,
      launch_fwd_pipe<L, bf16_bits, 2, 2, true, true>, launch_fwd_pipe<L, float, 2, 2, false, false, true>},
     {kSenderF32, 1, kSenderBF16, 1, kSenderBwd, 1, launch_bwd_pipe<LS, 2, 2, true>,

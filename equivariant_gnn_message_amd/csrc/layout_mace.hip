@@ -26,9 +26,9 @@ const BwdLauncher kBwd[] = {launch_bwd_tile<L, 4, 16, false, 1>, launch_bwd_pipe
                             launch_bwd<L, 2, 1>, launch_bwd_pipe<L, 4, 2>, launch_bwd_tile<L, 4, 8, false, 1>,
                             launch_bwd_tile<L, 4, 32, false, 1>, launch_bwd_tile<L, 4, 16>};
 
-const FwdLauncher kSenderF32[] = {launch_fwd_pipe<LS, float, 4, 2>};
+const FwdLauncher kSenderF32[] = {launch_fwd_pipe<LS, float, 4, 2, false, false, false, 1>};
 const FwdLauncher kSenderBF16[] = {launch_fwd_pipe<LS, bf16_bits, 4, 2>};
-const BwdLauncher kSenderBwd[] = {launch_bwd_pipe<LS, 2, 1>};
+const BwdLauncher kSenderBwd[] = {launch_bwd_pipe<LS, 2, 1, false, 1>};
 
 #define E3C_N(a) (int)(sizeof(a) / sizeof((a)[0]))
 
@@ -37,9 +37,9 @@ const BwdLauncher kSenderBwd[] = {launch_bwd_pipe<LS, 2, 1>};
 const KernelSet* kernels_mace() {
   static const KernelSet k = {
     L::C, L::XCODE, L::L, L::OCODE, &kTables, kCG.v,
-    {kF32, E3C_N(kF32), kBF16, E3C_N(kBF16), kBwd, E3C_N(kBwd), launch_bwd_pipe<L, 2, 1, true>,
-     launch_jvp_pipe<L, float, 2, 1, false>, launch_jvp_pipe<L, bf16_bits, 2, 1, true>, nullptr,
-     launch_bwd_pairs<L, 2, 16>, nullptr, nullptr, launch_fwd_pipe<L, float, 2, 1, false, false, true>},
+    {kF32, E3C_N(kF32), kBF16, E3C_N(kBF16), kBwd, E3C_N(kBwd), launch_bwd_pipe<L, 2, 1, true, 1>,
+     launch_jvp_pipe<L, float, 2, 1, false, 1>, launch_jvp_pipe<L, bf16_bits, 2, 1, true, 1>, nullptr,
+     launch_bwd_pairs<L, 2, 16, 1>, nullptr, nullptr, launch_fwd_pipe<L, float, 2, 1, false, false, true, 1>},
     {kSenderF32, 1, kSenderBF16, 1, kSenderBwd, 1, launch_bwd_pipe<LS, 2, 1, true>,
      launch_jvp_pipe<LS, float, 2, 1, false>, launch_jvp_pipe<LS, bf16_bits, 2, 1, true>},
   };
