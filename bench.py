@@ -56,8 +56,9 @@ def parse():
     ap.add_argument("--no-extra", action="store_true",
                     help="default run: skip the extra forward figures of workloads 2 and 3")
     ap.add_argument("--eager", action="store_true",
-                    help="time the step as eager launches only (default: the step captured once "
-                         "in a HIP graph and replayed is the headline; eager figures beside it)")
+                    help="time the training step as eager launches only (default: the step "
+                         "captured once in a HIP graph and replayed is the headline, eager figures "
+                         "beside it; a forward-only step is one kernel launch and always eager)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every compiled kernel variant (one JSON line each) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -484,10 +485,12 @@ def main():
 
     eager_ms_per_step = wall / args.steps * 1e3
     ms_per_step, graph_ms = eager_ms_per_step, None
-    if not args.eager:
-        # The headline step: the same step (every kernel of it) captured once in a HIP graph
-        # and replayed, W untimed replays, then K replays bracketed by synchronisations,
-        # timed by the host clock like the eager loop.
+    if w.backward and not args.eager:
+        # The headline training step: the same step (every kernel of it) captured once in a
+        # HIP graph and replayed, W untimed replays, then K replays bracketed by
+        # synchronisations, timed by the host clock like the eager loop.  (A graph removes the
+        # gaps between a step's kernel launches; a forward-only step is one launch, which a
+        # graph replay only makes slower, so it stays eager.)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
