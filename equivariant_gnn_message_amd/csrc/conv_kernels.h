@@ -663,6 +663,15 @@ __device__ __forceinline__ void load_raw(const IN* p, RawVec<IN, N>& r) {
   }
 }
 
+// A row of N floats at a wave-uniform address, read through the scalar cache.
+template <int N>
+__device__ __forceinline__ void load_row_uniform(const float* p, float (&v)[N]) {
+  typedef const __attribute__((address_space(4))) float cfloat;
+  cfloat* q = (cfloat*)(uintptr_t)p;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = q[i];
+}
+
 template <class LY, typename IN, int CPL>
 struct EdgeBuf {
   RawVec<IN, LY::NY> y;
@@ -1716,8 +1725,9 @@ __device__ __forceinline__ int find_receiver(const int* __restrict__ row_ptr, in
   return __builtin_amdgcn_readfirstlane((int)lo);
 }
 
+
 // One tile: the edges [e0, e1).
-template <class LY, int CPL, bool GEN>
+template <class LY, int CPL, bool GEN, bool SY = false, bool SS = false>
 __device__ __forceinline__ void bwd_tile(const BwdParams& prm, long e0, int e1, float* xt, int li,
                                          int grp) {
   constexpr int C = LY::C, NX = LY::NX, NO = LY::NO;
@@ -1769,9 +1779,32 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& prm, long e0, int e1, 
       // the next edge's rows (and the sender two edges ahead) are loaded
       // unconditionally, clamped to the tile's last edge
       const int en2 = en + G;
-      const int an2 = prm.src[en2 < last ? en2 : last];
+      int an2;
+      if constexpr (SS) {
+        // both groups' senders two edges ahead through the scalar cache
+        static_assert(G == 2, "two groups per wave");
+        typedef const __attribute__((address_space(4))) int cint;
+        cint* sp = (cint*)(uintptr_t)prm.src;
+        const int e0n2 = __builtin_amdgcn_readfirstlane(en2 - grp);
+        const int sa = sp[e0n2 < last ? e0n2 : last];
+        const int sb = sp[e0n2 + 1 < last ? e0n2 + 1 : last];
+        an2 = grp ? sb : sa;
+      } else {
+        an2 = prm.src[en2 < last ? en2 : last];
+      }
       const int ec = en < last ? en : last;
-      load_row<float, LY::NY>(prm.y + (size_t)ec * LY::NY, nxt.y);
+      // SY: the two groups' next y rows through the scalar cache (two scalar
+      // loads instead of four vector loads per group), each group taking its
+      // own at the end of the step
+      float ya[SY ? LY::NY : 1], yb[SY ? LY::NY : 1];
+      if constexpr (SY) {
+        static_assert(G == 2, "two groups per wave");
+        const int e0n = __builtin_amdgcn_readfirstlane(en - grp);
+        load_row_uniform<LY::NY>(prm.y + (size_t)(e0n < last ? e0n : last) * LY::NY, ya);
+        load_row_uniform<LY::NY>(prm.y + (size_t)(e0n + 1 < last ? e0n + 1 : last) * LY::NY, yb);
+      } else {
+        load_row<float, LY::NY>(prm.y + (size_t)ec * LY::NY, nxt.y);
+      }
 #pragma unroll
       for (int i = 0; i < NX; ++i)
         load_ch<float, CPL, false>(prm.x + ((size_t)an * NX + i) * C + li * CPL, nxt.x[i]);
@@ -1794,6 +1827,10 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& prm, long e0, int e1, 
       for (int p = 0; p < LY::NP; ++p)
 #pragma unroll
         for (int c = 0; c < CPL; ++c) nxt.s[p][c] = cur.s[p][c];
+      if constexpr (SY) {
+#pragma unroll
+        for (int j = 0; j < LY::NY; ++j) nxt.y[j] = grp ? yb[j] : ya[j];
+      }
       e = en;
       a = an;
       en = en2;
@@ -1815,7 +1852,7 @@ __device__ __forceinline__ void bwd_tile(const BwdParams& prm, long e0, int e1, 
 
 // The edges are cut into prm.tiles ranges of nearly equal length (differing by
 // at most one edge); wave w runs range w.
-template <class LY, int CPL, bool GEN = false, int WPB = 4>
+template <class LY, int CPL, bool GEN = false, int WPB = 4, bool SY = false, bool SS = false>
 __global__ void __launch_bounds__(64 * WPB) conv_bwd_tile(BwdParams prm) {
   constexpr int C = LY::C, NX = LY::NX;
   constexpr int LPG = C / CPL;
@@ -1831,7 +1868,7 @@ __global__ void __launch_bounds__(64 * WPB) conv_bwd_tile(BwdParams prm) {
   const long e0 = w * prm.num_edges / prm.tiles;
   const int e1 = (int)((w + 1) * prm.num_edges / prm.tiles);
   if (e0 >= e1) return;
-  bwd_tile<LY, CPL, GEN>(prm, e0, e1, xt_all[WPB > 1 ? threadIdx.x >> 6 : 0][grp], li, grp);
+  bwd_tile<LY, CPL, GEN, SY, SS>(prm, e0, e1, xt_all[WPB > 1 ? threadIdx.x >> 6 : 0][grp], li, grp);
 }
 
 // ------------------------------------------------ pair-stored backward ------
@@ -1883,14 +1920,6 @@ constexpr bool last_into_block(const LayoutTables& t, int j) {
   return j + 1 >= t.num_paths || t.path[path_by_out(t, j + 1)].o3 != t.path[path_by_out(t, j)].o3;
 }
 
-// A row of N floats at a wave-uniform address, read through the scalar cache.
-template <int N>
-__device__ __forceinline__ void load_row_uniform(const float* p, float (&v)[N]) {
-  typedef const __attribute__((address_space(4))) float cfloat;
-  cfloat* q = (cfloat*)(uintptr_t)p;
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = q[i];
-}
 
 template <class LY, int CPL>
 struct PairBuf {
@@ -2209,7 +2238,7 @@ hipError_t launch_bwd_pipe(const BwdParams& p, hipStream_t st) {
 }
 
 // One wave per tile of about T edges.
-template <class LY, int CPL, int T, bool GEN = false, int WPB = 4>
+template <class LY, int CPL, int T, bool GEN = false, int WPB = 4, bool SY = false, bool SS = false>
 hipError_t launch_bwd_tile(const BwdParams& prm, hipStream_t st) {
   BwdParams p = prm;
   if (p.num_nodes <= 0) return hipSuccess;
@@ -2218,7 +2247,7 @@ hipError_t launch_bwd_tile(const BwdParams& prm, hipStream_t st) {
     if (err != hipSuccess) return err;
   }
   if (p.num_edges <= 0) return hipSuccess;
-  const auto kernel = conv_bwd_tile<LY, CPL, GEN, WPB>;
+  const auto kernel = conv_bwd_tile<LY, CPL, GEN, WPB, SY, SS>;
   const long tiles = ((long)p.num_edges + T - 1) / T;
   p.tiles = (int)tiles;
   const long blocks = ((tiles + WPB - 1) / WPB + 7) / 8 * 8;   // whole rounds of the 8 XCDs (logical_wave)

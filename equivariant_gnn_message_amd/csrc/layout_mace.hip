@@ -16,15 +16,19 @@ constexpr CGValues<L::NNZ> kCG = L::CG;
 // when its last wave ends, so single-wave work-groups free each wave's slot
 // as soon as it is done (measured on MI355X, training step on the MACE-scale
 // graph: forward 0.660 against 0.667 ms, reverse 1.364 against 1.369 ms with
-// four-wave work-groups, variants 4 and 8).
+// four-wave work-groups, forward variant 4 and reverse variant 7).  The
+// reverse default reads the two groups' y rows and sender indices through
+// the scalar cache: 1.347 against 1.366 ms (reverse variant 8).
 const FwdLauncher kF32[] = {launch_fwd_pipe<L, float, 4, 2, false, false, false, 1>, launch_fwd<L, float, 2, 1>,
                             launch_fwd_pipe<L, float, 2, 1>, launch_fwd_pipe<L, float, 4, 1>,
                             launch_fwd_pipe<L, float, 4, 2>};
 const FwdLauncher kBF16[] = {launch_fwd_pipe<L, bf16_bits, 4, 2>, launch_fwd<L, bf16_bits, 2, 1>,
                              launch_fwd_pipe<L, bf16_bits, 2, 1>};
-const BwdLauncher kBwd[] = {launch_bwd_tile<L, 4, 16, false, 1>, launch_bwd_pipe<L, 2, 1>, launch_bwd<L, 4, 2>,
-                            launch_bwd<L, 2, 1>, launch_bwd_pipe<L, 4, 2>, launch_bwd_tile<L, 4, 8, false, 1>,
-                            launch_bwd_tile<L, 4, 32, false, 1>, launch_bwd_tile<L, 4, 16>};
+const BwdLauncher kBwd[] = {launch_bwd_tile<L, 4, 16, false, 1, true, true>, launch_bwd_pipe<L, 2, 1>,
+                            launch_bwd<L, 4, 2>, launch_bwd<L, 2, 1>, launch_bwd_pipe<L, 4, 2>,
+                            launch_bwd_tile<L, 4, 8, false, 1, true, true>,
+                            launch_bwd_tile<L, 4, 32, false, 1, true, true>, launch_bwd_tile<L, 4, 16>,
+                            launch_bwd_tile<L, 4, 16, false, 1>};
 
 const FwdLauncher kSenderF32[] = {launch_fwd_pipe<LS, float, 4, 2, false, false, false, 1>};
 const FwdLauncher kSenderBF16[] = {launch_fwd_pipe<LS, bf16_bits, 4, 2>};
