@@ -1434,12 +1434,18 @@ struct BwdBuf {
 };
 
 // The lane holds channels li, li+LPG, ... (one 4-byte access per channel).
+// With one group per wave (LPG = 64) the edge is wave-uniform and its y row
+// is read through the scalar cache.
 template <class LY, int CPL, int LPG>
 __device__ __forceinline__ void load_bwd_edge(BwdBuf<LY, CPL>& buf, const float* __restrict__ x,
                                               const float* __restrict__ y,
                                               const float* __restrict__ s, int e, int a, int li) {
   constexpr int C = LY::C, NX = LY::NX, NY = LY::NY, NP = LY::NP;
-  load_row<float, NY>(y + (size_t)e * NY, buf.y);
+  if constexpr (LPG == 64) {
+    load_row_uniform<NY>(y + (size_t)__builtin_amdgcn_readfirstlane(e) * NY, buf.y);
+  } else {
+    load_row<float, NY>(y + (size_t)e * NY, buf.y);
+  }
   const float* xrow = x + (size_t)a * NX * C + li;
 #pragma unroll
   for (int i = 0; i < NX; ++i)
